@@ -1,0 +1,55 @@
+"""One 1.5-SPSA step on the CPU, built from the oracle's primitives.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Order of work ("Stanford's 1.5-SPSA Trains OPT-30B Without Backpropagation", sections
+"How 1.5-SPSA Works" and "Probe-Space Preconditioning"; the ZOO training-loop flowchart
+of "Pretraining Transformers Without Backprop: What Two Zero-Order Papers Actually
+Measure"):
+
+  1. the clean loss L0 at the unperturbed parameters;
+  2. for each probe i: perturb to theta + eps*z_i, loss L+_i, restore; perturb to
+     theta - eps*z_i, loss L-_i, restore.  Each move is one in-place pass, so the
+     schedule is +eps, -eps (restore), -eps, +eps (restore): four passes per probe;
+  3. the probe weights c_i from (L+_i, L-_i, L0);
+  4. the update theta <- theta - eta * sum_i c_i z_i.
+
+The eps handed to the weights is the fp32 value that the passes actually added.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def spsa_step(theta: np.ndarray, *, seed: int, step: int, npert: int, eps: float,
+              eta: float, delta: float, loss_fn=None, losses=None, offset: int = 0,
+              bits=None) -> dict:
+    """Run one step in place on `theta` (float32, or uint16 bf16 bits).
+
+    loss_fn(theta) -> float gives the losses; alternatively `losses` = (L0, Lp, Lm)
+    supplies them (synthetic losses, or losses measured elsewhere), and the perturb and
+    restore passes still run.  bits: optional (npert, plane_bytes) packed rows.
+    """
+    from . import perturb, probe_weights, update  # late import: package init order
+
+    a = float(np.float32(eps))
+    if losses is not None:
+        L0, Lp, Lm = float(losses[0]), np.array(losses[1], dtype=np.float64), \
+            np.array(losses[2], dtype=np.float64)
+    else:
+        L0 = float(loss_fn(theta))
+        Lp = np.zeros(npert, dtype=np.float64)
+        Lm = np.zeros(npert, dtype=np.float64)
+    for i in range(npert):
+        row = None if bits is None else bits[i]
+        perturb(theta, offset, seed, step, i, +a, row)
+        if losses is None:
+            Lp[i] = loss_fn(theta)
+        perturb(theta, offset, seed, step, i, -a, row)
+        perturb(theta, offset, seed, step, i, -a, row)
+        if losses is None:
+            Lm[i] = loss_fn(theta)
+        perturb(theta, offset, seed, step, i, +a, row)
+    c, bad = probe_weights(Lp, Lm, L0, a, delta)
+    update(theta, offset, seed, step, c, eta, bits)
+    return {"L0": L0, "Lp": Lp, "Lm": Lm, "c": c, "nonfinite": bad}
