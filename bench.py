@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Throughput of one 1.5-SPSA step of the perturb / probe-weight / update path on one GPU.
+
+A step (per "Stanford's 1.5-SPSA Trains OPT-30B Without Backpropagation", sections "How
+1.5-SPSA Works" and "Probe-Space Preconditioning") is: for each of n_pert probes, four
+in-place passes over the parameters (+eps, restore, -eps, restore) with the per-probe
+losses taken between them, then the probe weights from the 2 n_pert + 1 losses, then one
+update pass theta <- theta - eta * sum_i c_i z_i.  Probes are regenerated from the
+counter-based generator in every pass (nothing stored).
+
+Default workload: an OPT-30B-shaped bf16 parameter set (48 layers, d = 7168, FFN 28672,
+vocab 50272: 29,959,831,552 params, 59.9 GB) updated in place, n_pert = 160, eps = 1e-3;
+theta ~ N(0, 0.02) drawn on the device; per-probe losses synthetic (drawn on the host per
+step and uploaded before the timed region).
+
+Prints one JSON line: probe*params/s for the whole job, plus the HBM roofline of the
+dominant kernel (the perturb pass) and the CPU oracle timed on a bounded slice.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import threading
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_perturb.json")
+PERTURB_SOURCES = ["forward_only_amd/csrc/k_perturb.hip", "forward_only_amd/csrc/zo_device.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=None, help="timed steps (default: config's)")
+    p.add_argument("--warmup", type=int, default=1)
+    p.add_argument("--config", default="opt30b",
+                   choices=["tiny", "flat125m", "opt13b", "opt30b"])
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip the CPU oracle leg (profiling runs)")
+    p.add_argument("--cpu-params-per-thread", type=int, default=1 << 18)
+    p.add_argument("--cpu-threads", type=int, default=None)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain 4 GiB device copy (counter calibration)")
+    return p.parse_args(argv)
+
+
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str, nbytes_alg: float):
+    """HBM bytes per perturb dispatch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source and this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_hash(PERTURB_SOURCES) or t.get("workload") != workload:
+        return None
+    return float(t["bytes_per_dispatch"])
+
+
+# ------------------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded slice of the same workload
+# ------------------------------------------------------------------------------------
+def cpu_baseline(cfg, params_per_thread: int, threads: int):
+    import numpy as np
+
+    import oracle
+    from workloads import gen
+
+    L0, Lp, Lm = gen.synthetic_losses(cfg.seed, 0, cfg.npert)
+    rng = np.random.default_rng(1234)
+    windows = []
+    for w in range(threads):
+        x = (rng.standard_normal(params_per_thread) * cfg.theta_std).astype(np.float32)
+        windows.append(oracle.f32_to_bf16(x) if cfg.dtype == "bf16" else x)
+    nblk_total = cfg.M // 128
+    offsets = [int(o) * 128 for o in np.linspace(0, nblk_total - params_per_thread // 128 - 1,
+                                                 threads).astype(np.int64)]
+    oracle.lib()  # build/load outside the timed region
+
+    def run(w):
+        oracle.spsa_step(windows[w], seed=cfg.seed, step=0, npert=cfg.npert, eps=cfg.eps,
+                         eta=cfg.eta, delta=cfg.delta, losses=(L0, Lp, Lm), offset=offsets[w])
+
+    ts = [threading.Thread(target=run, args=(w,)) for w in range(threads)]
+    t0 = time.perf_counter()
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    dt = time.perf_counter() - t0
+    work = cfg.npert * params_per_thread * threads
+    return {
+        "value": work / dt, "unit": "probe*params/s", "cores": threads, "kind": "oracle",
+        "sample": (f"{threads} windows x {params_per_thread} {cfg.dtype} params of the "
+                   f"{cfg.name} workload, one full step (n_pert={cfg.npert}, four passes "
+                   f"per probe, weights, update), one window per thread; {dt:.1f} s"),
+    }
+
+
+# ------------------------------------------------------------------------------------
+def copy_calibration():
+    import torch
+    nbytes = 4 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes,
+                      "dispatches": 3}), flush=True)
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this path has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", flush=True)
+        sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    import forward_only_amd as zo
+    from forward_only_amd.step import applied_eps
+    from workloads import CONFIGS, gen
+
+    cfg = CONFIGS[args.config]
+    K = args.steps if args.steps is not None else cfg.steps
+    W = args.warmup
+    n, M = cfg.npert, cfg.M
+    esize = 2 if cfg.dtype == "bf16" else 4
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+
+    # CPU oracle leg first (host only; keeps the GPU phase uninterrupted).
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        log(f"[bench] cpu baseline: {threads} threads x {args.cpu_params_per_thread} params")
+        cpu = cpu_baseline(cfg, args.cpu_params_per_thread, threads)
+        log(f"[bench] cpu baseline: {cpu['value']:.3e} probe*params/s")
+
+    ctx = zo.zo_init(cfg.seed)
+    log(f"[bench] {cfg.name}: M={M} {cfg.dtype} ({M * esize / 1e9:.2f} GB), n_pert={n}, "
+        f"steps={K}, warmup={W}")
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    theta = torch.empty(M, dtype=tdt, device=dev)
+    a_dev = None
+    if cfg.loss == "quad":
+        th0, a = gen.theta_and_a(cfg)
+        theta.copy_(torch.from_numpy(th0))
+        a_dev = torch.from_numpy(a).to(dev)
+        del th0, a
+    else:
+        gen.device_normal_(theta, cfg.theta_std, cfg.seed)
+    torch.cuda.synchronize()
+    log("[bench] parameters ready")
+
+    total = W + K
+    L0s = torch.empty((total, 1), dtype=torch.float64, device=dev)
+    Lps = torch.empty((total, n), dtype=torch.float64, device=dev)
+    Lms = torch.empty((total, n), dtype=torch.float64, device=dev)
+    if cfg.loss == "synthetic":
+        for s in range(total):
+            l0, lp, lm = gen.synthetic_losses(cfg.seed, s, n)
+            L0s[s, 0] = l0
+            Lps[s].copy_(torch.from_numpy(lp))
+            Lms[s].copy_(torch.from_numpy(lm))
+    c_buf = torch.empty(n, dtype=torch.float32, device=dev)
+    a = applied_eps(cfg.eps)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    per = {"perturb": [], "weights": [], "update": [], "loss": []}
+
+    def timed(kind, fn, record):
+        if record:
+            e0, e1 = ev(), ev()
+            e0.record()
+            fn()
+            e1.record()
+            per[kind].append((e0, e1))
+        else:
+            fn()
+
+    def one_step(s, record):
+        L0, Lp, Lm = L0s[s], Lps[s], Lms[s]
+        if cfg.loss == "quad":
+            timed("loss", lambda: zo.zo_quad_loss(ctx, theta, a_dev, out=L0), record)
+        for i in range(n):
+            timed("perturb", lambda: zo.zo_perturb(ctx, theta, 0, s, i, +a), record)
+            if cfg.loss == "quad":
+                timed("loss", lambda: zo.zo_quad_loss(ctx, theta, a_dev, out=Lp[i:i + 1]), record)
+            timed("perturb", lambda: zo.zo_perturb(ctx, theta, 0, s, i, -a), record)
+            timed("perturb", lambda: zo.zo_perturb(ctx, theta, 0, s, i, -a), record)
+            if cfg.loss == "quad":
+                timed("loss", lambda: zo.zo_quad_loss(ctx, theta, a_dev, out=Lm[i:i + 1]), record)
+            timed("perturb", lambda: zo.zo_perturb(ctx, theta, 0, s, i, +a), record)
+        timed("weights", lambda: zo.zo_probe_weights(ctx, Lp, Lm, L0, a, cfg.delta, out=c_buf),
+              record)
+        timed("update", lambda: zo.zo_update(ctx, theta, 0, s, c_buf, cfg.eta), record)
+
+    for s in range(W):
+        one_step(s, False)
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {s} done")
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(W, total):
+        one_step(s, True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    log(f"[bench] {K} timed steps done in {t1 - t0:.2f} s")
+    nonfinite = zo.zo_nonfinite_count(ctx)
+
+    def avg_ms(kind):
+        xs = [e0.elapsed_time(e1) for e0, e1 in per[kind]]
+        return (sum(xs) / len(xs)) if xs else None
+
+    T = (t1 - t0) / K
+    value = n * M / T
+    pert_ms, upd_ms, w_ms = avg_ms("perturb"), avg_ms("update"), avg_ms("weights")
+    pass_bytes = 2.0 * esize * M                      # one read + one write of theta
+    step_bytes = (4 * n + 1) * pass_bytes             # 4 passes per probe + the update
+    achieved = pass_bytes / (pert_ms * 1e-3) / 1e9
+    traffic = stored_traffic(cfg.name, pass_bytes)
+    result = {
+        "metric": "probe*params/s and HBM GB/s (% peak) per 1.5-SPSA step, n_pert=160, 1 GPU",
+        "value": value,
+        "unit": "probe*params/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": T * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": (f"{cfg.name}: {M} {cfg.dtype} params in one flat buffer, "
+                                f"n_pert={n}, eps={cfg.eps}, eta={cfg.eta}, four passes per "
+                                f"probe, probes regenerated, losses "
+                                f"{'synthetic' if cfg.loss == 'synthetic' else cfg.loss}"),
+                   "params": M, "n_pert": n, "schedule": "4 passes per probe"},
+        "hbm_gbps": step_bytes / T / 1e9,
+        "hbm_frac_of_peak": step_bytes / T / 1e9 / PEAK_HBM_GBPS,
+        "kernels_ms": {"perturb_avg": pert_ms, "update_avg": upd_ms, "weights_avg": w_ms,
+                       "loss_avg": avg_ms("loss")},
+        "roofline": {"kernel": "k_perturb_chunks (zo_perturb, bf16 regenerate)"
+                     if cfg.dtype == "bf16" else "k_perturb_chunks (zo_perturb, fp32 regenerate)",
+                     "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": traffic},
+        "update_roofline": {"achieved_GBps": pass_bytes / (upd_ms * 1e-3) / 1e9,
+                            "probe_params_per_s": n * M / (upd_ms * 1e-3)},
+        "nonfinite_probes": nonfinite,
+        "cpu_baseline": cpu,
+    }
+    ctx.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,179 @@
+"""forward_only_amd -- the 1.5-SPSA perturb / probe-weight / update path on MI355X.
+
+A thin Python face over libzo.so (include/zo.h).  Each function below has the name of the
+C entry point it calls and only marshals arguments: it checks that tensors live on the
+GPU with the expected dtype, contiguity and alignment, then passes their device pointers
+and torch's current HIP stream.  All arithmetic runs in the library's HIP kernels;
+there is no CPU path.
+
+    ctx = zo_init(seed)
+    zo_perturb(ctx, theta, offset, step, probe, +eps)      # theta + eps*z_probe, in place
+    ...
+    c = zo_probe_weights(ctx, Lp, Lm, L0, eps, delta)
+    zo_update(ctx, theta, offset, step, c, eta)             # theta - eta * sum c_i z_i
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (ZO_BF16, ZO_EHIP, ZO_EINVAL, ZO_ENOMEM, ZO_EUNSUPPORTED, ZO_FP32,  # noqa: F401
+                   ZO_MAX_NPERT, ZO_OK, ZOError)
+
+__all__ = [
+    "Context", "ZOError", "zo_init", "zo_destroy", "zo_bits_stride", "zo_gen_probes",
+    "zo_perturb", "zo_probe_weights", "zo_update", "zo_nonfinite_count",
+    "zo_reset_nonfinite", "zo_quad_loss", "library_path",
+]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+class Context:
+    """Owns one zo_ctx (probe seed, device counter); closes it on close() / GC."""
+
+    def __init__(self, handle: int, seed: int):
+        self._h = handle
+        self.seed = seed
+
+    @property
+    def handle(self) -> int:
+        if not self._h:
+            raise ValueError("context is closed")
+        return self._h
+
+    def close(self) -> None:
+        if self._h:
+            h, self._h = self._h, None
+            _lib.check(_lib.lib().zo_destroy(h), "zo_destroy")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return ZO_FP32
+    if t.dtype == torch.bfloat16:
+        return ZO_BF16
+    raise TypeError(f"parameters must be float32 or bfloat16, got {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def zo_init(seed: int) -> Context:
+    h = ctypes.c_void_p()
+    _lib.check(_lib.lib().zo_init(int(seed) & (2 ** 64 - 1), ctypes.byref(h)), "zo_init")
+    return Context(h.value, int(seed))
+
+
+def zo_destroy(ctx: Context) -> None:
+    ctx.close()
+
+
+def zo_bits_stride(n: int) -> int:
+    return int(_lib.lib().zo_bits_stride(int(n)))
+
+
+def zo_gen_probes(ctx: Context, step: int, probe0: int, n_probes: int, offset: int, n: int,
+                  out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Packed sign rows, uint8 tensor of shape (n_probes, zo_bits_stride(n))."""
+    stride = zo_bits_stride(n)
+    if out is None:
+        out = torch.empty((n_probes, stride), dtype=torch.uint8, device="cuda")
+    if out.numel() < n_probes * stride:
+        raise ValueError("out is too small")
+    _lib.check(_lib.lib().zo_gen_probes(ctx.handle, step, probe0, n_probes, offset, n,
+                                        _dev(out, "out", torch.uint8), _stream(stream)),
+               "zo_gen_probes")
+    return out
+
+
+def zo_perturb(ctx: Context, theta: torch.Tensor, offset: int, step: int, probe: int,
+               alpha: float, bits: torch.Tensor | None = None, stream=None) -> None:
+    """theta <- theta + alpha * z_probe in place (theta fp32 or bf16)."""
+    bp = None if bits is None else _dev(bits, "bits", torch.uint8)
+    if bits is not None and bits.numel() < zo_bits_stride(theta.numel()):
+        raise ValueError("bits row is too short")
+    _lib.check(_lib.lib().zo_perturb(ctx.handle, _dev(theta, "theta"), _dtype_code(theta),
+                                     offset, theta.numel(), step, probe, float(alpha), bp,
+                                     _stream(stream)), "zo_perturb")
+
+
+def zo_probe_weights(ctx: Context, Lp: torch.Tensor, Lm: torch.Tensor, L0: torch.Tensor,
+                     eps: float, delta: float, out: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    """c_i = g_i / max(|h_i|, delta) from float64 GPU tensors Lp[n], Lm[n], L0[1]."""
+    n = Lp.numel()
+    if Lm.numel() != n or L0.numel() < 1:
+        raise ValueError("Lp and Lm must have the same length, L0 one element")
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device="cuda")
+    if out.numel() < n:
+        raise ValueError("out is too small")
+    _lib.check(_lib.lib().zo_probe_weights(
+        ctx.handle, _dev(Lp, "Lp", torch.float64), _dev(Lm, "Lm", torch.float64),
+        _dev(L0, "L0", torch.float64), n, float(eps), float(delta),
+        _dev(out, "out", torch.float32), _stream(stream)), "zo_probe_weights")
+    return out
+
+
+def zo_update(ctx: Context, theta: torch.Tensor, offset: int, step: int, c: torch.Tensor,
+              eta: float, bits: torch.Tensor | None = None, stream=None) -> None:
+    """theta <- theta - eta * sum_i c_i z_i in place; bits: (n_pert, stride) rows or None."""
+    npert = c.numel()
+    bp = None
+    if bits is not None:
+        bp = _dev(bits, "bits", torch.uint8)
+        if bits.numel() < npert * zo_bits_stride(theta.numel()):
+            raise ValueError("bits must hold n_pert rows")
+    _lib.check(_lib.lib().zo_update(ctx.handle, _dev(theta, "theta"), _dtype_code(theta),
+                                    offset, theta.numel(), step, _dev(c, "c", torch.float32),
+                                    npert, float(eta), bp, _stream(stream)), "zo_update")
+
+
+def zo_nonfinite_count(ctx: Context, stream=None) -> int:
+    v = ctypes.c_uint32()
+    _lib.check(_lib.lib().zo_nonfinite_count(ctx.handle, _stream(stream), ctypes.byref(v)),
+               "zo_nonfinite_count")
+    return int(v.value)
+
+
+def zo_reset_nonfinite(ctx: Context, stream=None) -> None:
+    _lib.check(_lib.lib().zo_reset_nonfinite(ctx.handle, _stream(stream)), "zo_reset_nonfinite")
+
+
+def zo_quad_loss(ctx: Context, theta: torch.Tensor, a: torch.Tensor,
+                 out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """1/2 sum a_j theta_j^2 in fp64 into a one-element float64 GPU tensor."""
+    if a.numel() != theta.numel():
+        raise ValueError("a and theta must have the same length")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float64, device="cuda")
+    _lib.check(_lib.lib().zo_quad_loss(ctx.handle, _dev(theta, "theta"), _dtype_code(theta),
+                                       _dev(a, "a", torch.float32), theta.numel(),
+                                       _dev(out, "out", torch.float64), _stream(stream)),
+               "zo_quad_loss")
+    return out

@@ -1,0 +1,181 @@
+// api.hip -- the extern "C" boundary of libzo: context, argument validation, launches.
+// Every check happens before any launch; a rejected call touches no device memory.
+#include <new>
+
+#include "../../include/zo.h"
+#include "zo_launch.hpp"
+
+struct zo_ctx {
+    uint64_t seed;
+    int device;
+    int num_cus;
+    uint32_t *d_counter;   // non-finite probe counter
+    double *d_partials;    // quadratic-loss partial sums (zo::kLossPartials doubles)
+};
+
+namespace {
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline zo::Key key_of(const zo_ctx *c) { return {(uint32_t)c->seed, (uint32_t)(c->seed >> 32)}; }
+
+inline hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+inline zo_status from_hip(hipError_t e) { return e == hipSuccess ? ZO_OK : ZO_EHIP; }
+
+// Common checks for a parameter range [offset, offset + n).
+inline bool range_ok(uint64_t offset, uint64_t n)
+{
+    if (offset % 128u != 0) return false;
+    if (n > UINT64_MAX - offset) return false;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *zo_strerror(zo_status s)
+{
+    switch (s) {
+    case ZO_OK: return "ok";
+    case ZO_EINVAL: return "invalid argument";
+    case ZO_EHIP: return "HIP runtime error";
+    case ZO_ENOMEM: return "out of memory";
+    case ZO_EUNSUPPORTED: return "unsupported request (beyond a documented limit)";
+    }
+    return "unknown status";
+}
+
+uint64_t zo_bits_stride(uint64_t n) { return ((n + 127u) / 128u) * 16u; }
+
+zo_status zo_init(uint64_t seed, zo_ctx **out)
+{
+    if (!out) return ZO_EINVAL;
+    zo_ctx *c = new (std::nothrow) zo_ctx{};
+    if (!c) return ZO_ENOMEM;
+    c->seed = seed;
+    if (hipGetDevice(&c->device) != hipSuccess ||
+        hipDeviceGetAttribute(&c->num_cus, hipDeviceAttributeMultiprocessorCount, c->device) !=
+            hipSuccess ||
+        c->num_cus <= 0) {
+        delete c;
+        (void)hipGetLastError();
+        return ZO_EHIP;
+    }
+    if (hipMalloc(reinterpret_cast<void **>(&c->d_counter), 256) != hipSuccess) {
+        delete c;
+        (void)hipGetLastError();
+        return ZO_ENOMEM;
+    }
+    if (hipMalloc(reinterpret_cast<void **>(&c->d_partials), zo::kLossPartials * sizeof(double)) !=
+        hipSuccess) {
+        (void)hipFree(c->d_counter);
+        delete c;
+        (void)hipGetLastError();
+        return ZO_ENOMEM;
+    }
+    if (zo::launch_zero_u32(c->d_counter, 64, nullptr) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(c->d_partials);
+        (void)hipFree(c->d_counter);
+        delete c;
+        return ZO_EHIP;
+    }
+    *out = c;
+    return ZO_OK;
+}
+
+zo_status zo_destroy(zo_ctx *c)
+{
+    if (!c) return ZO_OK;
+    hipError_t e = hipDeviceSynchronize();
+    if (c->d_partials) (void)hipFree(c->d_partials);
+    if (c->d_counter) (void)hipFree(c->d_counter);
+    delete c;
+    return from_hip(e);
+}
+
+uint64_t zo_get_seed(const zo_ctx *c) { return c ? c->seed : 0; }
+
+zo_status zo_gen_probes(zo_ctx *c, uint32_t step, uint32_t probe0, uint32_t n_probes,
+                        uint64_t offset, uint64_t n, uint8_t *d_bits, void *stream)
+{
+    if (!c) return ZO_EINVAL;
+    if (!range_ok(offset, n)) return ZO_EINVAL;
+    if (n == 0 || n_probes == 0) return ZO_OK;
+    if (!d_bits || !aligned16(d_bits)) return ZO_EINVAL;
+    return from_hip(zo::launch_gen_probes(key_of(c), step, probe0, n_probes, offset, n, d_bits,
+                                          c->num_cus, as_stream(stream)));
+}
+
+zo_status zo_perturb(zo_ctx *c, void *d_theta, zo_dtype dtype, uint64_t offset, uint64_t n,
+                     uint32_t step, uint32_t probe, float alpha, const uint8_t *d_bits,
+                     void *stream)
+{
+    if (!c) return ZO_EINVAL;
+    if (dtype != ZO_FP32 && dtype != ZO_BF16) return ZO_EINVAL;
+    if (!range_ok(offset, n)) return ZO_EINVAL;
+    if (n == 0) return ZO_OK;
+    if (!d_theta || !aligned16(d_theta)) return ZO_EINVAL;
+    if (d_bits && !aligned16(d_bits)) return ZO_EINVAL;
+    return from_hip(zo::launch_perturb(d_theta, dtype == ZO_BF16, offset, n, key_of(c), step,
+                                       probe, alpha, d_bits, c->num_cus, as_stream(stream)));
+}
+
+zo_status zo_probe_weights(zo_ctx *c, const double *d_Lp, const double *d_Lm,
+                           const double *d_L0, uint32_t n_pert, double eps, double delta,
+                           float *d_c, void *stream)
+{
+    if (!c) return ZO_EINVAL;
+    if (!(eps == eps) || eps == 0.0 || eps - eps != 0.0) return ZO_EINVAL;       // NaN/0/inf
+    if (!(delta >= 0.0) || delta - delta != 0.0) return ZO_EINVAL;               // <0/NaN/inf
+    if (n_pert == 0) return ZO_OK;
+    if (!d_Lp || !d_Lm || !d_L0 || !d_c) return ZO_EINVAL;
+    return from_hip(zo::launch_probe_weights(d_Lp, d_Lm, d_L0, n_pert, eps, delta, d_c,
+                                             c->d_counter, as_stream(stream)));
+}
+
+zo_status zo_update(zo_ctx *c, void *d_theta, zo_dtype dtype, uint64_t offset, uint64_t n,
+                    uint32_t step, const float *d_c, uint32_t n_pert, float eta,
+                    const uint8_t *d_bits, void *stream)
+{
+    if (!c) return ZO_EINVAL;
+    if (dtype != ZO_FP32 && dtype != ZO_BF16) return ZO_EINVAL;
+    if (!range_ok(offset, n)) return ZO_EINVAL;
+    if (n_pert > ZO_MAX_NPERT) return ZO_EUNSUPPORTED;
+    if (n == 0 || n_pert == 0) return ZO_OK;
+    if (!d_theta || !aligned16(d_theta) || !d_c) return ZO_EINVAL;
+    if (d_bits && !aligned16(d_bits)) return ZO_EINVAL;
+    return from_hip(zo::launch_update(d_theta, dtype == ZO_BF16, offset, n, key_of(c), step, d_c,
+                                      n_pert, eta, d_bits, c->num_cus, as_stream(stream)));
+}
+
+zo_status zo_nonfinite_count(zo_ctx *c, void *stream, uint32_t *out)
+{
+    if (!c || !out) return ZO_EINVAL;
+    if (hipStreamSynchronize(as_stream(stream)) != hipSuccess) return ZO_EHIP;
+    uint32_t v = 0;
+    if (hipMemcpy(&v, c->d_counter, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess)
+        return ZO_EHIP;
+    *out = v;
+    return ZO_OK;
+}
+
+zo_status zo_reset_nonfinite(zo_ctx *c, void *stream)
+{
+    if (!c) return ZO_EINVAL;
+    return from_hip(zo::launch_zero_u32(c->d_counter, 1, as_stream(stream)));
+}
+
+zo_status zo_quad_loss(zo_ctx *c, const void *d_theta, zo_dtype dtype, const float *d_a,
+                       uint64_t n, double *d_out, void *stream)
+{
+    if (!c || !d_out) return ZO_EINVAL;
+    if (dtype != ZO_FP32 && dtype != ZO_BF16) return ZO_EINVAL;
+    if (n > 0 && (!d_theta || !d_a || !aligned16(d_theta) || !aligned16(d_a))) return ZO_EINVAL;
+    return from_hip(zo::launch_quad_loss(d_theta, dtype == ZO_BF16, d_a, n, c->d_partials, d_out,
+                                         as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,177 @@
+// k_perturb.hip -- in-place perturbation theta <- round(theta + alpha * z) of one probe,
+// the fused unpack/apply step of 1.5-SPSA (abstract of "Probe-Space Preconditioning for
+// Fast and Stable Zero-Order Training"; the moves to theta +/- eps*z_i of "How 1.5-SPSA
+// Works" on "Stanford's 1.5-SPSA Trains OPT-30B Without Backpropagation").
+//
+// Layout and mapping (gfx950, wave64):
+//  * A wave owns a chunk of 64 Philox blocks = 8192 consecutive params per iteration
+//    (16 KiB of bf16, 32 KiB of fp32) and walks the buffer grid-stride.
+//  * Each lane issues its 16 (bf16) or 32 (fp32) global_load_dwordx4 first; load k of
+//    lane L covers 16 bytes at chunk + 1 KiB*k + 16*L, so every load instruction moves
+//    one contiguous KiB per wave.
+//  * While those loads are in flight, lane L computes Philox for block L of the chunk
+//    (or reads its 16 bytes of a stored plane) and writes the 16 bytes to a 1 KiB LDS
+//    slice private to the wave.  The chunk's sign bits are then a linear 1 KiB array:
+//    bf16 load k of lane L needs byte 64k + L, fp32 load k needs the nibble
+//    (L & 1) of byte 32k + L/2 -- one ds_read_u8 each, with the load index folded
+//    into the instruction's offset.
+//  * Apply: flip alpha's sign bit when the param's bit is clear, one fp32 add, and for
+//    bf16 one v_cvt_pk_bf16_f32 (round to nearest even) per pair; store dwordx4.
+//  * The ragged end (fewer than 8192 params) goes to a small per-element kernel.
+// Every element is read once and written once; no element is touched by two lanes.
+#include <stdlib.h>
+
+#include "zo_device.hpp"
+#include "zo_launch.hpp"
+
+namespace zo {
+
+constexpr int kChunkParams = kWave * kBlockParams;  // 8192
+constexpr int kWavesPerWG = 4;
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <bool kBF16, bool kBits>
+__global__ __launch_bounds__(256) void k_perturb_chunks(u32x4_t *__restrict__ theta,
+                                                        uint64_t nchunks, uint64_t blk0,
+                                                        uint32_t step, uint32_t probe,
+                                                        uint32_t k0, uint32_t k1,
+                                                        uint32_t abits,
+                                                        const u32x4_t *__restrict__ bits)
+{
+    constexpr int kPerLoad = kBF16 ? 8 : 4;                      // params per 16 bytes
+    constexpr int kLoads = kChunkParams / (kPerLoad * kWave);   // 16 or 32
+    __shared__ u32x4_t xch_all[kWavesPerWG][kWave];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    u32x4_t *xch = xch_all[wv];
+    const uint8_t *xb = reinterpret_cast<const uint8_t *>(xch);
+    const uint64_t nwaves = (uint64_t)gridDim.x * kWavesPerWG;
+
+    for (uint64_t ch = (uint64_t)blockIdx.x * kWavesPerWG + wv; ch < nchunks; ch += nwaves) {
+        u32x4_t *base = theta + ch * (uint64_t)(kChunkParams / kPerLoad) + lane;
+        u32x4_t v[kLoads];
+#pragma unroll
+        for (int k = 0; k < kLoads; ++k) v[k] = __builtin_nontemporal_load(base + k * kWave);
+
+        const uint64_t lb = ch * kWave + lane;  // block index local to the buffer
+        u32x4_t w;
+        if constexpr (kBits) {
+            w = bits[lb];
+        } else {
+            const U32x4 r = probe_block_bits(blk0 + lb, probe, step, k0, k1);
+            w = u32x4_t{r.x, r.y, r.z, r.w};
+        }
+        wave_lds_sync();  // the previous chunk's byte reads precede this overwrite
+        xch[lane] = w;
+        wave_lds_sync();
+
+#pragma unroll
+        for (int k = 0; k < kLoads; ++k) {
+            uint32_t m;
+            if constexpr (kBF16) {
+                m = xb[64 * k + lane];
+            } else {
+                m = (uint32_t)xb[32 * k + (lane >> 1)] >> (4 * (lane & 1));
+            }
+            const uint32_t nm = ~m;
+            u32x4_t q = v[k];
+            if constexpr (kBF16) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float lo = bf16lo_to_f32(q[j]) + signed_alpha(nm, 2 * j, abits);
+                    const float hi = bf16hi_to_f32(q[j]) + signed_alpha(nm, 2 * j + 1, abits);
+                    q[j] = pack_bf16x2(lo, hi);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    q[j] = __float_as_uint(__uint_as_float(q[j]) + signed_alpha(nm, j, abits));
+            }
+            __builtin_nontemporal_store(q, base + k * kWave);
+        }
+    }
+}
+
+// Ragged end: one thread per element of [start, n).
+template <bool kBF16, bool kBits>
+__global__ __launch_bounds__(256) void k_perturb_tail(void *__restrict__ theta, uint64_t start,
+                                                      uint64_t n, uint64_t blk0, uint32_t step,
+                                                      uint32_t probe, uint32_t k0, uint32_t k1,
+                                                      uint32_t abits,
+                                                      const uint8_t *__restrict__ bits)
+{
+    const uint64_t e = start + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= n) return;
+    uint32_t bit;
+    if constexpr (kBits) {
+        bit = (bits[e >> 3] >> (e & 7)) & 1u;
+    } else {
+        const U32x4 r = probe_block_bits(blk0 + (e >> 7), probe, step, k0, k1);
+        const uint32_t sel = (uint32_t)(e >> 5) & 3u;
+        const uint32_t word = sel == 0 ? r.x : sel == 1 ? r.y : sel == 2 ? r.z : r.w;
+        bit = (word >> (e & 31)) & 1u;
+    }
+    const float a = __uint_as_float(abits ^ (bit ? 0u : 0x80000000u));
+    if constexpr (kBF16) {
+        uint16_t *t = static_cast<uint16_t *>(theta);
+        const float f = __uint_as_float((uint32_t)t[e] << 16) + a;
+        t[e] = (uint16_t)(pack_bf16x2(f, 0.0f) & 0xFFFFu);
+    } else {
+        float *t = static_cast<float *>(theta);
+        t[e] = t[e] + a;
+    }
+}
+
+static int env_int(const char *name, int dflt)
+{
+    const char *s = getenv(name);
+    if (!s || !*s) return dflt;
+    const int v = atoi(s);
+    return v > 0 ? v : dflt;
+}
+
+template <bool kBF16, bool kBits>
+static hipError_t perturb_impl(void *theta, uint64_t n, uint64_t blk0, uint32_t step,
+                               uint32_t probe, Key key, uint32_t abits, const uint8_t *bits,
+                               int num_cus, hipStream_t stream)
+{
+    const uint64_t nchunks = n / kChunkParams;
+    if (nchunks) {
+        // Persistent grid: a few resident workgroups per CU, each wave loops over chunks.
+        static const int wg_per_cu = env_int("ZO_PERTURB_WG_PER_CU", 8);
+        const uint64_t want = (nchunks + kWavesPerWG - 1) / kWavesPerWG;
+        const uint64_t cap = (uint64_t)num_cus * wg_per_cu;
+        const uint32_t grid = (uint32_t)(want < cap ? want : cap);
+        hipLaunchKernelGGL((k_perturb_chunks<kBF16, kBits>), dim3(grid), dim3(256), 0, stream,
+                           static_cast<u32x4_t *>(theta), nchunks, blk0, step, probe, key.k0,
+                           key.k1, abits, reinterpret_cast<const u32x4_t *>(bits));
+    }
+    const uint64_t start = nchunks * kChunkParams;
+    if (start < n) {
+        const uint32_t grid = (uint32_t)((n - start + 255) / 256);
+        hipLaunchKernelGGL((k_perturb_tail<kBF16, kBits>), dim3(grid), dim3(256), 0, stream,
+                           theta, start, n, blk0, step, probe, key.k0, key.k1, abits, bits);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_perturb(void *theta, bool bf16, uint64_t offset, uint64_t n, Key key,
+                          uint32_t step, uint32_t probe, float alpha, const uint8_t *bits,
+                          int num_cus, hipStream_t stream)
+{
+    const uint32_t abits = __builtin_bit_cast(uint32_t, alpha);
+    const uint64_t blk0 = offset / kBlockParams;
+    if (bf16)
+        return bits ? perturb_impl<true, true>(theta, n, blk0, step, probe, key, abits, bits,
+                                               num_cus, stream)
+                    : perturb_impl<true, false>(theta, n, blk0, step, probe, key, abits,
+                                                bits, num_cus, stream);
+    return bits ? perturb_impl<false, true>(theta, n, blk0, step, probe, key, abits, bits,
+                                            num_cus, stream)
+                : perturb_impl<false, false>(theta, n, blk0, step, probe, key, abits, bits,
+                                             num_cus, stream);
+}
+
+}  // namespace zo

@@ -1,0 +1,266 @@
+// k_update.hip -- fused multi-probe update theta <- round(theta - eta * sum_i c_i z_i)
+// (the update box of the ZOO loop flowchart in "Pretraining Transformers Without Backprop:
+// What Two Zero-Order Papers Actually Measure"; the probe sum of "How 1.5-SPSA Works" on
+// "Stanford's 1.5-SPSA Trains OPT-30B Without Backpropagation").
+//
+// Design (gfx950, wave64, 256-thread workgroups):
+//  * Tables.  Probes are taken eight at a time (group g = probes 8g .. 8g+7).  For each
+//    group the workgroup builds T_g[b] = sum_{k<8} (bit k of b ? +c : -c)_{8g+k} for all
+//    256 byte values b (k ascending, fp64) in LDS; n_pert = 160 needs 40 KiB.  Probes past
+//    n_pert are padded with c = 0.  Then s_j = sum_g T_g[b_gj] with b_gj the byte whose bit
+//    k is the sign bit of probe 8g+k at param j -- one LDS lookup per 8 probes.
+//  * Precision.  Tables and sums are fp64 (full-rate VALU adds on CDNA4), so s_j carries
+//    ~1e-16 relative error; the new value is (double)theta - (double)eta * s_j, rounded
+//    once: to fp32 directly, or to bf16 through round-to-odd fp32 and the hardware
+//    nearest-even fp32->bf16 convert, which together round the double correctly.  With
+//    fp32 sums the update could miss the bf16 result by several ulps wherever theta and
+//    eta*s nearly cancel.
+//  * Work split.  A wave takes 8 consecutive 128-param blocks; the 8 lanes of an "octet"
+//    share one block.  Per group, lane r of an octet produces probe 8g+r's 128 bits for
+//    that block (Philox, or 16 bytes of a stored row), so no Philox call is repeated.
+//    The octet swaps 32-bit words through a 1 KiB per-wave LDS slice so that lane r
+//    holds the 16 bits of all eight probes for its own 16 params 16r .. 16r+15; four
+//    v_perm_b32 select bytes and two 8x8 bit transposes turn them into 16 table indices.
+//  * Each lane keeps 16 fp64 sums (tables in ascending group order), then reads its 16
+//    params once, forms and rounds the new values, and writes them once.
+//  * Deterministic: every sum is taken in a fixed order independent of the grid.
+#include <stdlib.h>
+
+#include "zo_device.hpp"
+#include "zo_launch.hpp"
+
+namespace zo {
+
+constexpr int kUpdWavesPerWG = 8;
+constexpr int kUpdThreads = kUpdWavesPerWG * kWave;
+constexpr int kUpdBlocksPerWave = 8;
+constexpr uint32_t kXchWordsPerWave = 256;  // 8 octets x 8 lanes x 4 words
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// In-register transpose of an 8x8 bit matrix held as two dwords (rows 0-3 in L, rows
+// 4-7 in H, row k = byte k, column b = bit b): afterwards byte b holds column b.
+// Three masked delta swaps (distances 7, 14, 28 in the 64-bit view).
+__device__ __forceinline__ void transpose8x8(uint32_t &L, uint32_t &H)
+{
+    uint32_t t;
+    t = (L ^ (L >> 7)) & 0x00AA00AAu;
+    L = L ^ t ^ (t << 7);
+    t = (H ^ (H >> 7)) & 0x00AA00AAu;
+    H = H ^ t ^ (t << 7);
+    t = (L ^ (L >> 14)) & 0x0000CCCCu;
+    L = L ^ t ^ (t << 14);
+    t = (H ^ (H >> 14)) & 0x0000CCCCu;
+    H = H ^ t ^ (t << 14);
+    t = (L ^ (H << 4)) & 0xF0F0F0F0u;
+    L = L ^ t;
+    H = H ^ (t >> 4);
+}
+
+// double -> fp32 rounded to odd: truncate toward zero, then set the last bit if anything
+// was lost.  A later round-to-nearest-even to a format with at least two fewer
+// significand bits (bf16 has 8 against fp32's 24) then rounds the double correctly.
+__device__ __forceinline__ float f64_to_f32_round_odd(double d)
+{
+    const float f = (float)d;
+    const double back = (double)f;
+    uint32_t u = __float_as_uint(f);
+    if (__builtin_fabs(back) > __builtin_fabs(d)) u -= 1u;   // RNE rounded away from zero
+    if (back != d) u |= 1u;                                  // inexact (NaN stays NaN)
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint32_t bf16pair_from_f64(double lo, double hi)
+{
+    return pack_bf16x2(f64_to_f32_round_odd(lo), f64_to_f32_round_odd(hi));
+}
+
+template <bool kBF16>
+__device__ __forceinline__ void apply_update(void *theta, uint64_t e0, uint64_t n,
+                                             const double (&s)[16], double eta)
+{
+    if (e0 + 16 <= n) {
+        if constexpr (kBF16) {
+            u32x4_t *p = reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(theta) + e0);
+            u32x4_t t0 = __builtin_nontemporal_load(p);
+            u32x4_t t1 = __builtin_nontemporal_load(p + 1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                t0[j] = bf16pair_from_f64((double)bf16lo_to_f32(t0[j]) - eta * s[2 * j],
+                                          (double)bf16hi_to_f32(t0[j]) - eta * s[2 * j + 1]);
+                t1[j] = bf16pair_from_f64((double)bf16lo_to_f32(t1[j]) - eta * s[8 + 2 * j],
+                                          (double)bf16hi_to_f32(t1[j]) - eta * s[9 + 2 * j]);
+            }
+            __builtin_nontemporal_store(t0, p);
+            __builtin_nontemporal_store(t1, p + 1);
+        } else {
+            u32x4_t *p = reinterpret_cast<u32x4_t *>(static_cast<float *>(theta) + e0);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                u32x4_t t = __builtin_nontemporal_load(p + v);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    t[j] = __float_as_uint(
+                        (float)((double)__uint_as_float(t[j]) - eta * s[4 * v + j]));
+                __builtin_nontemporal_store(t, p + v);
+            }
+        }
+    } else if (e0 < n) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const uint64_t e = e0 + q;
+            if (e < n) {
+                if constexpr (kBF16) {
+                    uint16_t *t = static_cast<uint16_t *>(theta);
+                    const double v = (double)__uint_as_float((uint32_t)t[e] << 16) - eta * s[q];
+                    t[e] = (uint16_t)(bf16pair_from_f64(v, 0.0) & 0xFFFFu);
+                } else {
+                    float *t = static_cast<float *>(theta);
+                    t[e] = (float)((double)t[e] - eta * s[q]);
+                }
+            }
+        }
+    }
+}
+
+template <bool kBF16, bool kBits>
+__global__ __launch_bounds__(kUpdThreads) void k_update(void *__restrict__ theta, uint64_t n,
+                                                        uint64_t blk0, uint32_t step,
+                                                        uint32_t k0, uint32_t k1,
+                                                        const float *__restrict__ c,
+                                                        uint32_t npert, uint32_t ngroups,
+                                                        double eta,
+                                                        const uint8_t *__restrict__ bits,
+                                                        uint64_t stride)
+{
+    extern __shared__ double lds_d[];
+    double *tbl = lds_d;
+    const int wv = threadIdx.x / kWave;
+    uint32_t *xch = reinterpret_cast<uint32_t *>(lds_d + ngroups * 256u) + wv * kXchWordsPerWave;
+
+    // Signed partial-sum tables, probes ascending within each group.
+    for (uint32_t e = threadIdx.x; e < ngroups * 256u; e += blockDim.x) {
+        const uint32_t g = e >> 8, b = e & 255u;
+        double acc = 0.0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t i = g * 8u + (uint32_t)k;
+            const double ci = i < npert ? (double)c[i] : 0.0;
+            acc = acc + (((b >> k) & 1u) ? ci : -ci);
+        }
+        tbl[e] = acc;
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int oct = lane >> 3;
+    const int r = lane & 7;
+    uint32_t *oxch = xch + oct * 32;
+    const uint32_t beta = 2u * (uint32_t)(r & 1);
+    // byte beta of x, byte beta of y, byte beta+1 of x, byte beta+1 of y
+    const uint32_t sel = beta | ((4u + beta) << 8) | ((beta + 1u) << 16) | ((5u + beta) << 24);
+
+    const uint64_t nblk = (n + kBlockParams - 1) / kBlockParams;
+    const uint64_t nwc = (nblk + kUpdBlocksPerWave - 1) / kUpdBlocksPerWave;
+    const uint64_t nwaves = (uint64_t)gridDim.x * kUpdWavesPerWG;
+
+    for (uint64_t wc = (uint64_t)blockIdx.x * kUpdWavesPerWG + wv; wc < nwc; wc += nwaves) {
+        const uint64_t lb = wc * kUpdBlocksPerWave + oct;  // local block of this octet
+        const uint64_t e0 = lb * kBlockParams + 16u * (uint32_t)r;
+        double s[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) s[q] = 0.0;
+
+        for (uint32_t g = 0; g < ngroups; ++g) {
+            const uint32_t i = g * 8u + (uint32_t)r;
+            u32x4_t w = {0u, 0u, 0u, 0u};
+            if (i < npert) {
+                if constexpr (kBits) {
+                    if (lb < nblk)
+                        w = *reinterpret_cast<const u32x4_t *>(bits + (uint64_t)i * stride + lb * 16u);
+                } else {
+                    const U32x4 q = probe_block_bits(blk0 + lb, i, step, k0, k1);
+                    w = u32x4_t{q.x, q.y, q.z, q.w};
+                }
+            }
+            wave_lds_sync();  // previous group's reads precede these writes
+            oxch[0 * 8 + r] = w.x;
+            oxch[1 * 8 + r] = w.y;
+            oxch[2 * 8 + r] = w.z;
+            oxch[3 * 8 + r] = w.w;
+            wave_lds_sync();
+            // word (r >> 1) of probes 0..3 and 4..7 of the group
+            const u32x4_t a = *reinterpret_cast<const u32x4_t *>(oxch + (r >> 1) * 8);
+            const u32x4_t b = *reinterpret_cast<const u32x4_t *>(oxch + (r >> 1) * 8 + 4);
+            const uint32_t a01 = __builtin_amdgcn_perm(a.y, a.x, sel);
+            const uint32_t a23 = __builtin_amdgcn_perm(a.w, a.z, sel);
+            const uint32_t b01 = __builtin_amdgcn_perm(b.y, b.x, sel);
+            const uint32_t b23 = __builtin_amdgcn_perm(b.w, b.z, sel);
+            uint32_t Llo = __builtin_amdgcn_perm(a23, a01, 0x05040100u);
+            uint32_t Hlo = __builtin_amdgcn_perm(b23, b01, 0x05040100u);
+            uint32_t Lhi = __builtin_amdgcn_perm(a23, a01, 0x07060302u);
+            uint32_t Hhi = __builtin_amdgcn_perm(b23, b01, 0x07060302u);
+            transpose8x8(Llo, Hlo);
+            transpose8x8(Lhi, Hhi);
+            const double *tg = tbl + g * 256u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                s[q] += tg[(Llo >> (8 * q)) & 255u];
+                s[4 + q] += tg[(Hlo >> (8 * q)) & 255u];
+                s[8 + q] += tg[(Lhi >> (8 * q)) & 255u];
+                s[12 + q] += tg[(Hhi >> (8 * q)) & 255u];
+            }
+        }
+        apply_update<kBF16>(theta, e0, n, s, eta);
+    }
+}
+
+static int env_int(const char *name, int dflt)
+{
+    const char *s = getenv(name);
+    if (!s || !*s) return dflt;
+    const int v = atoi(s);
+    return v > 0 ? v : dflt;
+}
+
+template <bool kBF16, bool kBits>
+static hipError_t update_impl(void *theta, uint64_t n, uint64_t blk0, uint32_t step, Key key,
+                              const float *c, uint32_t npert, float eta, const uint8_t *bits,
+                              int num_cus, hipStream_t stream)
+{
+    const uint32_t ngroups = (npert + 7u) / 8u;
+    const size_t lds = (size_t)ngroups * 256u * 8u + (size_t)kUpdWavesPerWG * kXchWordsPerWave * 4u;
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_update<kBF16, kBits>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    const uint64_t nblk = (n + kBlockParams - 1) / kBlockParams;
+    const uint64_t nwc = (nblk + kUpdBlocksPerWave - 1) / kUpdBlocksPerWave;
+    static const int wg_per_cu = env_int("ZO_UPDATE_WG_PER_CU", 4);
+    const uint64_t want = (nwc + kUpdWavesPerWG - 1) / kUpdWavesPerWG;
+    const uint64_t cap = (uint64_t)num_cus * wg_per_cu;
+    const uint32_t grid = (uint32_t)(want < cap ? want : cap);
+    hipLaunchKernelGGL((k_update<kBF16, kBits>), dim3(grid), dim3(kUpdThreads), lds, stream,
+                       theta, n, blk0, step, key.k0, key.k1, c, npert, ngroups, (double)eta,
+                       bits, (uint64_t)nblk * 16u);
+    return hipGetLastError();
+}
+
+hipError_t launch_update(void *theta, bool bf16, uint64_t offset, uint64_t n, Key key,
+                         uint32_t step, const float *c, uint32_t npert, float eta,
+                         const uint8_t *bits, int num_cus, hipStream_t stream)
+{
+    const uint64_t blk0 = offset / kBlockParams;
+    if (bf16)
+        return bits ? update_impl<true, true>(theta, n, blk0, step, key, c, npert, eta, bits,
+                                              num_cus, stream)
+                    : update_impl<true, false>(theta, n, blk0, step, key, c, npert, eta, bits,
+                                               num_cus, stream);
+    return bits ? update_impl<false, true>(theta, n, blk0, step, key, c, npert, eta, bits,
+                                           num_cus, stream)
+                : update_impl<false, false>(theta, n, blk0, step, key, c, npert, eta, bits,
+                                            num_cus, stream);
+}
+
+}  // namespace zo

@@ -1,0 +1,42 @@
+// zo_launch.hpp -- host-side launchers of the gfx950 kernels (internal to libzo).
+// Arguments are validated by the C ABI layer (api.hip) before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace zo {
+
+struct Key {
+    uint32_t k0, k1;  // Philox key = (seed_lo, seed_hi)
+};
+
+// Packed sign rows: rows of ceil(n/128)*16 bytes for probes probe0 .. probe0+nprobes-1.
+hipError_t launch_gen_probes(Key key, uint32_t step, uint32_t probe0, uint32_t nprobes,
+                             uint64_t offset, uint64_t n, uint8_t *bits, int num_cus,
+                             hipStream_t stream);
+
+// theta[0..n) += alpha * z (fp32 or bf16), bits == nullptr regenerates.
+hipError_t launch_perturb(void *theta, bool bf16, uint64_t offset, uint64_t n, Key key,
+                          uint32_t step, uint32_t probe, float alpha, const uint8_t *bits,
+                          int num_cus, hipStream_t stream);
+
+// c[i] from (L+, L-, L0) in fp64; non-finite probes counted into *counter.
+hipError_t launch_probe_weights(const double *Lp, const double *Lm, const double *L0,
+                                uint32_t npert, double eps, double delta, float *c,
+                                uint32_t *counter, hipStream_t stream);
+
+// theta[0..n) -= eta * sum_i c_i z_i through per-8-probe LDS tables.
+hipError_t launch_update(void *theta, bool bf16, uint64_t offset, uint64_t n, Key key,
+                         uint32_t step, const float *c, uint32_t npert, float eta,
+                         const uint8_t *bits, int num_cus, hipStream_t stream);
+
+// counter[0] = 0 with a fill kernel (no memset node if the caller captures a graph).
+hipError_t launch_zero_u32(uint32_t *p, uint32_t count, hipStream_t stream);
+
+// 1/2 sum a_j theta_j^2 in fp64, two deterministic passes through `partials`.
+constexpr uint32_t kLossPartials = 1024;
+hipError_t launch_quad_loss(const void *theta, bool bf16, const float *a, uint64_t n,
+                            double *partials, double *out, hipStream_t stream);
+
+}  // namespace zo

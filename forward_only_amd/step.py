@@ -1,0 +1,63 @@
+"""One 1.5-SPSA step on the GPU, sequenced from the C entry points.
+
+Order of work ("Stanford's 1.5-SPSA Trains OPT-30B Without Backpropagation", sections "How
+1.5-SPSA Works" and "Probe-Space Preconditioning"; the ZOO loop flowchart of "Pretraining
+Transformers Without Backprop: What Two Zero-Order Papers Actually Measure"): the clean
+loss, then per probe four in-place passes +eps, -eps (restore), -eps, +eps (restore) with
+a loss after the first and third, then the probe weights, then one update pass.
+
+Python only orders the launches; every pass over the parameters, the weights and the
+update run in libzo's kernels on torch's current stream.  Losses stay on the device.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import zo_perturb, zo_probe_weights, zo_update
+
+
+def applied_eps(eps: float) -> float:
+    """The step the passes really add: eps rounded to fp32."""
+    return float(np.float32(eps))
+
+
+def spsa_step(ctx, theta: torch.Tensor, *, step: int, npert: int, eps: float, eta: float,
+              delta: float, loss=None, losses=None, offset: int = 0, bits=None,
+              buffers: dict | None = None) -> dict:
+    """Run one step in place on `theta`.
+
+    loss(theta, out) writes the loss at `theta` into the one-element float64 GPU tensor
+    `out`; alternatively `losses` = (L0[1], Lp[n], Lm[n]) float64 GPU tensors supply them
+    (synthetic or measured elsewhere) and the perturb / restore passes still run.
+    bits: optional (npert, stride) uint8 GPU tensor of packed rows (else regenerated).
+    Returns the device tensors L0, Lp, Lm and c.
+    """
+    a = applied_eps(eps)
+    b = buffers if buffers is not None else {}
+    if losses is not None:
+        L0, Lp, Lm = losses
+    else:
+        L0 = b.get("L0")
+        if L0 is None:
+            L0 = torch.empty(1, dtype=torch.float64, device=theta.device)
+        Lp = b.get("Lp")
+        if Lp is None:
+            Lp = torch.empty(npert, dtype=torch.float64, device=theta.device)
+        Lm = b.get("Lm")
+        if Lm is None:
+            Lm = torch.empty(npert, dtype=torch.float64, device=theta.device)
+        loss(theta, L0)
+    for i in range(npert):
+        row = None if bits is None else bits[i]
+        zo_perturb(ctx, theta, offset, step, i, +a, row)
+        if losses is None:
+            loss(theta, Lp[i:i + 1])
+        zo_perturb(ctx, theta, offset, step, i, -a, row)
+        zo_perturb(ctx, theta, offset, step, i, -a, row)
+        if losses is None:
+            loss(theta, Lm[i:i + 1])
+        zo_perturb(ctx, theta, offset, step, i, +a, row)
+    c = zo_probe_weights(ctx, Lp, Lm, L0, a, delta, out=b.get("c"))
+    zo_update(ctx, theta, offset, step, c, eta, bits)
+    return {"L0": L0, "Lp": Lp, "Lm": Lm, "c": c}

@@ -1,0 +1,149 @@
+/*
+ * zo.h -- C ABI of the 1.5-SPSA perturb / probe-weight / update library (libzo.so),
+ * hand-written HIP kernels for gfx950 (MI355X).
+ *
+ * The method ("Probe-Space Preconditioning for Fast and Stable Zero-Order Training",
+ * described on "Stanford's 1.5-SPSA Trains OPT-30B Without Backpropagation"): each step
+ * draws n_pert Rademacher probes z_i, evaluates the loss at the clean parameters and at
+ * theta +/- eps*z_i (in place, inference mode), turns the 2*n_pert + 1 losses into one
+ * weight c_i per probe, and moves theta <- theta - eta * sum_i c_i z_i.
+ *
+ * Conventions shared by every call
+ *  - Parameters are one flat buffer of n elements, fp32 or bf16, in device memory, that
+ *    holds the global parameter indices [offset, offset + n).  offset must be a multiple
+ *    of 128; a model kept in several buffers gets, per buffer, the same probe bits as one
+ *    flat buffer when each buffer is passed with its global offset.
+ *  - Probe signs are counter-based: z_j of probe p at step t under seed s is bit
+ *    (j mod 32) of word (j / 32) mod 4 of Philox4x32-10 (Salmon et al., SC'11) with
+ *    counter (blk_lo, blk_hi, p, t), blk = j / 128, and key (s_lo, s_hi); bit 1 means +1,
+ *    bit 0 means -1.  Nothing has to be stored: every call can regenerate the signs.
+ *  - A packed probe row ("plane") holds the signs of one probe over [offset, offset+n):
+ *    zo_bits_stride(n) bytes, byte m = params offset + 8m .. 8m+7, least significant bit
+ *    first (the four Philox words of each 128-param block, little-endian).  Bits past n in
+ *    the last block are Philox bits and are never applied.
+ *  - Every compute call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  The caller owns every buffer; hot-path calls allocate nothing.
+ *  - Return values report argument and launch errors only: ZO_EINVAL is returned before
+ *    anything is launched, ZO_EHIP when the HIP runtime reports an error.  Numeric
+ *    trouble is not an error (see zo_probe_weights).  n == 0 (or n_pert == 0) is a
+ *    valid empty call that launches nothing and returns ZO_OK.
+ *  - Threading: one host thread uses a context at a time.  Calls on different streams
+ *    that touch the same parameter buffer race, as any two kernels would.
+ */
+#ifndef ZO_H
+#define ZO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct zo_ctx zo_ctx;
+
+typedef enum {
+    ZO_OK = 0,
+    ZO_EINVAL = 1,        /* bad argument; nothing was launched */
+    ZO_EHIP = 2,          /* the HIP runtime reported an error */
+    ZO_ENOMEM = 3,        /* host or device allocation failed (zo_init only) */
+    ZO_EUNSUPPORTED = 4   /* valid request beyond a documented limit */
+} zo_status;
+
+typedef enum { ZO_FP32 = 0, ZO_BF16 = 1 } zo_dtype;
+
+/* Largest n_pert one zo_update call accepts (its sign tables live in LDS). */
+#define ZO_MAX_NPERT 512u
+
+/* Create a context for probe seed `seed` on the current HIP device.  Allocates the host
+ * context and a small device area (the non-finite counter and reduction partials).
+ * Errors: ZO_EINVAL if out is NULL; ZO_ENOMEM / ZO_EHIP if an allocation fails (for
+ * example when no GPU is present).  *out is set only on success. */
+zo_status zo_init(uint64_t seed, zo_ctx **out);
+
+/* Release a context (NULL is allowed).  Synchronizes the device first. */
+zo_status zo_destroy(zo_ctx *ctx);
+
+/* The seed the context was created with. */
+uint64_t zo_get_seed(const zo_ctx *ctx);
+
+/* Static description of a status code; never NULL. */
+const char *zo_strerror(zo_status status);
+
+/* Bytes of one packed probe row over n parameters: ceil(n / 128) * 16. */
+uint64_t zo_bits_stride(uint64_t n);
+
+/* Probe generator (the packed-bit generator of the abstract of "Probe-Space
+ * Preconditioning for Fast and Stable Zero-Order Training"; probes z_i of "How 1.5-SPSA
+ * Works").  Writes n_probes consecutive rows for probes probe0 .. probe0+n_probes-1 of
+ * step `step` over params [offset, offset+n): row r at d_bits + r*zo_bits_stride(n).
+ * d_bits: device, 16-byte aligned, n_probes*zo_bits_stride(n) bytes, written in full.
+ * Errors (ZO_EINVAL): ctx or d_bits NULL (with work to do), offset % 128 != 0,
+ * d_bits misaligned, offset + n beyond 2^64 - 1. */
+zo_status zo_gen_probes(zo_ctx *ctx, uint32_t step, uint32_t probe0, uint32_t n_probes,
+                        uint64_t offset, uint64_t n, uint8_t *d_bits, void *stream);
+
+/* In-place perturbation theta_j <- round(theta_j + alpha * z_j) of probe `probe` at
+ * `step` ("How 1.5-SPSA Works": losses at theta +/- eps*z_i; the abstract: in place,
+ * fused unpack/apply).  fp32: one IEEE add, round to nearest even.  bf16: widen to fp32,
+ * one fp32 add, round to nearest even back to bf16.  Restoring is the same call with
+ * -alpha.  d_bits NULL regenerates the signs; otherwise it is this probe's packed row
+ * over the same [offset, offset+n) (device, 16-byte aligned).
+ * d_theta: device, 16-byte aligned, n elements of `dtype`.
+ * Errors (ZO_EINVAL): ctx or d_theta NULL (with n > 0), unknown dtype, offset % 128 != 0,
+ * misaligned pointers, offset + n beyond 2^64 - 1. */
+zo_status zo_perturb(zo_ctx *ctx, void *d_theta, zo_dtype dtype, uint64_t offset,
+                     uint64_t n, uint32_t step, uint32_t probe, float alpha,
+                     const uint8_t *d_bits, void *stream);
+
+/* Probe weights ("How 1.5-SPSA Works" for the central difference; "Probe-Space
+ * Preconditioning" for the clean-pass curvature weight), computed in fp64:
+ *   g_i = (L+_i - L-_i) / (2 eps),   h_i = ((L+_i + L-_i) - 2 L0) / eps^2,
+ *   c_i = g_i / max(|h_i|, delta), rounded once to fp32.
+ * eps must be the step actually applied (the fp32 alpha of zo_perturb, widened).
+ * A probe with a non-finite L+_i, L-_i or L0 gets c_i = 0 and adds 1 to the context's
+ * device counter (read it with zo_nonfinite_count).
+ * d_Lp, d_Lm: device, n_pert doubles; d_L0: device, one double; d_c: device, n_pert
+ * floats (written).  Errors (ZO_EINVAL): NULL ctx or pointers (with n_pert > 0),
+ * eps not finite or zero, delta negative or not finite. */
+zo_status zo_probe_weights(zo_ctx *ctx, const double *d_Lp, const double *d_Lm,
+                           const double *d_L0, uint32_t n_pert, double eps, double delta,
+                           float *d_c, void *stream);
+
+/* Multi-probe update theta_j <- round(theta_j - eta * s_j), s_j = sum_i c_i z_ij over
+ * probes 0 .. n_pert-1 of `step` (the update box of the ZOO loop flowchart in
+ * "Pretraining Transformers Without Backprop: What Two Zero-Order Papers Actually
+ * Measure").  Each parameter is read and written once.  s_j is accumulated in fp64
+ * through per-8-probe tables of signed partial sums (probes in ascending order within a
+ * table, tables in ascending order); then t = (double)theta_j - (double)eta * s_j is
+ * rounded once, to nearest even, to the storage type (fp32, or bf16 directly from the
+ * double).  The result is deterministic (independent of launch geometry).
+ * d_c: device, n_pert floats.  d_bits NULL regenerates; otherwise n_pert packed rows of
+ * zo_bits_stride(n) bytes (device, 16-byte aligned), row i = probe i.
+ * Errors: ZO_EINVAL as for zo_perturb, or d_c NULL (with n_pert > 0);
+ * ZO_EUNSUPPORTED if n_pert > ZO_MAX_NPERT. */
+zo_status zo_update(zo_ctx *ctx, void *d_theta, zo_dtype dtype, uint64_t offset,
+                    uint64_t n, uint32_t step, const float *d_c, uint32_t n_pert,
+                    float eta, const uint8_t *d_bits, void *stream);
+
+/* Read the non-finite-probe counter: synchronizes `stream`, then copies it to *out. */
+zo_status zo_nonfinite_count(zo_ctx *ctx, void *stream, uint32_t *out);
+
+/* Zero the non-finite-probe counter (asynchronous on `stream`, a small fill kernel). */
+zo_status zo_reset_nonfinite(zo_ctx *ctx, void *stream);
+
+/* Diagonal quadratic loss L = 1/2 sum_j a_j theta_j^2, accumulated in fp64, written to
+ * d_out (one double).  Stand-in for the model's forward pass ("N forward passes" box of
+ * the ZOO loop flowchart) on the synthetic quadratic workloads.  Deterministic: fixed
+ * partition into partial sums, reduced in a fixed order.
+ * d_theta: device, n elements of dtype, 16-byte aligned; d_a: device, n floats, 16-byte
+ * aligned.  Errors (ZO_EINVAL): NULL pointers (with n > 0), unknown dtype, misalignment.
+ * n == 0 writes 0. */
+zo_status zo_quad_loss(zo_ctx *ctx, const void *d_theta, zo_dtype dtype, const float *d_a,
+                       uint64_t n, double *d_out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZO_H */

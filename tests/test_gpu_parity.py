@@ -1,0 +1,352 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, element by element.
+
+Sizes span several 8192-param chunks plus ragged tails; offsets, both sign modes (probes
+regenerated from the counter, or read from stored rows), special values and the argument
+checks are covered.  Tolerances: see tests/gpu_util.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import forward_only_amd as zo
+import oracle
+from forward_only_amd.step import spsa_step
+from gpu_util import (assert_bf16_within_ulp, assert_f32_update_close, assert_same_bits_or_nan,
+                      bf16_bits, to_dev_bf16, to_dev_f32)
+from workloads import CONFIGS, gen
+
+pytestmark = pytest.mark.gpu
+
+SEED = 0x0123456789ABCDEF
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    c = zo.zo_init(SEED)
+    yield c
+    c.close()
+
+
+def _theta(kind, n, seed, scale=1.0, specials=False):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(n) * scale).astype(np.float32)
+    if specials and n >= 12:
+        x[:12] = [np.nan, np.inf, -np.inf, 1e-40, -1e-40, 0.0, -0.0, 3e38, -3e38,
+                  1.17549435e-38, 2.0 ** -130, 1e-3]
+    if kind == "f32":
+        return x
+    return oracle.f32_to_bf16(x)
+
+
+def _dev(kind, h):
+    return to_dev_f32(h) if kind == "f32" else to_dev_bf16(h)
+
+
+def _host(kind, t):
+    return t.cpu().numpy() if kind == "f32" else bf16_bits(t)
+
+
+# ------------------------------------------------------------------------------------
+# probe planes
+# ------------------------------------------------------------------------------------
+@pytest.mark.parametrize("n,offset,step,probe0,nprobes", [
+    (4096, 0, 0, 0, 16), (1, 0, 3, 5, 2), (129, 128, 1, 0, 3), (1000, 128 * 77, 9, 100, 7),
+    (8192 * 3 + 1000, 0, 0xFFFFFFFF, 0xFFFFFFF0, 4), (77777, (1 << 40) * 128, 2, 1, 2)])
+def test_gen_probes_bit_exact(ctx, n, offset, step, probe0, nprobes):
+    got = zo.zo_gen_probes(ctx, step, probe0, nprobes, offset, n).cpu().numpy()
+    ref = oracle.gen_planes(SEED, step, probe0, nprobes, offset, n)
+    assert got.shape == ref.shape
+    assert np.array_equal(got, ref)
+
+
+def test_gen_probes_plane_125m(ctx):
+    n = 125_000_000
+    got = zo.zo_gen_probes(ctx, 4, 17, 1, 0, n).cpu().numpy()[0]
+    ref = oracle.gen_plane(SEED, 4, 17, 0, n)
+    assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------------------------------
+# perturb
+# ------------------------------------------------------------------------------------
+PERTURB_CASES = [(4096, 0), (8192, 128), (8192 * 3 + 1000, 0), (1, 256), (127, 0),
+                 (8192 * 9 + 8191, 128 * 5), (1 << 22, 0)]
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+@pytest.mark.parametrize("n,offset", PERTURB_CASES)
+@pytest.mark.parametrize("mode", ["regen", "bits"])
+def test_perturb_bit_exact(ctx, kind, n, offset, mode):
+    step, probe, alpha = 5, 11, (2.0 ** -10 if kind == "f32" else 1e-3)
+    h = _theta(kind, n, seed=n + offset, scale=1.0 if kind == "f32" else 0.02, specials=True)
+    t = _dev(kind, h)
+    bits_h = oracle.gen_plane(SEED, step, probe, offset, n) if mode == "bits" else None
+    bits_d = torch.from_numpy(bits_h).cuda() if mode == "bits" else None
+    for a in (alpha, -alpha, -3.0 * alpha):
+        zo.zo_perturb(ctx, t, offset, step, probe, a, bits_d)
+        oracle.perturb(h, offset, SEED, step, probe, a, bits_h)
+        assert_same_bits_or_nan(_host(kind, t), h, kind)
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+def test_perturb_restore_schedule_matches(ctx, kind):
+    n = 8192 * 5 + 333
+    h = _theta(kind, n, seed=3, scale=0.02)
+    t = _dev(kind, h)
+    for i in range(8):
+        for s in (+1e-3, -1e-3, -1e-3, +1e-3):
+            zo.zo_perturb(ctx, t, 0, 0, i, s)
+            oracle.perturb(h, 0, SEED, 0, i, s)
+    assert_same_bits_or_nan(_host(kind, t), h, kind)
+
+
+def test_perturb_restore_exact_on_dyadic_grid(ctx):
+    th0 = gen.dyadic_theta(8192 * 4 + 17, seed=9, frac_bits=12, max_abs_log2=11)
+    t = to_dev_f32(th0)
+    zo.zo_perturb(ctx, t, 0, 1, 2, 2.0 ** -10)
+    zo.zo_perturb(ctx, t, 0, 1, 2, -(2.0 ** -10))
+    assert np.array_equal(t.cpu().numpy().view(np.uint32), th0.view(np.uint32))
+
+
+def test_perturb_keeps_denormals(ctx):
+    # Subnormal inputs and steps must not be flushed: fp32 k * 2^-149 +/- 2^-147 and bf16
+    # subnormals +/- 2^-133 are exact, so flushing anything would show.
+    n = 8192 + 100
+    k = np.random.default_rng(3).integers(-2 ** 20, 2 ** 20, n)
+    x = (k.astype(np.float64) * 2.0 ** -149).astype(np.float32)
+    t = to_dev_f32(x)
+    zo.zo_perturb(ctx, t, 0, 0, 1, 2.0 ** -147)
+    oracle.perturb(x, 0, SEED, 0, 1, 2.0 ** -147)
+    assert_same_bits_or_nan(t.cpu().numpy(), x, "f32")
+    assert np.count_nonzero(np.abs(x) < 2.0 ** -126) > n // 2
+    hb = np.random.default_rng(4).integers(0, 0x7F, n).astype(np.uint16) | \
+        (np.random.default_rng(5).integers(0, 2, n).astype(np.uint16) << 15)
+    tb = to_dev_bf16(hb)
+    zo.zo_perturb(ctx, tb, 0, 0, 2, 2.0 ** -133)
+    oracle.perturb(hb, 0, SEED, 0, 2, 2.0 ** -133)
+    assert_same_bits_or_nan(bf16_bits(tb), hb, "bf16")
+
+
+# ------------------------------------------------------------------------------------
+# probe weights
+# ------------------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [1, 16, 160, 300, 1024])
+def test_probe_weights_bit_exact(ctx, n):
+    rng = np.random.default_rng(n)
+    L0 = 2.0 + rng.normal(0, 0.05)
+    u = rng.normal(0, 0.01, n)
+    Lp = L0 + u + rng.normal(0.002, 0.001, n)
+    Lm = L0 - u + rng.normal(0.002, 0.001, n)
+    if n >= 16:
+        Lp[3] = np.nan
+        Lm[5] = np.inf
+        Lp[7] = Lm[7] = L0            # h = 0: floored by delta
+        Lp[8], Lm[8] = L0 - 1e-6, L0 - 3e-6   # negative curvature
+    eps = float(np.float32(1e-3))
+    zo.zo_reset_nonfinite(ctx)
+    c = zo.zo_probe_weights(ctx, torch.from_numpy(Lp).cuda(), torch.from_numpy(Lm).cuda(),
+                            torch.tensor([L0], dtype=torch.float64).cuda(), eps, 1e-6)
+    ref, bad = oracle.probe_weights(Lp, Lm, L0, eps, 1e-6)
+    assert np.array_equal(c.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    assert zo.zo_nonfinite_count(ctx) == bad
+
+
+def test_probe_weights_nonfinite_clean_loss(ctx):
+    n = 40
+    Lp = torch.ones(n, dtype=torch.float64).cuda()
+    Lm = torch.ones(n, dtype=torch.float64).cuda()
+    zo.zo_reset_nonfinite(ctx)
+    c = zo.zo_probe_weights(ctx, Lp, Lm, torch.tensor([np.nan], dtype=torch.float64).cuda(),
+                            1e-3, 1e-6)
+    assert torch.all(c == 0)
+    assert zo.zo_nonfinite_count(ctx) == n
+    zo.zo_reset_nonfinite(ctx)
+    assert zo.zo_nonfinite_count(ctx) == 0
+
+
+# ------------------------------------------------------------------------------------
+# update
+# ------------------------------------------------------------------------------------
+UPDATE_CASES = [(4096, 0, 16), (1000, 128, 7), (8192 * 3 + 1000, 0, 160), (1, 0, 1),
+                (2_368_514, 0, 64), (33333, 128 * 3, 512), (8192, 0, 9)]
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+@pytest.mark.parametrize("n,offset,npert", UPDATE_CASES)
+@pytest.mark.parametrize("mode", ["regen", "bits"])
+def test_update_parity(ctx, kind, n, offset, npert, mode):
+    step = 3
+    rng = np.random.default_rng(n + npert)
+    h = _theta(kind, n, seed=n, scale=0.02)
+    c = (rng.standard_normal(npert) * 2.5e-3).astype(np.float32)
+    eta = 1.0 if kind == "bf16" else 1e-2      # large enough that bf16 updates do move
+    t = _dev(kind, h)
+    bits_h = oracle.gen_planes(SEED, step, 0, npert, offset, n) if mode == "bits" else None
+    bits_d = torch.from_numpy(bits_h).cuda() if mode == "bits" else None
+    zo.zo_update(ctx, t, offset, step, to_dev_f32(c), eta, bits_d)
+    oracle.update(h, offset, SEED, step, c, eta, bits_h)
+    got = _host(kind, t)
+    if kind == "f32":
+        assert_f32_update_close(got, h, eta, c)
+        same = np.mean(got.view(np.uint32) == h.view(np.uint32))
+    else:
+        assert_bf16_within_ulp(got, h)
+        same = np.mean(got == h)
+    # fp64 sums: all but (measure-zero) rounding ties agree bit for bit
+    assert same >= 0.9999, same
+
+
+def test_update_sum_error_within_recursive_summation_bound(ctx):
+    # s_j from the GPU (recovered with eta = 1 on theta = 0 in fp32: theta' = -s rounded
+    # once to fp32) vs the oracle's fp64 sums: |s_gpu - s| <= half an fp32 ulp of s plus
+    # gamma_(n/8 + 8) * sum |c_i| in fp64 (recursive summation, Higham), factor 2 margin.
+    n, npert = 8192 * 2 + 5, 160
+    c = (np.random.default_rng(1).standard_normal(npert) * 1e-2).astype(np.float32)
+    t = torch.zeros(n, dtype=torch.float32, device="cuda")
+    zo.zo_update(ctx, t, 0, 7, to_dev_f32(c), 1.0)
+    s_gpu = -t.cpu().numpy().astype(np.float64)
+    s = oracle.probe_sums(n, 0, SEED, 7, c)
+    u = 2.0 ** -53
+    k = npert // 8 + 8
+    gamma = k * u / (1 - k * u)
+    half_ulp = 0.5 * np.spacing(np.abs(s).astype(np.float32)).astype(np.float64)
+    bound = half_ulp + 2 * gamma * np.sum(np.abs(c.astype(np.float64)))
+    assert np.all(np.abs(s_gpu - s) <= bound)
+
+
+def test_update_single_probe_equals_perturb(ctx):
+    for kind in ("f32", "bf16"):
+        h = _theta(kind, 8192 * 2 + 100, seed=4, scale=0.02)
+        a, b = _dev(kind, h), _dev(kind, h)
+        eta = 2.0 ** -9
+        zo.zo_update(ctx, a, 0, 6, torch.tensor([1.0], device="cuda"), eta)
+        zo.zo_perturb(ctx, b, 0, 6, 0, -eta)
+        assert np.array_equal(_host(kind, a), _host(kind, b))
+
+
+def test_update_identity_cases(ctx):
+    h = _theta("f32", 9000, seed=6)
+    t = to_dev_f32(h)
+    zo.zo_update(ctx, t, 0, 1, torch.zeros(16, device="cuda"), 0.7)
+    zo.zo_update(ctx, t, 0, 1, torch.ones(16, device="cuda"), 0.0)
+    assert np.array_equal(t.cpu().numpy().view(np.uint32), h.view(np.uint32))
+
+
+def test_update_independent_of_split_and_geometry(ctx):
+    # Updating [0, n) at once or as two buffers with their global offsets gives the same
+    # bits: each element's sum is independent of the launch geometry.
+    n, cut, npert = 8192 * 7 + 300, 128 * 131, 40
+    h = _theta("bf16", n, seed=7, scale=0.02)
+    c = to_dev_f32(np.random.default_rng(2).standard_normal(npert).astype(np.float32) * 1e-2)
+    whole = to_dev_bf16(h)
+    zo.zo_update(ctx, whole, 0, 2, c, 1.0)
+    left, right = to_dev_bf16(h[:cut]), to_dev_bf16(h[cut:])
+    zo.zo_update(ctx, left, 0, 2, c, 1.0)
+    zo.zo_update(ctx, right, cut, 2, c, 1.0)
+    assert np.array_equal(bf16_bits(whole), np.concatenate([bf16_bits(left), bf16_bits(right)]))
+
+
+def test_update_brute_force_all_sign_patterns(ctx):
+    # sum over all 2^8 patterns of (z^T A theta) z = 256 A theta, exactly.
+    rng = np.random.Generator(np.random.PCG64(5))
+    B = rng.integers(-8, 9, (8, 8)) / 16.0
+    A = (B + B.T) / 2
+    th0 = (rng.integers(-64, 65, 8) / 16.0).astype(np.float32)
+    rows = np.zeros((256, 16), dtype=np.uint8)
+    rows[:, 0] = np.arange(256, dtype=np.uint8)
+    Z = np.array([[1.0 if (p >> j) & 1 else -1.0 for j in range(8)] for p in range(256)])
+    v = A @ th0.astype(np.float64)
+    c = (Z @ v).astype(np.float32)
+    eta = 2.0 ** -10
+    t = to_dev_f32(th0)
+    zo.zo_update(ctx, t, 0, 0, to_dev_f32(c), eta, torch.from_numpy(rows).cuda())
+    assert np.array_equal(t.cpu().numpy().astype(np.float64), th0 - eta * 256 * v)
+
+
+# ------------------------------------------------------------------------------------
+# loss kernel and argument checks
+# ------------------------------------------------------------------------------------
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [0, 1, 4096, 1_000_003])
+def test_quad_loss(ctx, kind, n):
+    h = _theta(kind, n, seed=8, scale=0.5)
+    a = np.power(10.0, np.random.default_rng(9).uniform(-2, 2, n)).astype(np.float32)
+    got = zo.zo_quad_loss(ctx, _dev(kind, h), to_dev_f32(a)).item()
+    ref = oracle.quad_loss(h, a)
+    assert abs(got - ref) <= 1e-13 * abs(ref) + 1e-300
+    assert zo.zo_quad_loss(ctx, _dev(kind, h), to_dev_f32(a)).item() == got  # deterministic
+
+
+def test_argument_checks(ctx):
+    t = torch.zeros(1024, dtype=torch.float32, device="cuda")
+    c = torch.zeros(4, dtype=torch.float32, device="cuda")
+    with pytest.raises(zo.ZOError) as e:
+        zo.zo_perturb(ctx, t[1:], 0, 0, 0, 1.0)          # misaligned
+    assert e.value.status == zo.ZO_EINVAL
+    with pytest.raises(zo.ZOError) as e:
+        zo.zo_perturb(ctx, t, 64, 0, 0, 1.0)             # offset not a multiple of 128
+    assert e.value.status == zo.ZO_EINVAL
+    with pytest.raises(zo.ZOError) as e:
+        zo.zo_update(ctx, t, 0, 0, torch.zeros(zo.ZO_MAX_NPERT + 1, device="cuda"), 1.0)
+    assert e.value.status == zo.ZO_EUNSUPPORTED
+    d = torch.zeros(4, dtype=torch.float64, device="cuda")
+    with pytest.raises(zo.ZOError) as e:
+        zo.zo_probe_weights(ctx, d, d, d[:1], 0.0, 1e-6)   # eps = 0
+    assert e.value.status == zo.ZO_EINVAL
+    empty = torch.zeros(0, dtype=torch.float32, device="cuda")
+    zo.zo_perturb(ctx, empty, 0, 0, 0, 1.0)               # empty calls are no-ops
+    zo.zo_update(ctx, empty, 0, 0, c, 1.0)
+    zo.zo_update(ctx, t, 0, 0, empty, 1.0)
+    assert torch.all(t == 0)
+
+
+# ------------------------------------------------------------------------------------
+# whole steps
+# ------------------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", ["regen", "bits"])
+def test_tiny_config_ten_steps(ctx, mode):
+    """The tiny quadratic workload end to end: per step, the oracle is fed the GPU's losses
+    (so the weights must be bit-identical) and the GPU's theta must stay within the update
+    tolerance of the oracle's; the loss must go down."""
+    cfg = CONFIGS["tiny"]
+    local = zo.zo_init(cfg.seed)
+    th0, a = gen.theta_and_a(cfg)
+    t = to_dev_f32(th0)
+    ad = to_dev_f32(a)
+    h = th0.copy()
+    lossf = lambda x, o: zo.zo_quad_loss(local, x, ad, out=o)  # noqa: E731
+    first = oracle.quad_loss(h, a)
+    for step in range(cfg.steps):
+        bits_h = oracle.gen_planes(cfg.seed, step, 0, cfg.npert, 0, cfg.M) if mode == "bits" else None
+        bits_d = torch.from_numpy(bits_h).cuda() if mode == "bits" else None
+        out = spsa_step(local, t, step=step, npert=cfg.npert, eps=cfg.eps, eta=cfg.eta,
+                        delta=cfg.delta, loss=lossf, bits=bits_d)
+        L0, Lp, Lm = out["L0"].item(), out["Lp"].cpu().numpy(), out["Lm"].cpu().numpy()
+        # the GPU losses agree with the oracle's loss of the same parameters
+        assert abs(L0 - oracle.quad_loss(h, a)) <= 1e-13 * abs(L0)
+        res = oracle.spsa_step(h, seed=cfg.seed, step=step, npert=cfg.npert, eps=cfg.eps,
+                               eta=cfg.eta, delta=cfg.delta, losses=(L0, Lp, Lm), bits=bits_h)
+        assert np.array_equal(out["c"].cpu().numpy(), res["c"])
+        got = t.cpu().numpy()
+        assert_f32_update_close(got, h, cfg.eta, res["c"])
+        h = got.copy()     # continue from the GPU's state (teacher forcing)
+    assert oracle.quad_loss(h, a) < first
+    local.close()
+
+
+def test_bf16_synthetic_step_small(ctx):
+    """A bf16 step with synthetic per-probe losses (the OPT-shaped workloads' loss model)
+    on a small buffer: perturb passes bit-exact, weights bit-exact, update within 1 ulp."""
+    cfg = CONFIGS["opt30b"]
+    n, npert = 8192 * 4 + 555, cfg.npert
+    h = _theta("bf16", n, seed=12, scale=0.02)
+    t = to_dev_bf16(h)
+    L0, Lp, Lm = gen.synthetic_losses(cfg.seed, 0, npert)
+    dl = (torch.tensor([L0], dtype=torch.float64).cuda(), torch.from_numpy(Lp).cuda(),
+          torch.from_numpy(Lm).cuda())
+    out = spsa_step(ctx, t, step=0, npert=npert, eps=cfg.eps, eta=1.0, delta=cfg.delta,
+                    losses=dl)
+    res = oracle.spsa_step(h, seed=SEED, step=0, npert=npert, eps=cfg.eps, eta=1.0,
+                           delta=cfg.delta, losses=(L0, Lp, Lm))
+    assert np.array_equal(out["c"].cpu().numpy(), res["c"])
+    assert_bf16_within_ulp(bf16_bits(t), h)
