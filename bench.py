@@ -2,11 +2,14 @@
 """Throughput of one 1.5-SPSA step of the perturb / probe-weight / update path on one GPU.
 
 A step (per "Stanford's 1.5-SPSA Trains OPT-30B Without Backpropagation", sections "How
-1.5-SPSA Works" and "Probe-Space Preconditioning") is: for each of n_pert probes, four
-in-place passes over the parameters (+eps, restore, -eps, restore) with the per-probe
-losses taken between them, then the probe weights from the 2 n_pert + 1 losses, then one
-update pass theta <- theta - eta * sum_i c_i z_i.  Probes are regenerated from the
-counter-based generator in every pass (nothing stored).
+1.5-SPSA Works" and "Probe-Space Preconditioning") evaluates the loss at the clean
+parameters and at theta +/- eps*z_i for each of n_pert probes, moving the parameters in
+place between evaluations, then forms the probe weights from the 2 n_pert + 1 losses and
+makes one update pass theta <- theta - eta * sum_i c_i z_i.  Schedules of the in-place
+moves: S2f (default) -- +eps z_0, then per probe -2 eps z_i and one fused pass restoring
+probe i and applying +eps z_(i+1): 2 n_pert + 1 passes; S4 -- +eps, restore, -eps,
+restore per probe: 4 n_pert passes.  Probes are regenerated from the counter-based
+generator in every pass (nothing stored).
 
 Default workload: an OPT-30B-shaped bf16 parameter set (48 layers, d = 7168, FFN 28672,
 vocab 50272: 29,959,831,552 params, 59.9 GB) updated in place, n_pert = 160, eps = 1e-3;
@@ -46,9 +49,12 @@ def parse_args(argv=None):
     p.add_argument("--warmup", type=int, default=1)
     p.add_argument("--config", default="opt30b",
                    choices=["tiny", "flat125m", "opt13b", "opt30b"])
+    p.add_argument("--schedule", default="S2f", choices=["S2f", "S4"],
+                   help="S2f: two passes per probe (restore fused with the next probe's "
+                        "move); S4: four passes per probe")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the CPU oracle leg (profiling runs)")
-    p.add_argument("--cpu-params-per-thread", type=int, default=1 << 18)
+    p.add_argument("--cpu-params-per-thread", type=int, default=1 << 20)
     p.add_argument("--cpu-threads", type=int, default=None)
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 4 GiB device copy (counter calibration)")
@@ -79,7 +85,7 @@ def stored_traffic(workload: str, nbytes_alg: float):
 # ------------------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, on a bounded slice of the same workload
 # ------------------------------------------------------------------------------------
-def cpu_baseline(cfg, params_per_thread: int, threads: int):
+def cpu_baseline(cfg, params_per_thread: int, threads: int, schedule: str):
     import numpy as np
 
     import oracle
@@ -98,7 +104,8 @@ def cpu_baseline(cfg, params_per_thread: int, threads: int):
 
     def run(w):
         oracle.spsa_step(windows[w], seed=cfg.seed, step=0, npert=cfg.npert, eps=cfg.eps,
-                         eta=cfg.eta, delta=cfg.delta, losses=(L0, Lp, Lm), offset=offsets[w])
+                         eta=cfg.eta, delta=cfg.delta, losses=(L0, Lp, Lm), offset=offsets[w],
+                         schedule=schedule)
 
     ts = [threading.Thread(target=run, args=(w,)) for w in range(threads)]
     t0 = time.perf_counter()
@@ -111,8 +118,8 @@ def cpu_baseline(cfg, params_per_thread: int, threads: int):
     return {
         "value": work / dt, "unit": "probe*params/s", "cores": threads, "kind": "oracle",
         "sample": (f"{threads} windows x {params_per_thread} {cfg.dtype} params of the "
-                   f"{cfg.name} workload, one full step (n_pert={cfg.npert}, four passes "
-                   f"per probe, weights, update), one window per thread; {dt:.1f} s"),
+                   f"{cfg.name} workload, one full step (n_pert={cfg.npert}, schedule "
+                   f"{schedule}, weights, update), one window per thread; {dt:.1f} s"),
     }
 
 
@@ -161,7 +168,7 @@ def main(argv=None):
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         log(f"[bench] cpu baseline: {threads} threads x {args.cpu_params_per_thread} params")
-        cpu = cpu_baseline(cfg, args.cpu_params_per_thread, threads)
+        cpu = cpu_baseline(cfg, args.cpu_params_per_thread, threads, args.schedule)
         log(f"[bench] cpu baseline: {cpu['value']:.3e} probe*params/s")
 
     ctx = zo.zo_init(cfg.seed)
@@ -194,7 +201,7 @@ def main(argv=None):
     a = applied_eps(cfg.eps)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    per = {"perturb": [], "weights": [], "update": [], "loss": []}
+    per = {"perturb": [], "perturb2": [], "weights": [], "update": [], "loss": []}
 
     def timed(kind, fn, record):
         if record:
@@ -206,19 +213,32 @@ def main(argv=None):
         else:
             fn()
 
+    def loss_into(out, record):
+        if cfg.loss == "quad":
+            timed("loss", lambda: zo.zo_quad_loss(ctx, theta, a_dev, out=out), record)
+
     def one_step(s, record):
         L0, Lp, Lm = L0s[s], Lps[s], Lms[s]
-        if cfg.loss == "quad":
-            timed("loss", lambda: zo.zo_quad_loss(ctx, theta, a_dev, out=L0), record)
-        for i in range(n):
-            timed("perturb", lambda: zo.zo_perturb(ctx, theta, 0, s, i, +a), record)
-            if cfg.loss == "quad":
-                timed("loss", lambda: zo.zo_quad_loss(ctx, theta, a_dev, out=Lp[i:i + 1]), record)
-            timed("perturb", lambda: zo.zo_perturb(ctx, theta, 0, s, i, -a), record)
-            timed("perturb", lambda: zo.zo_perturb(ctx, theta, 0, s, i, -a), record)
-            if cfg.loss == "quad":
-                timed("loss", lambda: zo.zo_quad_loss(ctx, theta, a_dev, out=Lm[i:i + 1]), record)
-            timed("perturb", lambda: zo.zo_perturb(ctx, theta, 0, s, i, +a), record)
+        loss_into(L0, record)
+        if args.schedule == "S4":
+            for i in range(n):
+                timed("perturb", lambda: zo.zo_perturb(ctx, theta, 0, s, i, +a), record)
+                loss_into(Lp[i:i + 1], record)
+                timed("perturb", lambda: zo.zo_perturb(ctx, theta, 0, s, i, -a), record)
+                timed("perturb", lambda: zo.zo_perturb(ctx, theta, 0, s, i, -a), record)
+                loss_into(Lm[i:i + 1], record)
+                timed("perturb", lambda: zo.zo_perturb(ctx, theta, 0, s, i, +a), record)
+        else:
+            timed("perturb", lambda: zo.zo_perturb(ctx, theta, 0, s, 0, +a), record)
+            for i in range(n):
+                loss_into(Lp[i:i + 1], record)
+                timed("perturb", lambda: zo.zo_perturb(ctx, theta, 0, s, i, -2.0 * a), record)
+                loss_into(Lm[i:i + 1], record)
+                if i + 1 < n:
+                    timed("perturb2",
+                          lambda: zo.zo_perturb2(ctx, theta, 0, s, i, +a, i + 1, +a), record)
+                else:
+                    timed("perturb", lambda: zo.zo_perturb(ctx, theta, 0, s, i, +a), record)
         timed("weights", lambda: zo.zo_probe_weights(ctx, Lp, Lm, L0, a, cfg.delta, out=c_buf),
               record)
         timed("update", lambda: zo.zo_update(ctx, theta, 0, s, c_buf, cfg.eta), record)
@@ -237,17 +257,22 @@ def main(argv=None):
     log(f"[bench] {K} timed steps done in {t1 - t0:.2f} s")
     nonfinite = zo.zo_nonfinite_count(ctx)
 
-    def avg_ms(kind):
-        xs = [e0.elapsed_time(e1) for e0, e1 in per[kind]]
+    def times(kinds):
+        return [e0.elapsed_time(e1) for k in kinds for e0, e1 in per[k]]
+
+    def avg_ms(*kinds):
+        xs = times(kinds)
         return (sum(xs) / len(xs)) if xs else None
 
     T = (t1 - t0) / K
     value = n * M / T
-    pert_ms, upd_ms, w_ms = avg_ms("perturb"), avg_ms("update"), avg_ms("weights")
+    # every pass of either perturb entry point runs k_perturb_chunks (one or two probes)
+    pert_ms, upd_ms, w_ms = avg_ms("perturb", "perturb2"), avg_ms("update"), avg_ms("weights")
+    passes = 4 * n if args.schedule == "S4" else 2 * n + 1
     pass_bytes = 2.0 * esize * M                      # one read + one write of theta
-    step_bytes = (4 * n + 1) * pass_bytes             # 4 passes per probe + the update
+    step_bytes = (passes + 1) * pass_bytes            # the passes + the update
     achieved = pass_bytes / (pert_ms * 1e-3) / 1e9
-    traffic = stored_traffic(cfg.name, pass_bytes)
+    traffic = stored_traffic(f"{cfg.name}/{args.schedule}", pass_bytes)
     result = {
         "metric": "probe*params/s and HBM GB/s (% peak) per 1.5-SPSA step, n_pert=160, 1 GPU",
         "value": value,
@@ -262,16 +287,19 @@ def main(argv=None):
         "dtype": cfg.dtype,
         "data": "synthetic",
         "config": {"workload": (f"{cfg.name}: {M} {cfg.dtype} params in one flat buffer, "
-                                f"n_pert={n}, eps={cfg.eps}, eta={cfg.eta}, four passes per "
-                                f"probe, probes regenerated, losses "
+                                f"n_pert={n}, eps={cfg.eps}, eta={cfg.eta}, schedule "
+                                f"{args.schedule} ({passes} passes + update), probes "
+                                f"regenerated, losses "
                                 f"{'synthetic' if cfg.loss == 'synthetic' else cfg.loss}"),
-                   "params": M, "n_pert": n, "schedule": "4 passes per probe"},
+                   "params": M, "n_pert": n, "schedule": args.schedule,
+                   "passes_per_step": passes + 1},
         "hbm_gbps": step_bytes / T / 1e9,
         "hbm_frac_of_peak": step_bytes / T / 1e9 / PEAK_HBM_GBPS,
-        "kernels_ms": {"perturb_avg": pert_ms, "update_avg": upd_ms, "weights_avg": w_ms,
-                       "loss_avg": avg_ms("loss")},
-        "roofline": {"kernel": "k_perturb_chunks (zo_perturb, bf16 regenerate)"
-                     if cfg.dtype == "bf16" else "k_perturb_chunks (zo_perturb, fp32 regenerate)",
+        "kernels_ms": {"pass_avg": pert_ms, "perturb_avg": avg_ms("perturb"),
+                       "perturb2_avg": avg_ms("perturb2"), "update_avg": upd_ms,
+                       "weights_avg": w_ms, "loss_avg": avg_ms("loss")},
+        "roofline": {"kernel": f"k_perturb_chunks ({cfg.dtype}, probes regenerated; every "
+                               f"zo_perturb / zo_perturb2 pass)",
                      "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": traffic},

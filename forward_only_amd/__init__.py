@@ -24,7 +24,7 @@ from ._lib import (ZO_BF16, ZO_EHIP, ZO_EINVAL, ZO_ENOMEM, ZO_EUNSUPPORTED, ZO_F
 
 __all__ = [
     "Context", "ZOError", "zo_init", "zo_destroy", "zo_bits_stride", "zo_gen_probes",
-    "zo_perturb", "zo_probe_weights", "zo_update", "zo_nonfinite_count",
+    "zo_perturb", "zo_perturb2", "zo_probe_weights", "zo_update", "zo_nonfinite_count",
     "zo_reset_nonfinite", "zo_quad_loss", "library_path",
 ]
 
@@ -120,6 +120,24 @@ def zo_perturb(ctx: Context, theta: torch.Tensor, offset: int, step: int, probe:
     _lib.check(_lib.lib().zo_perturb(ctx.handle, _dev(theta, "theta"), _dtype_code(theta),
                                      offset, theta.numel(), step, probe, float(alpha), bp,
                                      _stream(stream)), "zo_perturb")
+
+
+def zo_perturb2(ctx: Context, theta: torch.Tensor, offset: int, step: int, probe_a: int,
+                alpha_a: float, probe_b: int, alpha_b: float,
+                bits_a: torch.Tensor | None = None, bits_b: torch.Tensor | None = None,
+                stream=None) -> None:
+    """theta <- theta + (+/-alpha_a) + (+/-alpha_b) in one pass (probes a and b)."""
+    if (bits_a is None) != (bits_b is None):
+        raise ValueError("give both packed rows or neither")
+    pa = None if bits_a is None else _dev(bits_a, "bits_a", torch.uint8)
+    pb = None if bits_b is None else _dev(bits_b, "bits_b", torch.uint8)
+    for b in (bits_a, bits_b):
+        if b is not None and b.numel() < zo_bits_stride(theta.numel()):
+            raise ValueError("bits row is too short")
+    _lib.check(_lib.lib().zo_perturb2(ctx.handle, _dev(theta, "theta"), _dtype_code(theta),
+                                      offset, theta.numel(), step, probe_a, float(alpha_a),
+                                      probe_b, float(alpha_b), pa, pb, _stream(stream)),
+               "zo_perturb2")
 
 
 def zo_probe_weights(ctx: Context, Lp: torch.Tensor, Lm: torch.Tensor, L0: torch.Tensor,

@@ -30,6 +30,8 @@ SIGNATURES = {
     "zo_bits_stride": (_u64, [_u64]),
     "zo_gen_probes": (_int, [_vp, _u32, _u32, _u32, _u64, _u64, _vp, _vp]),
     "zo_perturb": (_int, [_vp, _vp, _int, _u64, _u64, _u32, _u32, _f32, _vp, _vp]),
+    "zo_perturb2": (_int, [_vp, _vp, _int, _u64, _u64, _u32, _u32, _f32, _u32, _f32, _vp, _vp,
+                           _vp]),
     "zo_probe_weights": (_int, [_vp, _vp, _vp, _vp, _u32, _f64, _f64, _vp, _vp]),
     "zo_update": (_int, [_vp, _vp, _int, _u64, _u64, _u32, _vp, _u32, _f32, _vp, _vp]),
     "zo_nonfinite_count": (_int, [_vp, _vp, ctypes.POINTER(_u32)]),

@@ -123,6 +123,23 @@ zo_status zo_perturb(zo_ctx *c, void *d_theta, zo_dtype dtype, uint64_t offset, 
                                        probe, alpha, d_bits, c->num_cus, as_stream(stream)));
 }
 
+zo_status zo_perturb2(zo_ctx *c, void *d_theta, zo_dtype dtype, uint64_t offset, uint64_t n,
+                      uint32_t step, uint32_t probe_a, float alpha_a, uint32_t probe_b,
+                      float alpha_b, const uint8_t *d_bits_a, const uint8_t *d_bits_b,
+                      void *stream)
+{
+    if (!c) return ZO_EINVAL;
+    if (dtype != ZO_FP32 && dtype != ZO_BF16) return ZO_EINVAL;
+    if (!range_ok(offset, n)) return ZO_EINVAL;
+    if ((d_bits_a == nullptr) != (d_bits_b == nullptr)) return ZO_EINVAL;
+    if (n == 0) return ZO_OK;
+    if (!d_theta || !aligned16(d_theta)) return ZO_EINVAL;
+    if (d_bits_a && (!aligned16(d_bits_a) || !aligned16(d_bits_b))) return ZO_EINVAL;
+    return from_hip(zo::launch_perturb2(d_theta, dtype == ZO_BF16, offset, n, key_of(c), step,
+                                        probe_a, alpha_a, probe_b, alpha_b, d_bits_a, d_bits_b,
+                                        c->num_cus, as_stream(stream)));
+}
+
 zo_status zo_probe_weights(zo_ctx *c, const double *d_Lp, const double *d_Lm,
                            const double *d_L0, uint32_t n_pert, double eps, double delta,
                            float *d_c, void *stream)

@@ -18,6 +18,10 @@
 //  * Apply: flip alpha's sign bit when the param's bit is clear, one fp32 add, and for
 //    bf16 one v_cvt_pk_bf16_f32 (round to nearest even) per pair; store dwordx4.
 //  * The ragged end (fewer than 8192 params) goes to a small per-element kernel.
+//  * Two-probe variant (zo_perturb2): the restore of probe a and the move of probe b in
+//    one pass.  Each lane computes both Philox blocks, both land in LDS, and the step is
+//    d = (+/-alpha_a) + (+/-alpha_b) in fp32 followed by the same add and narrow; this
+//    halves the passes of a step (two per probe instead of four).
 // Every element is read once and written once; no element is touched by two lanes.
 #include <stdlib.h>
 
@@ -31,22 +35,27 @@ constexpr int kWavesPerWG = 4;
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-template <bool kBF16, bool kBits>
+template <bool kBF16, bool kBits, bool kTwo>
 __global__ __launch_bounds__(256) void k_perturb_chunks(u32x4_t *__restrict__ theta,
                                                         uint64_t nchunks, uint64_t blk0,
-                                                        uint32_t step, uint32_t probe,
-                                                        uint32_t k0, uint32_t k1,
-                                                        uint32_t abits,
-                                                        const u32x4_t *__restrict__ bits)
+                                                        uint32_t step, uint32_t probe_a,
+                                                        uint32_t probe_b, uint32_t k0,
+                                                        uint32_t k1, uint32_t abits,
+                                                        uint32_t bbits,
+                                                        const u32x4_t *__restrict__ bits_a,
+                                                        const u32x4_t *__restrict__ bits_b)
 {
     constexpr int kPerLoad = kBF16 ? 8 : 4;                      // params per 16 bytes
     constexpr int kLoads = kChunkParams / (kPerLoad * kWave);   // 16 or 32
-    __shared__ u32x4_t xch_all[kWavesPerWG][kWave];
+    constexpr int kProbes = kTwo ? 2 : 1;
+    __shared__ u32x4_t xch_all[kWavesPerWG][kProbes][kWave];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
-    u32x4_t *xch = xch_all[wv];
-    const uint8_t *xb = reinterpret_cast<const uint8_t *>(xch);
+    u32x4_t *xa = xch_all[wv][0];
+    u32x4_t *xb = xch_all[wv][kProbes - 1];
+    const uint8_t *ba = reinterpret_cast<const uint8_t *>(xa);
+    const uint8_t *bb = reinterpret_cast<const uint8_t *>(xb);
     const uint64_t nwaves = (uint64_t)gridDim.x * kWavesPerWG;
 
     for (uint64_t ch = (uint64_t)blockIdx.x * kWavesPerWG + wv; ch < nchunks; ch += nwaves) {
@@ -56,38 +65,53 @@ __global__ __launch_bounds__(256) void k_perturb_chunks(u32x4_t *__restrict__ th
         for (int k = 0; k < kLoads; ++k) v[k] = __builtin_nontemporal_load(base + k * kWave);
 
         const uint64_t lb = ch * kWave + lane;  // block index local to the buffer
-        u32x4_t w;
+        u32x4_t wa, wb;
         if constexpr (kBits) {
-            w = bits[lb];
+            wa = bits_a[lb];
+            if constexpr (kTwo) wb = bits_b[lb];
         } else {
-            const U32x4 r = probe_block_bits(blk0 + lb, probe, step, k0, k1);
-            w = u32x4_t{r.x, r.y, r.z, r.w};
+            const U32x4 r = probe_block_bits(blk0 + lb, probe_a, step, k0, k1);
+            wa = u32x4_t{r.x, r.y, r.z, r.w};
+            if constexpr (kTwo) {
+                const U32x4 q = probe_block_bits(blk0 + lb, probe_b, step, k0, k1);
+                wb = u32x4_t{q.x, q.y, q.z, q.w};
+            }
         }
         wave_lds_sync();  // the previous chunk's byte reads precede this overwrite
-        xch[lane] = w;
+        xa[lane] = wa;
+        if constexpr (kTwo) xb[lane] = wb;
         wave_lds_sync();
 
 #pragma unroll
         for (int k = 0; k < kLoads; ++k) {
-            uint32_t m;
+            uint32_t ma, mb = 0;
             if constexpr (kBF16) {
-                m = xb[64 * k + lane];
+                ma = ba[64 * k + lane];
+                if constexpr (kTwo) mb = bb[64 * k + lane];
             } else {
-                m = (uint32_t)xb[32 * k + (lane >> 1)] >> (4 * (lane & 1));
+                ma = (uint32_t)ba[32 * k + (lane >> 1)] >> (4 * (lane & 1));
+                if constexpr (kTwo) mb = (uint32_t)bb[32 * k + (lane >> 1)] >> (4 * (lane & 1));
             }
-            const uint32_t nm = ~m;
+            const uint32_t nma = ~ma, nmb = ~mb;
             u32x4_t q = v[k];
             if constexpr (kBF16) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float lo = bf16lo_to_f32(q[j]) + signed_alpha(nm, 2 * j, abits);
-                    const float hi = bf16hi_to_f32(q[j]) + signed_alpha(nm, 2 * j + 1, abits);
-                    q[j] = pack_bf16x2(lo, hi);
+                    float dlo = signed_alpha(nma, 2 * j, abits);
+                    float dhi = signed_alpha(nma, 2 * j + 1, abits);
+                    if constexpr (kTwo) {
+                        dlo = dlo + signed_alpha(nmb, 2 * j, bbits);
+                        dhi = dhi + signed_alpha(nmb, 2 * j + 1, bbits);
+                    }
+                    q[j] = pack_bf16x2(bf16lo_to_f32(q[j]) + dlo, bf16hi_to_f32(q[j]) + dhi);
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    q[j] = __float_as_uint(__uint_as_float(q[j]) + signed_alpha(nm, j, abits));
+                for (int j = 0; j < 4; ++j) {
+                    float d = signed_alpha(nma, j, abits);
+                    if constexpr (kTwo) d = d + signed_alpha(nmb, j, bbits);
+                    q[j] = __float_as_uint(__uint_as_float(q[j]) + d);
+                }
             }
             __builtin_nontemporal_store(q, base + k * kWave);
         }
@@ -95,32 +119,41 @@ __global__ __launch_bounds__(256) void k_perturb_chunks(u32x4_t *__restrict__ th
 }
 
 // Ragged end: one thread per element of [start, n).
-template <bool kBF16, bool kBits>
+__device__ __forceinline__ uint32_t element_bit(uint64_t e, uint64_t blk0, uint32_t probe,
+                                                uint32_t step, uint32_t k0, uint32_t k1,
+                                                const uint8_t *bits)
+{
+    if (bits) return (bits[e >> 3] >> (e & 7)) & 1u;
+    const U32x4 r = probe_block_bits(blk0 + (e >> 7), probe, step, k0, k1);
+    const uint32_t sel = (uint32_t)(e >> 5) & 3u;
+    const uint32_t word = sel == 0 ? r.x : sel == 1 ? r.y : sel == 2 ? r.z : r.w;
+    return (word >> (e & 31)) & 1u;
+}
+
+template <bool kBF16, bool kTwo>
 __global__ __launch_bounds__(256) void k_perturb_tail(void *__restrict__ theta, uint64_t start,
                                                       uint64_t n, uint64_t blk0, uint32_t step,
-                                                      uint32_t probe, uint32_t k0, uint32_t k1,
-                                                      uint32_t abits,
-                                                      const uint8_t *__restrict__ bits)
+                                                      uint32_t probe_a, uint32_t probe_b,
+                                                      uint32_t k0, uint32_t k1, uint32_t abits,
+                                                      uint32_t bbits,
+                                                      const uint8_t *__restrict__ bits_a,
+                                                      const uint8_t *__restrict__ bits_b)
 {
     const uint64_t e = start + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (e >= n) return;
-    uint32_t bit;
-    if constexpr (kBits) {
-        bit = (bits[e >> 3] >> (e & 7)) & 1u;
-    } else {
-        const U32x4 r = probe_block_bits(blk0 + (e >> 7), probe, step, k0, k1);
-        const uint32_t sel = (uint32_t)(e >> 5) & 3u;
-        const uint32_t word = sel == 0 ? r.x : sel == 1 ? r.y : sel == 2 ? r.z : r.w;
-        bit = (word >> (e & 31)) & 1u;
+    const uint32_t bit_a = element_bit(e, blk0, probe_a, step, k0, k1, bits_a);
+    float d = __uint_as_float(abits ^ (bit_a ? 0u : 0x80000000u));
+    if constexpr (kTwo) {
+        const uint32_t bit_b = element_bit(e, blk0, probe_b, step, k0, k1, bits_b);
+        d = d + __uint_as_float(bbits ^ (bit_b ? 0u : 0x80000000u));
     }
-    const float a = __uint_as_float(abits ^ (bit ? 0u : 0x80000000u));
     if constexpr (kBF16) {
         uint16_t *t = static_cast<uint16_t *>(theta);
-        const float f = __uint_as_float((uint32_t)t[e] << 16) + a;
+        const float f = __uint_as_float((uint32_t)t[e] << 16) + d;
         t[e] = (uint16_t)(pack_bf16x2(f, 0.0f) & 0xFFFFu);
     } else {
         float *t = static_cast<float *>(theta);
-        t[e] = t[e] + a;
+        t[e] = t[e] + d;
     }
 }
 
@@ -132,9 +165,10 @@ static int env_int(const char *name, int dflt)
     return v > 0 ? v : dflt;
 }
 
-template <bool kBF16, bool kBits>
+template <bool kBF16, bool kBits, bool kTwo>
 static hipError_t perturb_impl(void *theta, uint64_t n, uint64_t blk0, uint32_t step,
-                               uint32_t probe, Key key, uint32_t abits, const uint8_t *bits,
+                               uint32_t probe_a, uint32_t probe_b, Key key, uint32_t abits,
+                               uint32_t bbits, const uint8_t *bits_a, const uint8_t *bits_b,
                                int num_cus, hipStream_t stream)
 {
     const uint64_t nchunks = n / kChunkParams;
@@ -144,15 +178,18 @@ static hipError_t perturb_impl(void *theta, uint64_t n, uint64_t blk0, uint32_t 
         const uint64_t want = (nchunks + kWavesPerWG - 1) / kWavesPerWG;
         const uint64_t cap = (uint64_t)num_cus * wg_per_cu;
         const uint32_t grid = (uint32_t)(want < cap ? want : cap);
-        hipLaunchKernelGGL((k_perturb_chunks<kBF16, kBits>), dim3(grid), dim3(256), 0, stream,
-                           static_cast<u32x4_t *>(theta), nchunks, blk0, step, probe, key.k0,
-                           key.k1, abits, reinterpret_cast<const u32x4_t *>(bits));
+        hipLaunchKernelGGL((k_perturb_chunks<kBF16, kBits, kTwo>), dim3(grid), dim3(256), 0,
+                           stream, static_cast<u32x4_t *>(theta), nchunks, blk0, step, probe_a,
+                           probe_b, key.k0, key.k1, abits, bbits,
+                           reinterpret_cast<const u32x4_t *>(bits_a),
+                           reinterpret_cast<const u32x4_t *>(bits_b));
     }
     const uint64_t start = nchunks * kChunkParams;
     if (start < n) {
         const uint32_t grid = (uint32_t)((n - start + 255) / 256);
-        hipLaunchKernelGGL((k_perturb_tail<kBF16, kBits>), dim3(grid), dim3(256), 0, stream,
-                           theta, start, n, blk0, step, probe, key.k0, key.k1, abits, bits);
+        hipLaunchKernelGGL((k_perturb_tail<kBF16, kTwo>), dim3(grid), dim3(256), 0, stream,
+                           theta, start, n, blk0, step, probe_a, probe_b, key.k0, key.k1,
+                           abits, bbits, bits_a, bits_b);
     }
     return hipGetLastError();
 }
@@ -164,14 +201,39 @@ hipError_t launch_perturb(void *theta, bool bf16, uint64_t offset, uint64_t n, K
     const uint32_t abits = __builtin_bit_cast(uint32_t, alpha);
     const uint64_t blk0 = offset / kBlockParams;
     if (bf16)
-        return bits ? perturb_impl<true, true>(theta, n, blk0, step, probe, key, abits, bits,
-                                               num_cus, stream)
-                    : perturb_impl<true, false>(theta, n, blk0, step, probe, key, abits,
-                                                bits, num_cus, stream);
-    return bits ? perturb_impl<false, true>(theta, n, blk0, step, probe, key, abits, bits,
-                                            num_cus, stream)
-                : perturb_impl<false, false>(theta, n, blk0, step, probe, key, abits, bits,
-                                             num_cus, stream);
+        return bits ? perturb_impl<true, true, false>(theta, n, blk0, step, probe, probe, key,
+                                                      abits, 0u, bits, nullptr, num_cus, stream)
+                    : perturb_impl<true, false, false>(theta, n, blk0, step, probe, probe, key,
+                                                       abits, 0u, nullptr, nullptr, num_cus,
+                                                       stream);
+    return bits ? perturb_impl<false, true, false>(theta, n, blk0, step, probe, probe, key,
+                                                   abits, 0u, bits, nullptr, num_cus, stream)
+                : perturb_impl<false, false, false>(theta, n, blk0, step, probe, probe, key,
+                                                    abits, 0u, nullptr, nullptr, num_cus,
+                                                    stream);
+}
+
+hipError_t launch_perturb2(void *theta, bool bf16, uint64_t offset, uint64_t n, Key key,
+                           uint32_t step, uint32_t probe_a, float alpha_a, uint32_t probe_b,
+                           float alpha_b, const uint8_t *bits_a, const uint8_t *bits_b,
+                           int num_cus, hipStream_t stream)
+{
+    const uint32_t abits = __builtin_bit_cast(uint32_t, alpha_a);
+    const uint32_t bbits = __builtin_bit_cast(uint32_t, alpha_b);
+    const uint64_t blk0 = offset / kBlockParams;
+    if (bf16)
+        return bits_a ? perturb_impl<true, true, true>(theta, n, blk0, step, probe_a, probe_b,
+                                                       key, abits, bbits, bits_a, bits_b,
+                                                       num_cus, stream)
+                      : perturb_impl<true, false, true>(theta, n, blk0, step, probe_a, probe_b,
+                                                        key, abits, bbits, nullptr, nullptr,
+                                                        num_cus, stream);
+    return bits_a ? perturb_impl<false, true, true>(theta, n, blk0, step, probe_a, probe_b, key,
+                                                    abits, bbits, bits_a, bits_b, num_cus,
+                                                    stream)
+                  : perturb_impl<false, false, true>(theta, n, blk0, step, probe_a, probe_b,
+                                                     key, abits, bbits, nullptr, nullptr,
+                                                     num_cus, stream);
 }
 
 }  // namespace zo

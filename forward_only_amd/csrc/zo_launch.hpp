@@ -21,6 +21,13 @@ hipError_t launch_perturb(void *theta, bool bf16, uint64_t offset, uint64_t n, K
                           uint32_t step, uint32_t probe, float alpha, const uint8_t *bits,
                           int num_cus, hipStream_t stream);
 
+// theta[0..n) += (+/-alpha_a) + (+/-alpha_b) in one pass (probes a and b); bits_a and
+// bits_b are both given or both nullptr.
+hipError_t launch_perturb2(void *theta, bool bf16, uint64_t offset, uint64_t n, Key key,
+                           uint32_t step, uint32_t probe_a, float alpha_a, uint32_t probe_b,
+                           float alpha_b, const uint8_t *bits_a, const uint8_t *bits_b,
+                           int num_cus, hipStream_t stream);
+
 // c[i] from (L+, L-, L0) in fp64; non-finite probes counted into *counter.
 hipError_t launch_probe_weights(const double *Lp, const double *Lm, const double *L0,
                                 uint32_t npert, double eps, double delta, float *c,

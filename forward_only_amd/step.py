@@ -6,6 +6,10 @@ Transformers Without Backprop: What Two Zero-Order Papers Actually Measure"): th
 loss, then per probe four in-place passes +eps, -eps (restore), -eps, +eps (restore) with
 a loss after the first and third, then the probe weights, then one update pass.
 
+schedule="S2f" visits the same points with two passes per probe: +eps z_0, then per
+probe a -2 eps z_i pass (to theta - eps z_i) and one fused pass (zo_perturb2) that restores
+probe i and applies +eps z_(i+1); the last fused pass only restores.
+
 Python only orders the launches; every pass over the parameters, the weights and the
 update run in libzo's kernels on torch's current stream.  Losses stay on the device.
 """
@@ -14,7 +18,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import zo_perturb, zo_probe_weights, zo_update
+from . import zo_perturb, zo_perturb2, zo_probe_weights, zo_update
 
 
 def applied_eps(eps: float) -> float:
@@ -24,7 +28,7 @@ def applied_eps(eps: float) -> float:
 
 def spsa_step(ctx, theta: torch.Tensor, *, step: int, npert: int, eps: float, eta: float,
               delta: float, loss=None, losses=None, offset: int = 0, bits=None,
-              buffers: dict | None = None) -> dict:
+              buffers: dict | None = None, schedule: str = "S4") -> dict:
     """Run one step in place on `theta`.
 
     loss(theta, out) writes the loss at `theta` into the one-element float64 GPU tensor
@@ -48,16 +52,32 @@ def spsa_step(ctx, theta: torch.Tensor, *, step: int, npert: int, eps: float, et
         if Lm is None:
             Lm = torch.empty(npert, dtype=torch.float64, device=theta.device)
         loss(theta, L0)
-    for i in range(npert):
-        row = None if bits is None else bits[i]
-        zo_perturb(ctx, theta, offset, step, i, +a, row)
-        if losses is None:
-            loss(theta, Lp[i:i + 1])
-        zo_perturb(ctx, theta, offset, step, i, -a, row)
-        zo_perturb(ctx, theta, offset, step, i, -a, row)
-        if losses is None:
-            loss(theta, Lm[i:i + 1])
-        zo_perturb(ctx, theta, offset, step, i, +a, row)
+    row = (lambda i: None) if bits is None else (lambda i: bits[i])
+    if schedule == "S4":
+        for i in range(npert):
+            zo_perturb(ctx, theta, offset, step, i, +a, row(i))
+            if losses is None:
+                loss(theta, Lp[i:i + 1])
+            zo_perturb(ctx, theta, offset, step, i, -a, row(i))
+            zo_perturb(ctx, theta, offset, step, i, -a, row(i))
+            if losses is None:
+                loss(theta, Lm[i:i + 1])
+            zo_perturb(ctx, theta, offset, step, i, +a, row(i))
+    elif schedule == "S2f":
+        if npert > 0:
+            zo_perturb(ctx, theta, offset, step, 0, +a, row(0))
+        for i in range(npert):
+            if losses is None:
+                loss(theta, Lp[i:i + 1])
+            zo_perturb(ctx, theta, offset, step, i, -2.0 * a, row(i))
+            if losses is None:
+                loss(theta, Lm[i:i + 1])
+            if i + 1 < npert:
+                zo_perturb2(ctx, theta, offset, step, i, +a, i + 1, +a, row(i), row(i + 1))
+            else:
+                zo_perturb(ctx, theta, offset, step, i, +a, row(i))
+    else:
+        raise ValueError(f"unknown schedule {schedule!r}")
     c = zo_probe_weights(ctx, Lp, Lm, L0, a, delta, out=b.get("c"))
     zo_update(ctx, theta, offset, step, c, eta, bits)
     return {"L0": L0, "Lp": Lp, "Lm": Lm, "c": c}

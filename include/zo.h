@@ -96,6 +96,19 @@ zo_status zo_perturb(zo_ctx *ctx, void *d_theta, zo_dtype dtype, uint64_t offset
                      uint64_t n, uint32_t step, uint32_t probe, float alpha,
                      const uint8_t *d_bits, void *stream);
 
+/* Two probes in one in-place pass: theta_j <- round(theta_j + d_j) with
+ * d_j = (+/-alpha_a) + (+/-alpha_b) added in fp32 (exact when |alpha_a| == |alpha_b|),
+ * then the same add and nearest-even narrow as zo_perturb.  It fuses the restore of
+ * probe a (alpha_a = +eps after its -eps point) with the +eps move of probe b, so that a
+ * step visits every theta +/- eps*z_i ("How 1.5-SPSA Works") in two passes per probe
+ * instead of four; with alpha_b = 0 it is zo_perturb of probe a.
+ * d_bits_a / d_bits_b: both NULL (regenerate) or both the probes' packed rows.
+ * Errors (ZO_EINVAL): as zo_perturb, or exactly one of the two rows given. */
+zo_status zo_perturb2(zo_ctx *ctx, void *d_theta, zo_dtype dtype, uint64_t offset,
+                      uint64_t n, uint32_t step, uint32_t probe_a, float alpha_a,
+                      uint32_t probe_b, float alpha_b, const uint8_t *d_bits_a,
+                      const uint8_t *d_bits_b, void *stream);
+
 /* Probe weights ("How 1.5-SPSA Works" for the central difference; "Probe-Space
  * Preconditioning" for the clean-pass curvature weight), computed in fp64:
  *   g_i = (L+_i - L-_i) / (2 eps),   h_i = ((L+_i + L-_i) - 2 L0) / eps^2,

@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         "ora_f32_to_bf16_array": (None, [f32p, u16p, u64]),
         "ora_perturb_f32": (None, [f32p, u64, u64, u64, u32, u32, f32, u8p]),
         "ora_perturb_bf16": (None, [u16p, u64, u64, u64, u32, u32, f32, u8p]),
+        "ora_perturb2_f32": (None, [f32p, u64, u64, u64, u32, u32, f32, u32, f32, u8p, u8p]),
+        "ora_perturb2_bf16": (None, [u16p, u64, u64, u64, u32, u32, f32, u32, f32, u8p, u8p]),
         "ora_probe_weights": (u32, [f64p, f64p, f64, u32, f64, f64, f32p]),
         "ora_update_f32": (None, [f32p, u64, u64, u64, u32, f32p, u32, f32, u8p]),
         "ora_update_bf16": (None, [u16p, u64, u64, u64, u32, f32p, u32, f32, u8p]),
@@ -165,6 +167,21 @@ def perturb(theta: np.ndarray, offset: int, seed: int, step: int, probe: int, al
     elif theta.dtype == np.uint16:
         lib().ora_perturb_bf16(_ptr(theta, ctypes.c_uint16), theta.size, offset, seed, step,
                                probe, a, _bits_ptr(bits))
+    else:
+        raise TypeError(theta.dtype)
+
+
+def perturb2(theta: np.ndarray, offset: int, seed: int, step: int, probe_a: int,
+             alpha_a: float, probe_b: int, alpha_b: float, bits_a=None, bits_b=None) -> None:
+    """theta <- round(theta + ((+/-alpha_a) + (+/-alpha_b))) in one pass, in place."""
+    assert offset % 128 == 0
+    aa, ab = float(np.float32(alpha_a)), float(np.float32(alpha_b))
+    if theta.dtype == np.float32:
+        lib().ora_perturb2_f32(_ptr(theta, ctypes.c_float), theta.size, offset, seed, step,
+                               probe_a, aa, probe_b, ab, _bits_ptr(bits_a), _bits_ptr(bits_b))
+    elif theta.dtype == np.uint16:
+        lib().ora_perturb2_bf16(_ptr(theta, ctypes.c_uint16), theta.size, offset, seed, step,
+                                probe_a, aa, probe_b, ab, _bits_ptr(bits_a), _bits_ptr(bits_b))
     else:
         raise TypeError(theta.dtype)
 

@@ -15,6 +15,10 @@ Measure"):
   4. the update theta <- theta - eta * sum_i c_i z_i.
 
 The eps handed to the weights is the fp32 value that the passes actually added.
+
+schedule="S2f" visits the same perturbed points with two passes per probe instead of
+four: +eps z_0; then for each i a pass of -2 eps z_i (to theta - eps z_i) and a fused pass
+that restores probe i and applies +eps z_(i+1) (the last one only restores).
 """
 from __future__ import annotations
 
@@ -23,14 +27,14 @@ import numpy as np
 
 def spsa_step(theta: np.ndarray, *, seed: int, step: int, npert: int, eps: float,
               eta: float, delta: float, loss_fn=None, losses=None, offset: int = 0,
-              bits=None) -> dict:
+              bits=None, schedule: str = "S4") -> dict:
     """Run one step in place on `theta` (float32, or uint16 bf16 bits).
 
     loss_fn(theta) -> float gives the losses; alternatively `losses` = (L0, Lp, Lm)
     supplies them (synthetic losses, or losses measured elsewhere), and the perturb and
     restore passes still run.  bits: optional (npert, plane_bytes) packed rows.
     """
-    from . import perturb, probe_weights, update  # late import: package init order
+    from . import perturb, perturb2, probe_weights, update  # late import: package init order
 
     a = float(np.float32(eps))
     if losses is not None:
@@ -40,16 +44,32 @@ def spsa_step(theta: np.ndarray, *, seed: int, step: int, npert: int, eps: float
         L0 = float(loss_fn(theta))
         Lp = np.zeros(npert, dtype=np.float64)
         Lm = np.zeros(npert, dtype=np.float64)
-    for i in range(npert):
-        row = None if bits is None else bits[i]
-        perturb(theta, offset, seed, step, i, +a, row)
-        if losses is None:
-            Lp[i] = loss_fn(theta)
-        perturb(theta, offset, seed, step, i, -a, row)
-        perturb(theta, offset, seed, step, i, -a, row)
-        if losses is None:
-            Lm[i] = loss_fn(theta)
-        perturb(theta, offset, seed, step, i, +a, row)
+    row = (lambda i: None) if bits is None else (lambda i: bits[i])
+    if schedule == "S4":
+        for i in range(npert):
+            perturb(theta, offset, seed, step, i, +a, row(i))
+            if losses is None:
+                Lp[i] = loss_fn(theta)
+            perturb(theta, offset, seed, step, i, -a, row(i))
+            perturb(theta, offset, seed, step, i, -a, row(i))
+            if losses is None:
+                Lm[i] = loss_fn(theta)
+            perturb(theta, offset, seed, step, i, +a, row(i))
+    elif schedule == "S2f":
+        if npert > 0:
+            perturb(theta, offset, seed, step, 0, +a, row(0))
+        for i in range(npert):
+            if losses is None:
+                Lp[i] = loss_fn(theta)
+            perturb(theta, offset, seed, step, i, -2.0 * a, row(i))
+            if losses is None:
+                Lm[i] = loss_fn(theta)
+            if i + 1 < npert:
+                perturb2(theta, offset, seed, step, i, +a, i + 1, +a, row(i), row(i + 1))
+            else:
+                perturb(theta, offset, seed, step, i, +a, row(i))
+    else:
+        raise ValueError(schedule)
     c, bad = probe_weights(Lp, Lm, L0, a, delta)
     update(theta, offset, seed, step, c, eta, bits)
     return {"L0": L0, "Lp": Lp, "Lm": Lm, "c": c, "nonfinite": bad}

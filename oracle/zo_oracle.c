@@ -184,6 +184,46 @@ void ora_perturb_bf16(uint16_t *th, uint64_t n, uint64_t offset, uint64_t seed,
     }
 }
 
+/* Fused move of two probes in one pass: theta_j <- round(theta_j + d_j) with
+ * d_j = (+/-alpha_a) + (+/-alpha_b) formed in fp32 (exact when |alpha_a| == |alpha_b|,
+ * the case of a restore of probe a fused with the next probe b), then the same fp32 add
+ * (and for bf16 the same nearest-even narrow) as a single-probe perturb.  The restore of
+ * one probe and the +eps move of the next ("How 1.5-SPSA Works": losses at theta +/-
+ * eps*z_i, restoring in between) thereby take one pass instead of two. */
+static float ora_fused_delta(int bit_a, float alpha_a, int bit_b, float alpha_b)
+{
+    float da = bit_a ? alpha_a : -alpha_a;
+    float db = bit_b ? alpha_b : -alpha_b;
+    return da + db;
+}
+
+void ora_perturb2_f32(float *th, uint64_t n, uint64_t offset, uint64_t seed, uint32_t step,
+                      uint32_t probe_a, float alpha_a, uint32_t probe_b, float alpha_b,
+                      const uint8_t *bits_a, const uint8_t *bits_b)
+{
+    for (uint64_t e = 0; e < n; ++e) {
+        int ba = bits_a ? ora_plane_bit(bits_a, e)
+                        : (ora_sign(seed, step, probe_a, offset + e) > 0);
+        int bb = bits_b ? ora_plane_bit(bits_b, e)
+                        : (ora_sign(seed, step, probe_b, offset + e) > 0);
+        th[e] = th[e] + ora_fused_delta(ba, alpha_a, bb, alpha_b);
+    }
+}
+
+void ora_perturb2_bf16(uint16_t *th, uint64_t n, uint64_t offset, uint64_t seed, uint32_t step,
+                       uint32_t probe_a, float alpha_a, uint32_t probe_b, float alpha_b,
+                       const uint8_t *bits_a, const uint8_t *bits_b)
+{
+    for (uint64_t e = 0; e < n; ++e) {
+        int ba = bits_a ? ora_plane_bit(bits_a, e)
+                        : (ora_sign(seed, step, probe_a, offset + e) > 0);
+        int bb = bits_b ? ora_plane_bit(bits_b, e)
+                        : (ora_sign(seed, step, probe_b, offset + e) > 0);
+        float t = ora_bf16_to_f32(th[e]) + ora_fused_delta(ba, alpha_a, bb, alpha_b);
+        th[e] = ora_f32_to_bf16(t);
+    }
+}
+
 /* ---------------------------------------------------------------------------------- */
 /* Probe weights ("How 1.5-SPSA Works" for g; "Probe-Space Preconditioning" for the   */
 /* clean-pass curvature weighting), in double:                                       */

@@ -350,3 +350,78 @@ def test_bf16_synthetic_step_small(ctx):
                            delta=cfg.delta, losses=(L0, Lp, Lm))
     assert np.array_equal(out["c"].cpu().numpy(), res["c"])
     assert_bf16_within_ulp(bf16_bits(t), h)
+
+
+# ------------------------------------------------------------------------------------
+# fused two-probe pass and the two-pass schedule
+# ------------------------------------------------------------------------------------
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+@pytest.mark.parametrize("n,offset", [(8192 * 3 + 1000, 0), (127, 128), (1 << 22, 128 * 9)])
+@pytest.mark.parametrize("mode", ["regen", "bits"])
+def test_perturb2_bit_exact(ctx, kind, n, offset, mode):
+    step, pa, pb = 2, 5, 6
+    h = _theta(kind, n, seed=n + 1, scale=0.02, specials=True)
+    t = _dev(kind, h)
+    if mode == "bits":
+        ra, rb = (oracle.gen_plane(SEED, step, p, offset, n) for p in (pa, pb))
+        da, db = torch.from_numpy(ra).cuda(), torch.from_numpy(rb).cuda()
+    else:
+        ra = rb = da = db = None
+    for aa, ab in ((1e-3, 1e-3), (-2e-3, 1e-3), (1e-3, -3e-3), (2.0 ** -10, 0.0)):
+        zo.zo_perturb2(ctx, t, offset, step, pa, aa, pb, ab, da, db)
+        oracle.perturb2(h, offset, SEED, step, pa, aa, pb, ab, ra, rb)
+        assert_same_bits_or_nan(_host(kind, t), h, kind)
+
+
+def test_perturb2_requires_both_rows(ctx):
+    t = torch.zeros(256, dtype=torch.float32, device="cuda")
+    row = torch.zeros(zo.zo_bits_stride(256), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        zo.zo_perturb2(ctx, t, 0, 0, 0, 1.0, 1, 1.0, row, None)
+    from forward_only_amd import _lib
+    st = _lib.lib().zo_perturb2(ctx.handle, t.data_ptr(), 0, 0, 256, 0, 0, 1.0, 1, 1.0,
+                                row.data_ptr(), None, None)
+    assert st == zo.ZO_EINVAL
+
+
+@pytest.mark.parametrize("mode", ["regen", "bits"])
+def test_tiny_config_two_pass_schedule(ctx, mode):
+    """The tiny workload with the two-pass schedule: weights bit-identical to the oracle fed
+    the GPU's losses, theta within the update tolerance, loss going down."""
+    cfg = CONFIGS["tiny"]
+    local = zo.zo_init(cfg.seed)
+    th0, a = gen.theta_and_a(cfg)
+    t, ad, h = to_dev_f32(th0), to_dev_f32(a), th0.copy()
+    lossf = lambda x, o: zo.zo_quad_loss(local, x, ad, out=o)  # noqa: E731
+    first = oracle.quad_loss(h, a)
+    for step in range(cfg.steps):
+        bits_h = oracle.gen_planes(cfg.seed, step, 0, cfg.npert, 0, cfg.M) if mode == "bits" else None
+        bits_d = torch.from_numpy(bits_h).cuda() if mode == "bits" else None
+        out = spsa_step(local, t, step=step, npert=cfg.npert, eps=cfg.eps, eta=cfg.eta,
+                        delta=cfg.delta, loss=lossf, bits=bits_d, schedule="S2f")
+        L0, Lp, Lm = out["L0"].item(), out["Lp"].cpu().numpy(), out["Lm"].cpu().numpy()
+        res = oracle.spsa_step(h, seed=cfg.seed, step=step, npert=cfg.npert, eps=cfg.eps,
+                               eta=cfg.eta, delta=cfg.delta, losses=(L0, Lp, Lm), bits=bits_h,
+                               schedule="S2f")
+        assert np.array_equal(out["c"].cpu().numpy(), res["c"])
+        got = t.cpu().numpy()
+        assert_f32_update_close(got, h, cfg.eta, res["c"])
+        h = got.copy()
+    assert oracle.quad_loss(h, a) < first
+    local.close()
+
+
+def test_bf16_synthetic_two_pass_step_small(ctx):
+    cfg = CONFIGS["opt30b"]
+    n, npert = 8192 * 4 + 555, cfg.npert
+    h = _theta("bf16", n, seed=13, scale=0.02)
+    t = to_dev_bf16(h)
+    L0, Lp, Lm = gen.synthetic_losses(cfg.seed, 1, npert)
+    dl = (torch.tensor([L0], dtype=torch.float64).cuda(), torch.from_numpy(Lp).cuda(),
+          torch.from_numpy(Lm).cuda())
+    spsa_step(ctx, t, step=1, npert=npert, eps=cfg.eps, eta=0.0, delta=cfg.delta, losses=dl,
+              schedule="S2f")
+    oracle.spsa_step(h, seed=SEED, step=1, npert=npert, eps=cfg.eps, eta=0.0,
+                     delta=cfg.delta, losses=(L0, Lp, Lm), schedule="S2f")
+    # eta = 0: the passes alone, which are bit-exact
+    assert np.array_equal(bf16_bits(t), h)

@@ -185,3 +185,73 @@ def test_perturb_nan_inf_denormal():
     d = np.array([1e-40], dtype=np.float32)
     oracle.perturb(d, 0, 0, 0, 0, 0.0)
     assert d[0] == np.float32(1e-40) and d[0] != 0.0
+
+
+# ------------------------------------------------------------------------------------
+# fused two-probe pass (restore of probe a + move of probe b in one pass)
+# ------------------------------------------------------------------------------------
+def test_perturb2_reduces_to_single_probe():
+    n = 3000
+    rng = np.random.default_rng(21)
+    for kind in ("f32", "bf16"):
+        base = (rng.standard_normal(n) * 0.02).astype(np.float32)
+        t0 = base if kind == "f32" else oracle.f32_to_bf16(base)
+        # alpha_b = 0: the single-probe move of probe a
+        x, y = t0.copy(), t0.copy()
+        oracle.perturb2(x, 128, 4, 1, 7, 1e-3, 9, 0.0)
+        oracle.perturb(y, 128, 4, 1, 7, 1e-3)
+        assert np.array_equal(x, y), kind
+        # the same probe twice: one move by 2 alpha
+        x, y = t0.copy(), t0.copy()
+        oracle.perturb2(x, 0, 4, 1, 7, 1e-3, 7, 1e-3)
+        oracle.perturb(y, 0, 4, 1, 7, 2e-3)
+        assert np.array_equal(x, y), kind
+
+
+def test_perturb2_bf16_against_exact_rounding():
+    n = 500
+    rng = np.random.default_rng(22)
+    h0 = oracle.f32_to_bf16((rng.standard_normal(n) * 0.02).astype(np.float32))
+    za = oracle.signs_from_plane(oracle.gen_plane(5, 2, 3, 0, n), n).astype(np.float32)
+    zb = oracle.signs_from_plane(oracle.gen_plane(5, 2, 4, 0, n), n).astype(np.float32)
+    aa, ab = np.float32(1e-3), np.float32(-3e-3)
+    h = h0.copy()
+    oracle.perturb2(h, 0, 5, 2, 3, float(aa), 4, float(ab))
+    d = (aa * za) + (ab * zb)                    # numpy fp32 adds
+    t = oracle.bf16_to_f32(h0) + d
+    for j in range(n):
+        assert int(h[j]) == brute_bf16(float(t[j])), j
+
+
+def test_s2f_and_s4_visit_the_same_points_on_exact_inputs():
+    # On a binary grid every move is exact, so both schedules evaluate the loss at exactly
+    # theta +/- eps z_i and leave theta where it started: identical losses and weights.
+    M, n = 4096, 12
+    rng = np.random.Generator(np.random.PCG64(31))
+    th0 = (rng.integers(-4095, 4096, M) / 256.0).astype(np.float32)
+    a = (rng.integers(1, 256, M) / 16.0).astype(np.float32)
+    lossf = lambda t: oracle.quad_loss(t, a)  # noqa: E731
+    out = {}
+    for sch in ("S4", "S2f"):
+        th = th0.copy()
+        out[sch] = oracle.spsa_step(th, seed=3, step=1, npert=n, eps=2.0 ** -8, eta=2.0 ** -12,
+                                    delta=1e-6, loss_fn=lossf, schedule=sch)
+        out[sch]["theta"] = th
+    for k in ("Lp", "Lm", "c", "theta"):
+        assert np.array_equal(out["S4"][k], out["S2f"][k]), k
+    assert out["S4"]["L0"] == out["S2f"]["L0"]
+
+
+def test_s2f_bf16_drift_is_bounded():
+    # The two-pass schedule, run without an update, leaves bf16 theta within one ulp of
+    # |theta| + eps of its start however many probes it runs.
+    n = 20000
+    rng = np.random.Generator(np.random.PCG64(0))
+    h0 = oracle.f32_to_bf16((rng.standard_normal(n) * 0.02).astype(np.float32))
+    x0 = oracle.bf16_to_f32(h0).astype(np.float64)
+    ulp = np.spacing((np.abs(x0) + 1e-3).astype(np.float32)).astype(np.float64) * 2.0 ** 16
+    h = h0.copy()
+    L = (np.zeros(64), np.zeros(64))
+    oracle.spsa_step(h, seed=0, step=0, npert=64, eps=1e-3, eta=0.0, delta=1e-6,
+                     losses=(0.0, L[0], L[1]), schedule="S2f")
+    assert np.all(np.abs(oracle.bf16_to_f32(h) - x0) <= ulp)
