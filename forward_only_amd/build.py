@@ -21,6 +21,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libzo.so")
+CEILING_SRC = os.path.join(HERE, "ceiling", "hbm_ceiling.hip")
+CEILING_BIN = os.path.join(HERE, "hbm_ceiling")
 ARCH = os.environ.get("ZO_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -60,7 +62,21 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_ceiling(verbose)
     return LIB
+
+
+def build_ceiling(verbose: bool = False) -> str:
+    """The standalone HBM-ceiling microbenchmark (read, write, copy, in-place RMW)."""
+    tmp = CEILING_BIN + f".tmp{os.getpid()}"
+    cmd = [HIPCC, *CFLAGS, "-o", tmp, CEILING_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {CEILING_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, CEILING_BIN)
+    return CEILING_BIN
 
 
 if __name__ == "__main__":
