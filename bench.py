@@ -34,6 +34,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix, vendor figure
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_perturb.json")
 PERTURB_SOURCES = ["forward_only_amd/csrc/k_perturb.hip", "forward_only_amd/csrc/zo_device.hpp"]
 
@@ -48,7 +49,7 @@ def parse_args(argv=None):
     p.add_argument("--steps", type=int, default=None, help="timed steps (default: config's)")
     p.add_argument("--warmup", type=int, default=1)
     p.add_argument("--config", default="opt30b",
-                   choices=["tiny", "flat125m", "opt13b", "opt30b"])
+                   choices=["tiny", "flat125m", "mlp", "opt13b", "opt30b"])
     p.add_argument("--schedule", default="S2f", choices=["S2f", "S4"],
                    help="S2f: two passes per probe (restore fused with the next probe's "
                         "move); S4: four passes per probe")
@@ -165,7 +166,7 @@ def main(argv=None):
 
     # CPU oracle leg first (host only; keeps the GPU phase uninterrupted).
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and cfg.loss != "mlp":
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         log(f"[bench] cpu baseline: {threads} threads x {args.cpu_params_per_thread} params")
         cpu = cpu_baseline(cfg, args.cpu_params_per_thread, threads, args.schedule)
@@ -177,7 +178,19 @@ def main(argv=None):
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     theta = torch.empty(M, dtype=tdt, device=dev)
     a_dev = None
-    if cfg.loss == "quad":
+    mlp = None
+    if cfg.loss == "mlp":
+        e = cfg.extra
+        X, y = gen.mlp_data(cfg)
+        th0, _ = gen.theta_and_a(cfg)
+        theta.copy_(torch.from_numpy(th0))
+        mlp = {"X": torch.from_numpy(X).to(dev), "y": torch.from_numpy(y).to(dev),
+               "ws": torch.empty(zo.zo_mlp_workspace_bytes(e["batch"], e["d_in"], e["d_hid"],
+                                                           e["d_out"]), dtype=torch.uint8,
+                                 device=dev), "d_hid": e["d_hid"], "d_out": e["d_out"],
+               "flop": 2.0 * e["batch"] * e["d_in"] * e["d_hid"]}
+        del th0
+    elif cfg.loss == "quad":
         th0, a = gen.theta_and_a(cfg)
         theta.copy_(torch.from_numpy(th0))
         a_dev = torch.from_numpy(a).to(dev)
@@ -201,7 +214,7 @@ def main(argv=None):
     a = applied_eps(cfg.eps)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    per = {"perturb": [], "perturb2": [], "weights": [], "update": [], "loss": []}
+    per = {"perturb": [], "perturb2": [], "weights": [], "update": [], "loss": [], "mlp": []}
 
     def timed(kind, fn, record):
         if record:
@@ -217,8 +230,28 @@ def main(argv=None):
         if cfg.loss == "quad":
             timed("loss", lambda: zo.zo_quad_loss(ctx, theta, a_dev, out=out), record)
 
+    def mlp_loss(out, probe, alpha, s, record):
+        if probe is None:
+            timed("mlp", lambda: zo.zo_mlp_loss(ctx, theta, mlp["X"], mlp["y"], mlp["d_hid"],
+                                                 mlp["d_out"], workspace=mlp["ws"], out=out),
+                  record)
+        else:
+            timed("mlp", lambda: zo.zo_mlp_loss_perturbed(
+                ctx, theta, 0, s, probe, alpha, mlp["X"], mlp["y"], mlp["d_hid"],
+                mlp["d_out"], workspace=mlp["ws"], out=out), record)
+
     def one_step(s, record):
         L0, Lp, Lm = L0s[s], Lps[s], Lms[s]
+        if mlp is not None:
+            # the forward applies each probe while reading the weights: no passes over theta
+            mlp_loss(L0, None, 0.0, s, record)
+            for i in range(n):
+                mlp_loss(Lp[i:i + 1], i, +a, s, record)
+                mlp_loss(Lm[i:i + 1], i, -a, s, record)
+            timed("weights", lambda: zo.zo_probe_weights(ctx, Lp, Lm, L0, a, cfg.delta,
+                                                         out=c_buf), record)
+            timed("update", lambda: zo.zo_update(ctx, theta, 0, s, c_buf, cfg.eta), record)
+            return
         loss_into(L0, record)
         if args.schedule == "S4":
             for i in range(n):
@@ -268,10 +301,19 @@ def main(argv=None):
     value = n * M / T
     # every pass of either perturb entry point runs k_perturb_chunks (one or two probes)
     pert_ms, upd_ms, w_ms = avg_ms("perturb", "perturb2"), avg_ms("update"), avg_ms("weights")
-    passes = 4 * n if args.schedule == "S4" else 2 * n + 1
+    passes = 0 if mlp is not None else (4 * n if args.schedule == "S4" else 2 * n + 1)
     pass_bytes = 2.0 * esize * M                      # one read + one write of theta
     step_bytes = (passes + 1) * pass_bytes            # the passes + the update
-    achieved = pass_bytes / (pert_ms * 1e-3) / 1e9
+    if mlp is not None:
+        mlp_ms = avg_ms("mlp")
+        achieved = mlp["flop"] / (mlp_ms * 1e-3) / 1e12
+        roofline = {"kernel": "k_mlp_tiles (MFMA fp32 GEMM of the MLP forward, fused probe)",
+                    "bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS,
+                    "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
+                    "traffic": None}
+    else:
+        achieved = pass_bytes / (pert_ms * 1e-3) / 1e9
+        roofline = None
     traffic = stored_traffic(f"{cfg.name}/{args.schedule}", pass_bytes)
     result = {
         "metric": "probe*params/s and HBM GB/s (% peak) per 1.5-SPSA step, n_pert=160, 1 GPU",
@@ -287,22 +329,26 @@ def main(argv=None):
         "dtype": cfg.dtype,
         "data": "synthetic",
         "config": {"workload": (f"{cfg.name}: {M} {cfg.dtype} params in one flat buffer, "
-                                f"n_pert={n}, eps={cfg.eps}, eta={cfg.eta}, schedule "
-                                f"{args.schedule} ({passes} passes + update), probes "
-                                f"regenerated, losses "
-                                f"{'synthetic' if cfg.loss == 'synthetic' else cfg.loss}"),
-                   "params": M, "n_pert": n, "schedule": args.schedule,
+                                f"n_pert={n}, eps={cfg.eps}, eta={cfg.eta}, " +
+                                ("probes applied inside the MFMA forward (no passes over "
+                                 "theta) + update" if mlp is not None else
+                                 f"schedule {args.schedule} ({passes} passes + update)") +
+                                ", probes regenerated, losses " +
+                                ("synthetic" if cfg.loss == "synthetic" else cfg.loss)),
+                   "params": M, "n_pert": n,
+                   "schedule": "fused forward" if mlp is not None else args.schedule,
                    "passes_per_step": passes + 1},
         "hbm_gbps": step_bytes / T / 1e9,
         "hbm_frac_of_peak": step_bytes / T / 1e9 / PEAK_HBM_GBPS,
         "kernels_ms": {"pass_avg": pert_ms, "perturb_avg": avg_ms("perturb"),
                        "perturb2_avg": avg_ms("perturb2"), "update_avg": upd_ms,
-                       "weights_avg": w_ms, "loss_avg": avg_ms("loss")},
-        "roofline": {"kernel": f"k_perturb_chunks ({cfg.dtype}, probes regenerated; every "
-                               f"zo_perturb / zo_perturb2 pass)",
-                     "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": traffic},
+                       "weights_avg": w_ms, "loss_avg": avg_ms("loss"),
+                       "mlp_forward_avg": avg_ms("mlp")},
+        "roofline": roofline or {"kernel": f"k_perturb_chunks ({cfg.dtype}, probes regenerated; "
+                                           f"every zo_perturb / zo_perturb2 pass)",
+                                 "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
+                                 "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                                 "traffic": traffic},
         "update_roofline": {"achieved_GBps": pass_bytes / (upd_ms * 1e-3) / 1e9,
                             "probe_params_per_s": n * M / (upd_ms * 1e-3)},
         "nonfinite_probes": nonfinite,

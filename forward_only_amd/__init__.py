@@ -25,7 +25,8 @@ from ._lib import (ZO_BF16, ZO_EHIP, ZO_EINVAL, ZO_ENOMEM, ZO_EUNSUPPORTED, ZO_F
 __all__ = [
     "Context", "ZOError", "zo_init", "zo_destroy", "zo_bits_stride", "zo_gen_probes",
     "zo_perturb", "zo_perturb2", "zo_probe_weights", "zo_update", "zo_nonfinite_count",
-    "zo_reset_nonfinite", "zo_quad_loss", "library_path",
+    "zo_reset_nonfinite", "zo_quad_loss", "zo_mlp_workspace_bytes", "zo_mlp_loss",
+    "zo_mlp_loss_perturbed", "library_path",
 ]
 
 
@@ -194,4 +195,57 @@ def zo_quad_loss(ctx: Context, theta: torch.Tensor, a: torch.Tensor,
                                        _dev(a, "a", torch.float32), theta.numel(),
                                        _dev(out, "out", torch.float64), _stream(stream)),
                "zo_quad_loss")
+    return out
+
+
+def zo_mlp_workspace_bytes(batch: int, d_in: int, d_hid: int, d_out: int) -> int:
+    return int(_lib.lib().zo_mlp_workspace_bytes(batch, d_in, d_hid, d_out))
+
+
+def _mlp_args(params, X, labels, d_hid, d_out, workspace, out):
+    batch, d_in = X.shape
+    nparams = d_hid * d_in + d_hid + d_out * d_hid + d_out
+    if params.numel() != nparams:
+        raise ValueError(f"params must hold {nparams} values")
+    if labels.numel() != batch:
+        raise ValueError("one label per row")
+    need = zo_mlp_workspace_bytes(batch, d_in, d_hid, d_out)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device="cuda")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float64, device="cuda")
+    return (batch, d_in, _dev(params, "params", torch.float32), _dev(X, "X", torch.float32),
+            _dev(labels, "labels", torch.int64), workspace, _dev(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), out)
+
+
+def zo_mlp_loss(ctx: Context, params: torch.Tensor, X: torch.Tensor, labels: torch.Tensor,
+                d_hid: int, d_out: int, workspace: torch.Tensor | None = None,
+                out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Mean cross-entropy of the MLP at `params` into a one-element float64 GPU tensor."""
+    batch, d_in, pp, px, pl, ws, pw, wbytes, out = _mlp_args(params, X, labels, d_hid, d_out,
+                                                             workspace, out)
+    _lib.check(_lib.lib().zo_mlp_loss(ctx.handle, pp, px, pl, batch, d_in, d_hid, d_out, pw,
+                                      wbytes, _dev(out, "out", torch.float64), _stream(stream)),
+               "zo_mlp_loss")
+    return out
+
+
+def zo_mlp_loss_perturbed(ctx: Context, params: torch.Tensor, offset: int, step: int,
+                          probe: int, alpha: float, X: torch.Tensor, labels: torch.Tensor,
+                          d_hid: int, d_out: int, bits: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None,
+                          out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The MLP loss at params + alpha * z_probe, without writing params."""
+    batch, d_in, pp, px, pl, ws, pw, wbytes, out = _mlp_args(params, X, labels, d_hid, d_out,
+                                                             workspace, out)
+    bp = None
+    if bits is not None:
+        bp = _dev(bits, "bits", torch.uint8)
+        if bits.numel() < zo_bits_stride(params.numel()):
+            raise ValueError("bits row is too short")
+    _lib.check(_lib.lib().zo_mlp_loss_perturbed(
+        ctx.handle, pp, offset, step, probe, float(alpha), bp, px, pl, batch, d_in, d_hid,
+        d_out, pw, wbytes, _dev(out, "out", torch.float64), _stream(stream)),
+        "zo_mlp_loss_perturbed")
     return out

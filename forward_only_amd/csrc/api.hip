@@ -195,4 +195,56 @@ zo_status zo_quad_loss(zo_ctx *c, const void *d_theta, zo_dtype dtype, const flo
                                          as_stream(stream)));
 }
 
+uint64_t zo_mlp_workspace_bytes(uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out)
+{
+    (void)d_in;
+    return ((uint64_t)(d_hid / 16u) * batch * d_out + batch) * sizeof(double);
+}
+
+static zo_status mlp_checks(zo_ctx *c, const float *d_params, const float *d_X,
+                            const int64_t *d_labels, uint32_t batch, uint32_t d_in,
+                            uint32_t d_hid, uint32_t d_out, void *d_workspace,
+                            uint64_t workspace_bytes, double *d_loss)
+{
+    if (!c || !d_params || !d_X || !d_labels || !d_workspace || !d_loss) return ZO_EINVAL;
+    if (batch == 0 || d_in == 0 || d_hid == 0 || batch % 16u || d_in % 16u || d_hid % 16u)
+        return ZO_EINVAL;
+    if (d_out == 0 || d_out > 16u) return ZO_EINVAL;
+    if (!aligned16(d_params) || !aligned16(d_X) || (reinterpret_cast<uintptr_t>(d_workspace) & 7u))
+        return ZO_EINVAL;
+    if (workspace_bytes < zo_mlp_workspace_bytes(batch, d_in, d_hid, d_out)) return ZO_EINVAL;
+    return ZO_OK;
+}
+
+zo_status zo_mlp_loss(zo_ctx *c, const float *d_params, const float *d_X,
+                      const int64_t *d_labels, uint32_t batch, uint32_t d_in, uint32_t d_hid,
+                      uint32_t d_out, void *d_workspace, uint64_t workspace_bytes,
+                      double *d_loss, void *stream)
+{
+    const zo_status st = mlp_checks(c, d_params, d_X, d_labels, batch, d_in, d_hid, d_out,
+                                    d_workspace, workspace_bytes, d_loss);
+    if (st != ZO_OK) return st;
+    return from_hip(zo::launch_mlp_loss(d_params, d_X, d_labels, batch, d_in, d_hid, d_out,
+                                        static_cast<double *>(d_workspace), d_loss, nullptr,
+                                        key_of(c), as_stream(stream)));
+}
+
+zo_status zo_mlp_loss_perturbed(zo_ctx *c, const float *d_params, uint64_t offset,
+                                uint32_t step, uint32_t probe, float alpha,
+                                const uint8_t *d_bits, const float *d_X,
+                                const int64_t *d_labels, uint32_t batch, uint32_t d_in,
+                                uint32_t d_hid, uint32_t d_out, void *d_workspace,
+                                uint64_t workspace_bytes, double *d_loss, void *stream)
+{
+    const zo_status st = mlp_checks(c, d_params, d_X, d_labels, batch, d_in, d_hid, d_out,
+                                    d_workspace, workspace_bytes, d_loss);
+    if (st != ZO_OK) return st;
+    const uint64_t nparams = (uint64_t)d_hid * d_in + d_hid + (uint64_t)d_out * d_hid + d_out;
+    if (!range_ok(offset, nparams)) return ZO_EINVAL;
+    const zo::MlpPerturb pert{offset, step, probe, alpha, d_bits};
+    return from_hip(zo::launch_mlp_loss(d_params, d_X, d_labels, batch, d_in, d_hid, d_out,
+                                        static_cast<double *>(d_workspace), d_loss, &pert,
+                                        key_of(c), as_stream(stream)));
+}
+
 }  // extern "C"

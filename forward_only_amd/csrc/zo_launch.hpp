@@ -46,4 +46,17 @@ constexpr uint32_t kLossPartials = 1024;
 hipError_t launch_quad_loss(const void *theta, bool bf16, const float *a, uint64_t n,
                             double *partials, double *out, hipStream_t stream);
 
+// Two-layer MLP classifier loss (fp32 parameters, MFMA GEMM, fp64 reduction); with
+// `pert` the parameters are read as theta + alpha * z_probe without being written.
+struct MlpPerturb {
+    uint64_t offset;
+    uint32_t step, probe;
+    float alpha;
+    const uint8_t *bits;
+};
+hipError_t launch_mlp_loss(const float *params, const float *X, const int64_t *labels,
+                           uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out,
+                           double *partial, double *out, const MlpPerturb *pert, Key key,
+                           hipStream_t stream);
+
 }  // namespace zo

@@ -81,3 +81,28 @@ def spsa_step(ctx, theta: torch.Tensor, *, step: int, npert: int, eps: float, et
     c = zo_probe_weights(ctx, Lp, Lm, L0, a, delta, out=b.get("c"))
     zo_update(ctx, theta, offset, step, c, eta, bits)
     return {"L0": L0, "Lp": Lp, "Lm": Lm, "c": c}
+
+
+def spsa_step_fused(ctx, theta: torch.Tensor, *, step: int, npert: int, eps: float, eta: float,
+                    delta: float, loss_at, offset: int = 0, bits=None,
+                    buffers: dict | None = None) -> dict:
+    """One step whose forward applies each probe while reading the parameters.
+
+    loss_at(probe, alpha, row, out) writes the loss at theta + alpha * z_probe (probe None:
+    the clean loss) into `out`; theta itself is only written by the update.  Used with
+    zo_mlp_loss_perturbed: no perturb or restore pass over the parameters at all.
+    """
+    a = applied_eps(eps)
+    b = buffers if buffers is not None else {}
+    dev = theta.device
+    L0 = b.get("L0") if b.get("L0") is not None else torch.empty(1, dtype=torch.float64, device=dev)
+    Lp = b.get("Lp") if b.get("Lp") is not None else torch.empty(npert, dtype=torch.float64, device=dev)
+    Lm = b.get("Lm") if b.get("Lm") is not None else torch.empty(npert, dtype=torch.float64, device=dev)
+    loss_at(None, 0.0, None, L0)
+    for i in range(npert):
+        row = None if bits is None else bits[i]
+        loss_at(i, +a, row, Lp[i:i + 1])
+        loss_at(i, -a, row, Lm[i:i + 1])
+    c = zo_probe_weights(ctx, Lp, Lm, L0, a, delta, out=b.get("c"))
+    zo_update(ctx, theta, offset, step, c, eta, bits)
+    return {"L0": L0, "Lp": Lp, "Lm": Lm, "c": c}

@@ -155,6 +155,40 @@ zo_status zo_reset_nonfinite(zo_ctx *ctx, void *stream);
 zo_status zo_quad_loss(zo_ctx *ctx, const void *d_theta, zo_dtype dtype, const float *d_a,
                        uint64_t n, double *d_out, void *stream);
 
+/* Loss of a two-layer MLP classifier -- the model forward of the ZOO loop ("N forward
+ * passes, loss only" box of the flowchart in "Pretraining Transformers Without Backprop:
+ * What Two Zero-Order Papers Actually Measure") for the small real-model workload:
+ *   loss = mean_b [ logsumexp(z_b) - z_b[label_b] ],  z = GELU(X W1^T + b1) W2^T + b2,
+ * GELU in its exact erf form.  d_params: device fp32, flat W1 [d_hid x d_in] row-major,
+ * b1 [d_hid], W2 [d_out x d_hid] row-major, b2 [d_out], 16-byte aligned.  d_X: device fp32
+ * [batch x d_in] row-major, 16-byte aligned.  d_labels: device int64 [batch], each in
+ * [0, d_out) (an out-of-range label makes the loss NaN).  The GEMM runs on MFMA in fp32;
+ * the partial logits and the cross-entropy are reduced in fp64 in a fixed order
+ * (deterministic).  d_workspace: device, 8-byte aligned, at least
+ * zo_mlp_workspace_bytes(...) bytes, owned by the caller.  d_loss: device, one double.
+ * Limits: batch, d_in, d_hid multiples of 16; 1 <= d_out <= 16.
+ * Errors (ZO_EINVAL): NULL pointers, shapes outside the limits, misalignment, a workspace
+ * that is too small. */
+uint64_t zo_mlp_workspace_bytes(uint32_t batch, uint32_t d_in, uint32_t d_hid,
+                                uint32_t d_out);
+zo_status zo_mlp_loss(zo_ctx *ctx, const float *d_params, const float *d_X,
+                      const int64_t *d_labels, uint32_t batch, uint32_t d_in, uint32_t d_hid,
+                      uint32_t d_out, void *d_workspace, uint64_t workspace_bytes,
+                      double *d_loss, void *stream);
+
+/* The same loss at theta + alpha * z_probe without touching theta: every parameter is
+ * read as theta_j + (+/-alpha) in fp32 -- exactly the value zo_perturb would store -- so the
+ * result equals zo_perturb followed by zo_mlp_loss, bit for bit, and a step's 2*n_pert
+ * perturbed losses need no pass over the parameters.  offset: global index of
+ * d_params[0] (multiple of 128); d_bits: NULL (regenerate) or the probe's packed row over
+ * the parameters.  Other arguments and errors as zo_mlp_loss. */
+zo_status zo_mlp_loss_perturbed(zo_ctx *ctx, const float *d_params, uint64_t offset,
+                                uint32_t step, uint32_t probe, float alpha,
+                                const uint8_t *d_bits, const float *d_X,
+                                const int64_t *d_labels, uint32_t batch, uint32_t d_in,
+                                uint32_t d_hid, uint32_t d_out, void *d_workspace,
+                                uint64_t workspace_bytes, double *d_loss, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

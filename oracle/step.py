@@ -16,6 +16,9 @@ Measure"):
 
 The eps handed to the weights is the fp32 value that the passes actually added.
 
+schedule="none" runs no passes at all (the losses must be given): the step of a forward
+that applies the probe on the fly while reading the parameters, leaving them untouched.
+
 schedule="S2f" visits the same perturbed points with two passes per probe instead of
 four: +eps z_0; then for each i a pass of -2 eps z_i (to theta - eps z_i) and a fused pass
 that restores probe i and applies +eps z_(i+1) (the last one only restores).
@@ -68,6 +71,9 @@ def spsa_step(theta: np.ndarray, *, seed: int, step: int, npert: int, eps: float
                 perturb2(theta, offset, seed, step, i, +a, i + 1, +a, row(i), row(i + 1))
             else:
                 perturb(theta, offset, seed, step, i, +a, row(i))
+    elif schedule == "none":
+        if losses is None:
+            raise ValueError("schedule 'none' needs the losses")
     else:
         raise ValueError(schedule)
     c, bad = probe_weights(Lp, Lm, L0, a, delta)

@@ -62,3 +62,25 @@ def assert_same_bits_or_nan(got: np.ndarray, ref: np.ndarray, kind: str):
         nan = np.isnan(bf16_values(got)) & np.isnan(bf16_values(ref))
     diff = (gv != rv) & ~nan
     assert not diff.any(), f"{diff.sum()} elements differ; first at {np.argmax(diff)}"
+
+
+def weight_bound(Lp, Lm, L0, dL, eps, delta, c):
+    """Largest |c_gpu - c_oracle| the loss differences |dL| (per loss, a bound) can cause.
+
+    c = g / max(|h|, delta), g = (L+ - L-)/(2 eps), h = (L+ + L- - 2 L0)/eps^2.  With every
+    loss off by at most dL: |dg| <= dL / eps, |dh| <= 4 dL / eps^2, and
+    c' - c = dg / (d + dd) - g dd / (d (d + dd)) with d = max(|h|, delta) and |dd| <= |dh|
+    (the max is 1-Lipschitz), so |dc| <= (|dg| + |g| |dh| / d) / (d - |dh|), plus one fp32
+    rounding of c on each side.  Returns inf where d <= 2 |dh|.
+    """
+    Lp, Lm = np.asarray(Lp, np.float64), np.asarray(Lm, np.float64)
+    g = (Lp - Lm) / (2 * eps)
+    h = (Lp + Lm - 2 * L0) / eps ** 2
+    dg = dL / eps
+    dh = 4 * dL / eps ** 2
+    d = np.maximum(np.abs(h), delta)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        b = (dg + np.abs(g) * dh / d) / (d - dh)
+    b = np.where(d > 2 * dh, b, np.inf)
+    ulp = np.spacing(np.abs(np.asarray(c, np.float32))).astype(np.float64)
+    return b + 2 * ulp

@@ -1,0 +1,159 @@
+"""The MLP loss on MFMA and its perturbation-fused variant, against the fp64 oracle.
+
+Tolerance for the loss: 1e-5 relative.  The GEMM accumulates K = d_in fp32 products per
+hidden unit (typical error ~ sqrt(K) * 2^-24 * |h|, ~1e-6 relative at K = 768) and the
+loss averages ~batch * d_hid such terms, so the observed error is far below this; a
+dropped bias, a wrong activation or a transposed operand moves the loss by >= 1e-3.
+The fused variant is held to bit-equality with perturb-in-place-then-forward.
+"""
+import numpy as np
+import pytest
+import torch
+
+import forward_only_amd as zo
+import oracle
+from forward_only_amd.step import spsa_step_fused
+from gpu_util import to_dev_f32, weight_bound
+from workloads import CONFIGS, gen
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(16, 16, 16, 2), (32, 48, 64, 3), (48, 32, 128, 16), (128, 768, 3072, 2)]
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    c = zo.zo_init(11)
+    yield c
+    c.close()
+
+
+def _problem(batch, d_in, d_hid, d_out, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    M = d_hid * d_in + d_hid + d_out * d_hid + d_out
+    theta = (rng.standard_normal(M) * 0.02).astype(np.float32)
+    X = rng.standard_normal((batch, d_in)).astype(np.float32)
+    y = rng.integers(0, d_out, batch).astype(np.int64)
+    return theta, X, y
+
+
+def _dev(theta, X, y):
+    return to_dev_f32(theta), to_dev_f32(X), torch.from_numpy(y).cuda()
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_mlp_loss_matches_oracle(ctx, shape):
+    batch, d_in, d_hid, d_out = shape
+    theta, X, y = _problem(*shape, seed=sum(shape))
+    t, x, yl = _dev(theta, X, y)
+    got = zo.zo_mlp_loss(ctx, t, x, yl, d_hid, d_out).item()
+    ref = oracle.mlp_loss(theta, X, y, d_hid, d_out)
+    assert abs(got - ref) <= 1e-5 * abs(ref), (got, ref)
+    again = zo.zo_mlp_loss(ctx, t, x, yl, d_hid, d_out).item()
+    assert again == got                                   # deterministic
+
+
+def test_mlp_config_loss(ctx):
+    cfg = CONFIGS["mlp"]
+    e = cfg.extra
+    theta, _ = gen.theta_and_a(cfg)
+    X, y = gen.mlp_data(cfg)
+    got = zo.zo_mlp_loss(ctx, to_dev_f32(theta), to_dev_f32(X), torch.from_numpy(y).cuda(),
+                         e["d_hid"], e["d_out"]).item()
+    ref = oracle.mlp_loss(theta, X, y, e["d_hid"], e["d_out"])
+    assert abs(got - ref) <= 1e-5 * abs(ref), (got, ref)
+
+
+@pytest.mark.parametrize("shape", [(16, 16, 16, 2), (32, 48, 64, 3), (128, 768, 3072, 2)])
+@pytest.mark.parametrize("mode", ["regen", "bits"])
+def test_fused_perturbation_equals_perturb_then_forward(ctx, shape, mode):
+    batch, d_in, d_hid, d_out = shape
+    theta, X, y = _problem(*shape, seed=7 + sum(shape))
+    t, x, yl = _dev(theta, X, y)
+    M = theta.size
+    for probe, alpha in ((0, 1e-3), (3, -1e-3), (5, 2.0 ** -7)):
+        bits = zo.zo_gen_probes(ctx, 2, probe, 1, 0, M)[0] if mode == "bits" else None
+        fused = zo.zo_mlp_loss_perturbed(ctx, t, 0, 2, probe, alpha, x, yl, d_hid, d_out,
+                                         bits=bits).item()
+        moved = t.clone()
+        zo.zo_perturb(ctx, moved, 0, 2, probe, alpha, bits)
+        direct = zo.zo_mlp_loss(ctx, moved, x, yl, d_hid, d_out).item()
+        assert fused == direct, (probe, alpha, fused, direct)
+        # and the oracle at the perturbed point
+        h = theta.copy()
+        oracle.perturb(h, 0, 11, 2, probe, alpha)
+        ref = oracle.mlp_loss(h, X, y, d_hid, d_out)
+        assert abs(fused - ref) <= 1e-5 * abs(ref)
+    assert np.array_equal(t.cpu().numpy(), theta)          # parameters untouched
+
+
+def test_mlp_argument_checks(ctx):
+    theta8, X8, y8 = _problem(16, 8, 16, 2, seed=2)
+    with pytest.raises(zo.ZOError) as e:
+        zo.zo_mlp_loss(ctx, *_dev(theta8, X8, y8), 16, 2)              # d_in not a multiple of 16
+    assert e.value.status == zo.ZO_EINVAL
+    theta17, X17, y17 = _problem(16, 16, 16, 17, seed=3)
+    with pytest.raises(zo.ZOError):
+        zo.zo_mlp_loss(ctx, *_dev(theta17, X17, y17), 16, 17)          # more than 16 classes
+    theta, X, y = _problem(16, 16, 16, 2, seed=1)
+    t, x, yl = _dev(theta, X, y)
+    ws = torch.empty(8, dtype=torch.uint8, device="cuda")
+    with pytest.raises(zo.ZOError):
+        zo.zo_mlp_loss(ctx, t, x, yl, 16, 2, workspace=ws)             # workspace too small
+
+
+@pytest.mark.parametrize("mode", ["bits", "regen"])
+def test_mlp_config_fused_step(ctx, mode):
+    """One step of the MLP workload with the fused forward, each side on its own from the
+    seeded parameters (n_pert cut to 16 to bound the oracle's time): the oracle evaluates
+    L(theta +/- eps z_i) by its own perturb and fp64 forward.  Losses agree within the loss
+    tolerance; since the weight arithmetic is identical on both sides, the weights must lie
+    within the bound implied by the measured loss differences; theta within the update
+    tolerance plus eta * sum of those bounds; the GPU's parameters are untouched by the
+    16 x 2 perturbed forwards (only the update moves them)."""
+    cfg = CONFIGS["mlp"]
+    e = cfg.extra
+    npert, step = 16, 0
+    local = zo.zo_init(cfg.seed)
+    theta, _ = gen.theta_and_a(cfg)
+    X, y = gen.mlp_data(cfg)
+    t, x, yl = to_dev_f32(theta), to_dev_f32(X), torch.from_numpy(y).cuda()
+    ws = torch.empty(zo.zo_mlp_workspace_bytes(e["batch"], e["d_in"], e["d_hid"], e["d_out"]),
+                     dtype=torch.uint8, device="cuda")
+
+    def loss_at(probe, alpha, row, out):
+        if probe is None:
+            zo.zo_mlp_loss(local, t, x, yl, e["d_hid"], e["d_out"], workspace=ws, out=out)
+        else:
+            zo.zo_mlp_loss_perturbed(local, t, 0, step, probe, alpha, x, yl, e["d_hid"],
+                                     e["d_out"], bits=row, workspace=ws, out=out)
+
+    bits = zo.zo_gen_probes(local, step, 0, npert, 0, cfg.M) if mode == "bits" else None
+    out = spsa_step_fused(local, t, step=step, npert=npert, eps=cfg.eps, eta=cfg.eta,
+                          delta=cfg.delta, loss_at=loss_at, bits=bits)
+    a = float(np.float32(cfg.eps))
+    lossf = lambda p: oracle.mlp_loss(p, X, y, e["d_hid"], e["d_out"])  # noqa: E731
+    L0 = lossf(theta)
+    Lp, Lm = np.zeros(npert), np.zeros(npert)
+    for i in range(npert):
+        for sgn, dst in ((+1, Lp), (-1, Lm)):
+            p = theta.copy()
+            oracle.perturb(p, 0, cfg.seed, step, i, sgn * a)
+            dst[i] = lossf(p)
+    h = theta.copy()
+    res = oracle.spsa_step(h, seed=cfg.seed, step=step, npert=npert, eps=cfg.eps, eta=cfg.eta,
+                           delta=cfg.delta, losses=(L0, Lp, Lm), schedule="none")
+    gL0, gLp, gLm = out["L0"].item(), out["Lp"].cpu().numpy(), out["Lm"].cpu().numpy()
+    dL = max(abs(gL0 - L0), np.max(np.abs(gLp - Lp)), np.max(np.abs(gLm - Lm)))
+    assert dL <= 1e-5 * L0, dL
+    bound = weight_bound(Lp, Lm, L0, dL * (1 + 1e-12), a, cfg.delta, res["c"])
+    c = out["c"].cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(c - res["c"]) <= bound), (c, res["c"], bound)
+    finite = np.isfinite(bound).all()
+    if finite:
+        got = t.cpu().numpy()
+        scale = np.maximum(np.abs(h.astype(np.float64)),
+                           float(np.float32(cfg.eta)) * float(np.sum(np.abs(res["c"]))))
+        extra = float(np.float32(cfg.eta)) * float(np.sum(bound))
+        assert np.all(np.abs(got.astype(np.float64) - h) <= 1e-5 * scale + extra)
+    local.close()

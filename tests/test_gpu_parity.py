@@ -12,7 +12,7 @@ import forward_only_amd as zo
 import oracle
 from forward_only_amd.step import spsa_step
 from gpu_util import (assert_bf16_within_ulp, assert_f32_update_close, assert_same_bits_or_nan,
-                      bf16_bits, to_dev_bf16, to_dev_f32)
+                      bf16_bits, to_dev_bf16, to_dev_f32, weight_bound)
 from workloads import CONFIGS, gen
 
 pytestmark = pytest.mark.gpu
@@ -81,7 +81,7 @@ def test_perturb_bit_exact(ctx, kind, n, offset, mode):
     h = _theta(kind, n, seed=n + offset, scale=1.0 if kind == "f32" else 0.02, specials=True)
     t = _dev(kind, h)
     bits_h = oracle.gen_plane(SEED, step, probe, offset, n) if mode == "bits" else None
-    bits_d = torch.from_numpy(bits_h).cuda() if mode == "bits" else None
+    bits_d = zo.zo_gen_probes(ctx, step, probe, 1, offset, n)[0] if mode == "bits" else None
     for a in (alpha, -alpha, -3.0 * alpha):
         zo.zo_perturb(ctx, t, offset, step, probe, a, bits_d)
         oracle.perturb(h, offset, SEED, step, probe, a, bits_h)
@@ -182,7 +182,7 @@ def test_update_parity(ctx, kind, n, offset, npert, mode):
     eta = 1.0 if kind == "bf16" else 1e-2      # large enough that bf16 updates do move
     t = _dev(kind, h)
     bits_h = oracle.gen_planes(SEED, step, 0, npert, offset, n) if mode == "bits" else None
-    bits_d = torch.from_numpy(bits_h).cuda() if mode == "bits" else None
+    bits_d = zo.zo_gen_probes(ctx, step, 0, npert, offset, n) if mode == "bits" else None
     zo.zo_update(ctx, t, offset, step, to_dev_f32(c), eta, bits_d)
     oracle.update(h, offset, SEED, step, c, eta, bits_h)
     got = _host(kind, t)
@@ -303,34 +303,59 @@ def test_argument_checks(ctx):
 # ------------------------------------------------------------------------------------
 # whole steps
 # ------------------------------------------------------------------------------------
+def _quad_loss_error_bound(theta, a):
+    """Bound on |L_gpu - L_oracle| for the fp64 quadratic loss: both sides sum M products
+    of size <= max(a theta^2) in fp64, each with at most M roundings (Higham's bound for
+    recursive summation, doubled for the two sides), plus the products' own roundings."""
+    t = theta.astype(np.float64) if theta.dtype == np.float32 else oracle.bf16_to_f32(theta).astype(np.float64)
+    terms = 0.5 * a.astype(np.float64) * t * t
+    M = t.size
+    return 2 * (M + 3) * 2.0 ** -53 * np.sum(np.abs(terms)) * 1.01
+
+
+@pytest.mark.parametrize("schedule", ["S4", "S2f"])
 @pytest.mark.parametrize("mode", ["regen", "bits"])
-def test_tiny_config_ten_steps(ctx, mode):
-    """The tiny quadratic workload end to end: per step, the oracle is fed the GPU's losses
-    (so the weights must be bit-identical) and the GPU's theta must stay within the update
-    tolerance of the oracle's; the loss must go down."""
+def test_tiny_config_steps_from_seeded_theta(ctx, schedule, mode):
+    """The tiny quadratic workload end to end, each side on its own: from the seeded theta,
+    the GPU step (GPU losses) and the oracle step (oracle losses) for steps 0..9 (different
+    probes each): the losses agree to the fp64 summation bound, the weights within the
+    bound those loss differences imply, and theta within the update tolerance plus
+    eta * sum |dc|."""
     cfg = CONFIGS["tiny"]
     local = zo.zo_init(cfg.seed)
     th0, a = gen.theta_and_a(cfg)
-    t = to_dev_f32(th0)
     ad = to_dev_f32(a)
-    h = th0.copy()
+    dL = _quad_loss_error_bound(th0, a) * 1.1
     lossf = lambda x, o: zo.zo_quad_loss(local, x, ad, out=o)  # noqa: E731
-    first = oracle.quad_loss(h, a)
     for step in range(cfg.steps):
+        t = to_dev_f32(th0)
+        h = th0.copy()
+        bits_d = zo.zo_gen_probes(local, step, 0, cfg.npert, 0, cfg.M) if mode == "bits" else None
         bits_h = oracle.gen_planes(cfg.seed, step, 0, cfg.npert, 0, cfg.M) if mode == "bits" else None
-        bits_d = torch.from_numpy(bits_h).cuda() if mode == "bits" else None
         out = spsa_step(local, t, step=step, npert=cfg.npert, eps=cfg.eps, eta=cfg.eta,
-                        delta=cfg.delta, loss=lossf, bits=bits_d)
-        L0, Lp, Lm = out["L0"].item(), out["Lp"].cpu().numpy(), out["Lm"].cpu().numpy()
-        # the GPU losses agree with the oracle's loss of the same parameters
-        assert abs(L0 - oracle.quad_loss(h, a)) <= 1e-13 * abs(L0)
+                        delta=cfg.delta, loss=lossf, bits=bits_d, schedule=schedule)
         res = oracle.spsa_step(h, seed=cfg.seed, step=step, npert=cfg.npert, eps=cfg.eps,
-                               eta=cfg.eta, delta=cfg.delta, losses=(L0, Lp, Lm), bits=bits_h)
-        assert np.array_equal(out["c"].cpu().numpy(), res["c"])
+                               eta=cfg.eta, delta=cfg.delta, loss_fn=lambda x: oracle.quad_loss(x, a),
+                               bits=bits_h, schedule=schedule)
+        L0, Lp, Lm = out["L0"].item(), out["Lp"].cpu().numpy(), out["Lm"].cpu().numpy()
+        assert abs(L0 - res["L0"]) <= dL
+        assert np.all(np.abs(Lp - res["Lp"]) <= dL) and np.all(np.abs(Lm - res["Lm"]) <= dL)
+        c = out["c"].cpu().numpy()
+        eps = float(np.float32(cfg.eps))
+        bound = weight_bound(res["Lp"], res["Lm"], res["L0"], dL, eps, cfg.delta, res["c"])
+        assert np.all(np.abs(c.astype(np.float64) - res["c"]) <= bound)
         got = t.cpu().numpy()
-        assert_f32_update_close(got, h, cfg.eta, res["c"])
-        h = got.copy()     # continue from the GPU's state (teacher forcing)
-    assert oracle.quad_loss(h, a) < first
+        extra = float(np.float32(cfg.eta)) * float(np.sum(bound))
+        scale = np.maximum(np.abs(h.astype(np.float64)),
+                           float(np.float32(cfg.eta)) * float(np.sum(np.abs(res["c"]))))
+        assert np.all(np.abs(got.astype(np.float64) - h) <= 1e-5 * scale + extra)
+    # GPU alone along a 10-step trajectory: the loss goes down
+    t = to_dev_f32(th0)
+    first = zo.zo_quad_loss(local, t, ad).item()
+    for step in range(cfg.steps):
+        spsa_step(local, t, step=step, npert=cfg.npert, eps=cfg.eps, eta=cfg.eta,
+                  delta=cfg.delta, loss=lossf, schedule=schedule)
+    assert zo.zo_quad_loss(local, t, ad).item() < first
     local.close()
 
 
@@ -364,7 +389,7 @@ def test_perturb2_bit_exact(ctx, kind, n, offset, mode):
     t = _dev(kind, h)
     if mode == "bits":
         ra, rb = (oracle.gen_plane(SEED, step, p, offset, n) for p in (pa, pb))
-        da, db = torch.from_numpy(ra).cuda(), torch.from_numpy(rb).cuda()
+        da, db = (zo.zo_gen_probes(ctx, step, p, 1, offset, n)[0] for p in (pa, pb))
     else:
         ra = rb = da = db = None
     for aa, ab in ((1e-3, 1e-3), (-2e-3, 1e-3), (1e-3, -3e-3), (2.0 ** -10, 0.0)):
@@ -382,33 +407,6 @@ def test_perturb2_requires_both_rows(ctx):
     st = _lib.lib().zo_perturb2(ctx.handle, t.data_ptr(), 0, 0, 256, 0, 0, 1.0, 1, 1.0,
                                 row.data_ptr(), None, None)
     assert st == zo.ZO_EINVAL
-
-
-@pytest.mark.parametrize("mode", ["regen", "bits"])
-def test_tiny_config_two_pass_schedule(ctx, mode):
-    """The tiny workload with the two-pass schedule: weights bit-identical to the oracle fed
-    the GPU's losses, theta within the update tolerance, loss going down."""
-    cfg = CONFIGS["tiny"]
-    local = zo.zo_init(cfg.seed)
-    th0, a = gen.theta_and_a(cfg)
-    t, ad, h = to_dev_f32(th0), to_dev_f32(a), th0.copy()
-    lossf = lambda x, o: zo.zo_quad_loss(local, x, ad, out=o)  # noqa: E731
-    first = oracle.quad_loss(h, a)
-    for step in range(cfg.steps):
-        bits_h = oracle.gen_planes(cfg.seed, step, 0, cfg.npert, 0, cfg.M) if mode == "bits" else None
-        bits_d = torch.from_numpy(bits_h).cuda() if mode == "bits" else None
-        out = spsa_step(local, t, step=step, npert=cfg.npert, eps=cfg.eps, eta=cfg.eta,
-                        delta=cfg.delta, loss=lossf, bits=bits_d, schedule="S2f")
-        L0, Lp, Lm = out["L0"].item(), out["Lp"].cpu().numpy(), out["Lm"].cpu().numpy()
-        res = oracle.spsa_step(h, seed=cfg.seed, step=step, npert=cfg.npert, eps=cfg.eps,
-                               eta=cfg.eta, delta=cfg.delta, losses=(L0, Lp, Lm), bits=bits_h,
-                               schedule="S2f")
-        assert np.array_equal(out["c"].cpu().numpy(), res["c"])
-        got = t.cpu().numpy()
-        assert_f32_update_close(got, h, cfg.eta, res["c"])
-        h = got.copy()
-    assert oracle.quad_loss(h, a) < first
-    local.close()
 
 
 def test_bf16_synthetic_two_pass_step_small(ctx):
