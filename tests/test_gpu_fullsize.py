@@ -1,0 +1,89 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark times.
+
+The whole parameter buffer goes through the same calls the benchmark makes (zo_perturb,
+zo_perturb2, zo_update on the full buffer, probes regenerated); sampled windows (random
+ones, the first, the one holding the ragged tail and the last) are copied to the host
+before and after and recomputed by the oracle from their global offsets -- the probe bits
+are counter-based, so a window is an exact sub-problem.  Passes are compared bit for bit,
+the update within the update tolerance (fp32) or one bf16 ulp.
+"""
+import numpy as np
+import pytest
+import torch
+
+import forward_only_amd as zo
+import oracle
+from gpu_util import assert_bf16_within_ulp, assert_f32_update_close, bf16_bits
+from workloads import CONFIGS, gen
+
+pytestmark = pytest.mark.gpu
+
+WIN = 8192
+
+
+def _windows(M, k, seed):
+    rng = np.random.default_rng(seed)
+    nblk = M // 128
+    starts = set((rng.integers(1, nblk - WIN // 128 - 1, k) * 128).tolist())
+    starts |= {0, (M // 8192) * 8192 - 4096, ((M - 1) // 128) * 128 - WIN + 128}
+    return sorted(s for s in starts if 0 <= s < M)
+
+
+def _take(t, starts, kind):
+    out = []
+    for s in starts:
+        w = t[s:s + WIN]
+        out.append(w.cpu().numpy().copy() if kind == "f32" else bf16_bits(w).copy())
+    return out
+
+
+def _run_and_check(t, M, kind, seed, npert, eps, eta, label):
+    starts = _windows(M, 24, seed=M % 1000)
+    before = _take(t, starts, kind)
+    ctx = zo.zo_init(seed)
+    a = float(np.float32(eps))
+    c = (np.random.default_rng(7).standard_normal(npert) * 2.5e-3).astype(np.float32)
+    print(f"[fullsize] {label}: M={M} passes", flush=True)
+    zo.zo_perturb(ctx, t, 0, 1, 0, +a)
+    zo.zo_perturb(ctx, t, 0, 1, 0, -2.0 * a)
+    zo.zo_perturb2(ctx, t, 0, 1, 0, +a, 1, +a)
+    torch.cuda.synchronize()
+    after_passes = _take(t, starts, kind)
+    print(f"[fullsize] {label}: update n_pert={npert}", flush=True)
+    zo.zo_update(ctx, t, 0, 1, torch.from_numpy(c).cuda(), eta)
+    torch.cuda.synchronize()
+    after_update = _take(t, starts, kind)
+    ctx.close()
+    for s, h0, hp, hu in zip(starts, before, after_passes, after_update):
+        h = h0.copy()
+        oracle.perturb(h, s, seed, 1, 0, +a)
+        oracle.perturb(h, s, seed, 1, 0, -2.0 * a)
+        oracle.perturb2(h, s, seed, 1, 0, +a, 1, +a)
+        assert np.array_equal(h.view(np.uint32 if kind == "f32" else np.uint16),
+                              hp.view(np.uint32 if kind == "f32" else np.uint16)), (label, s)
+        oracle.update(h, s, seed, 1, c, eta)
+        if kind == "f32":
+            assert_f32_update_close(hu, h, eta, c)
+        else:
+            assert_bf16_within_ulp(hu, h)
+    return len(starts)
+
+
+def test_flat125m_full_size():
+    cfg = CONFIGS["flat125m"]
+    th0, _ = gen.theta_and_a(cfg)
+    t = torch.from_numpy(th0).cuda()
+    del th0
+    n = _run_and_check(t, cfg.M, "f32", cfg.seed, cfg.npert, cfg.eps, cfg.eta, "flat125m")
+    assert n >= 20
+
+
+@pytest.mark.parametrize("name", ["opt13b", "opt30b"])
+def test_opt_shaped_bf16_full_size(name):
+    cfg = CONFIGS[name]
+    t = torch.empty(cfg.M, dtype=torch.bfloat16, device="cuda")
+    gen.device_normal_(t, cfg.theta_std, cfg.seed)
+    n = _run_and_check(t, cfg.M, "bf16", cfg.seed, cfg.npert, cfg.eps, 1.0, name)
+    assert n >= 20
+    del t
+    torch.cuda.empty_cache()
