@@ -20,11 +20,12 @@ import torch
 
 from . import _lib
 from ._lib import (ZO_BF16, ZO_EHIP, ZO_EINVAL, ZO_ENOMEM, ZO_EUNSUPPORTED, ZO_FP32,  # noqa: F401
-                   ZO_MAX_NPERT, ZO_OK, ZOError)
+                   ZO_MAX_NPERT, ZO_OK, ZO_WEIGHTS_POWER, ZO_WEIGHTS_PRECOND,
+                   ZO_WEIGHTS_SPSA_MEAN, ZOError)
 
 __all__ = [
     "Context", "ZOError", "zo_init", "zo_destroy", "zo_bits_stride", "zo_gen_probes",
-    "zo_perturb", "zo_perturb2", "zo_probe_weights", "zo_update", "zo_nonfinite_count",
+    "zo_perturb", "zo_perturb2", "zo_probe_weights", "zo_probe_weights_ex", "zo_update", "zo_nonfinite_count",
     "zo_reset_nonfinite", "zo_quad_loss", "zo_mlp_workspace_bytes", "zo_mlp_loss",
     "zo_mlp_loss_perturbed", "library_path",
 ]
@@ -156,6 +157,24 @@ def zo_probe_weights(ctx: Context, Lp: torch.Tensor, Lm: torch.Tensor, L0: torch
         ctx.handle, _dev(Lp, "Lp", torch.float64), _dev(Lm, "Lm", torch.float64),
         _dev(L0, "L0", torch.float64), n, float(eps), float(delta),
         _dev(out, "out", torch.float32), _stream(stream)), "zo_probe_weights")
+    return out
+
+
+def zo_probe_weights_ex(ctx: Context, Lp: torch.Tensor, Lm: torch.Tensor,
+                        L0: torch.Tensor | None, eps: float, delta: float, mode: int,
+                        power: float = 1.0, out: torch.Tensor | None = None,
+                        stream=None) -> torch.Tensor:
+    """Weights in one of the pages' forms (ZO_WEIGHTS_PRECOND / _POWER / _SPSA_MEAN)."""
+    n = Lp.numel()
+    if Lm.numel() != n:
+        raise ValueError("Lp and Lm must have the same length")
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device="cuda")
+    p0 = None if L0 is None else _dev(L0, "L0", torch.float64)
+    _lib.check(_lib.lib().zo_probe_weights_ex(
+        ctx.handle, _dev(Lp, "Lp", torch.float64), _dev(Lm, "Lm", torch.float64), p0, n,
+        float(eps), float(delta), int(mode), float(power), _dev(out, "out", torch.float32),
+        _stream(stream)), "zo_probe_weights_ex")
     return out
 
 

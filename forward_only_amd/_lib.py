@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(HERE, "libzo.so")
 
 ZO_OK, ZO_EINVAL, ZO_EHIP, ZO_ENOMEM, ZO_EUNSUPPORTED = 0, 1, 2, 3, 4
 ZO_FP32, ZO_BF16 = 0, 1
+ZO_WEIGHTS_PRECOND, ZO_WEIGHTS_POWER, ZO_WEIGHTS_SPSA_MEAN = 0, 1, 2
 ZO_MAX_NPERT = 512
 
 _vp = ctypes.c_void_p
@@ -33,6 +34,7 @@ SIGNATURES = {
     "zo_perturb2": (_int, [_vp, _vp, _int, _u64, _u64, _u32, _u32, _f32, _u32, _f32, _vp, _vp,
                            _vp]),
     "zo_probe_weights": (_int, [_vp, _vp, _vp, _vp, _u32, _f64, _f64, _vp, _vp]),
+    "zo_probe_weights_ex": (_int, [_vp, _vp, _vp, _vp, _u32, _f64, _f64, _int, _f64, _vp, _vp]),
     "zo_update": (_int, [_vp, _vp, _int, _u64, _u64, _u32, _vp, _u32, _f32, _vp, _vp]),
     "zo_nonfinite_count": (_int, [_vp, _vp, ctypes.POINTER(_u32)]),
     "zo_reset_nonfinite": (_int, [_vp, _vp]),

@@ -149,8 +149,25 @@ zo_status zo_probe_weights(zo_ctx *c, const double *d_Lp, const double *d_Lm,
     if (!(delta >= 0.0) || delta - delta != 0.0) return ZO_EINVAL;               // <0/NaN/inf
     if (n_pert == 0) return ZO_OK;
     if (!d_Lp || !d_Lm || !d_L0 || !d_c) return ZO_EINVAL;
-    return from_hip(zo::launch_probe_weights(d_Lp, d_Lm, d_L0, n_pert, eps, delta, d_c,
+    return from_hip(zo::launch_probe_weights(d_Lp, d_Lm, d_L0, n_pert, eps, delta, 0, 1.0, d_c,
                                              c->d_counter, as_stream(stream)));
+}
+
+zo_status zo_probe_weights_ex(zo_ctx *c, const double *d_Lp, const double *d_Lm,
+                              const double *d_L0, uint32_t n_pert, double eps, double delta,
+                              zo_weights_mode mode, double power, float *d_c, void *stream)
+{
+    if (!c) return ZO_EINVAL;
+    if (mode != ZO_WEIGHTS_PRECOND && mode != ZO_WEIGHTS_POWER && mode != ZO_WEIGHTS_SPSA_MEAN)
+        return ZO_EINVAL;
+    if (!(eps == eps) || eps == 0.0 || eps - eps != 0.0) return ZO_EINVAL;
+    if (mode != ZO_WEIGHTS_SPSA_MEAN && (!(delta >= 0.0) || delta - delta != 0.0))
+        return ZO_EINVAL;
+    if (mode == ZO_WEIGHTS_POWER && (!(power >= 0.0) || power - power != 0.0)) return ZO_EINVAL;
+    if (n_pert == 0) return ZO_OK;
+    if (!d_Lp || !d_Lm || !d_c || (mode != ZO_WEIGHTS_SPSA_MEAN && !d_L0)) return ZO_EINVAL;
+    return from_hip(zo::launch_probe_weights(d_Lp, d_Lm, d_L0, n_pert, eps, delta, (int)mode,
+                                             power, d_c, c->d_counter, as_stream(stream)));
 }
 
 zo_status zo_update(zo_ctx *c, void *d_theta, zo_dtype dtype, uint64_t offset, uint64_t n,

@@ -12,38 +12,50 @@ namespace zo {
 // Division, add and multiply are the IEEE double operations (no contraction in this
 // file), then one round-to-nearest-even to fp32.  A non-finite loss drops the probe
 // (c = 0) and bumps the device counter.
+// The other weight forms of the pages share the kernel (mode): 1 divides by
+// max(|h|, delta)^power (the curvature-power weight of "Probe-Space Preconditioning", whose
+// exponent the page gives as 0.1), 2 is the plain 1SPSA mean g / n_pert of "How 1.5-SPSA
+// Works" (no clean pass; L0 is not read).
 __global__ __launch_bounds__(256) void k_probe_weights(const double *__restrict__ Lp,
                                                        const double *__restrict__ Lm,
                                                        const double *__restrict__ L0p,
                                                        uint32_t npert, double eps, double delta,
+                                                       int mode, double power,
                                                        float *__restrict__ c,
                                                        uint32_t *__restrict__ counter)
 {
-    const double L0 = *L0p;
+    const bool uses_l0 = mode != 2;
+    const double L0 = uses_l0 ? *L0p : 0.0;
     for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < npert;
          i += gridDim.x * blockDim.x) {
         const double lp = Lp[i], lm = Lm[i];
-        if (!__builtin_isfinite(lp) || !__builtin_isfinite(lm) || !__builtin_isfinite(L0)) {
+        if (!__builtin_isfinite(lp) || !__builtin_isfinite(lm) ||
+            (uses_l0 && !__builtin_isfinite(L0))) {
             c[i] = 0.0f;
             atomicAdd(counter, 1u);
             continue;
         }
         const double g = (lp - lm) / (2.0 * eps);
+        if (mode == 2) {
+            c[i] = (float)(g / (double)npert);
+            continue;
+        }
         const double h = ((lp + lm) - 2.0 * L0) / (eps * eps);
         const double ah = __builtin_fabs(h);
-        const double den = ah > delta ? ah : delta;
+        double den = ah > delta ? ah : delta;
+        if (mode == 1) den = pow(den, power);
         c[i] = (float)(g / den);
     }
 }
 
 hipError_t launch_probe_weights(const double *Lp, const double *Lm, const double *L0,
-                                uint32_t npert, double eps, double delta, float *c,
-                                uint32_t *counter, hipStream_t stream)
+                                uint32_t npert, double eps, double delta, int mode,
+                                double power, float *c, uint32_t *counter, hipStream_t stream)
 {
     const uint32_t grid = (npert + 255u) / 256u;
     const uint32_t g = grid < 64u ? grid : 64u;
     hipLaunchKernelGGL(k_probe_weights, dim3(g), dim3(256), 0, stream, Lp, Lm, L0, npert, eps,
-                       delta, c, counter);
+                       delta, mode, power, c, counter);
     return hipGetLastError();
 }
 

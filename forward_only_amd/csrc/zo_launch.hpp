@@ -29,9 +29,10 @@ hipError_t launch_perturb2(void *theta, bool bf16, uint64_t offset, uint64_t n, 
                            int num_cus, hipStream_t stream);
 
 // c[i] from (L+, L-, L0) in fp64; non-finite probes counted into *counter.
+// mode 0: g / max(|h|, delta); 1: g / max(|h|, delta)^power; 2: g / npert (L0 unused).
 hipError_t launch_probe_weights(const double *Lp, const double *Lm, const double *L0,
-                                uint32_t npert, double eps, double delta, float *c,
-                                uint32_t *counter, hipStream_t stream);
+                                uint32_t npert, double eps, double delta, int mode,
+                                double power, float *c, uint32_t *counter, hipStream_t stream);
 
 // theta[0..n) -= eta * sum_i c_i z_i through per-8-probe LDS tables.
 hipError_t launch_update(void *theta, bool bf16, uint64_t offset, uint64_t n, Key key,

@@ -123,6 +123,26 @@ zo_status zo_probe_weights(zo_ctx *ctx, const double *d_Lp, const double *d_Lm,
                            const double *d_L0, uint32_t n_pert, double eps, double delta,
                            float *d_c, void *stream);
 
+/* Weight forms for zo_probe_weights_ex. */
+typedef enum {
+    ZO_WEIGHTS_PRECOND = 0,   /* c_i = g_i / max(|h_i|, delta)        (zo_probe_weights) */
+    ZO_WEIGHTS_POWER = 1,     /* c_i = g_i / max(|h_i|, delta)^power                      */
+    ZO_WEIGHTS_SPSA_MEAN = 2  /* c_i = g_i / n_pert, no clean loss                        */
+} zo_weights_mode;
+
+/* The other probe-weight forms of the pages, in fp64 with one rounding to fp32:
+ * ZO_WEIGHTS_POWER is the curvature-power weighting of "Probe-Space Preconditioning" (a
+ * weight |curvature|^alpha from the clean and perturbed losses that shrinks high-curvature
+ * probes; the page's alpha is 0.1; power = 1 is ZO_WEIGHTS_PRECOND, 0 the plain central
+ * difference).  ZO_WEIGHTS_SPSA_MEAN is the plain 1SPSA estimator of "How 1.5-SPSA Works"
+ * averaged over the probes (no clean pass; d_L0 is not read and may be NULL).  Non-finite
+ * losses that a mode reads drop the probe (c_i = 0, counter + 1) as in zo_probe_weights.
+ * Errors (ZO_EINVAL): as zo_probe_weights, an unknown mode, or power negative or not finite
+ * (ZO_WEIGHTS_POWER).  delta is not read by ZO_WEIGHTS_SPSA_MEAN. */
+zo_status zo_probe_weights_ex(zo_ctx *ctx, const double *d_Lp, const double *d_Lm,
+                              const double *d_L0, uint32_t n_pert, double eps, double delta,
+                              zo_weights_mode mode, double power, float *d_c, void *stream);
+
 /* Multi-probe update theta_j <- round(theta_j - eta * s_j), s_j = sum_i c_i z_ij over
  * probes 0 .. n_pert-1 of `step` (the update box of the ZOO loop flowchart in
  * "Pretraining Transformers Without Backprop: What Two Zero-Order Papers Actually

@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
         "ora_perturb2_f32": (None, [f32p, u64, u64, u64, u32, u32, f32, u32, f32, u8p, u8p]),
         "ora_perturb2_bf16": (None, [u16p, u64, u64, u64, u32, u32, f32, u32, f32, u8p, u8p]),
         "ora_probe_weights": (u32, [f64p, f64p, f64, u32, f64, f64, f32p]),
+        "ora_probe_weights_ex": (u32, [f64p, f64p, f64, u32, f64, f64, ctypes.c_int, f64, f32p]),
         "ora_update_f32": (None, [f32p, u64, u64, u64, u32, f32p, u32, f32, u8p]),
         "ora_update_bf16": (None, [u16p, u64, u64, u64, u32, f32p, u32, f32, u8p]),
         "ora_probe_sums": (None, [f64p, u64, u64, u64, u32, f32p, u32, u8p]),
@@ -196,6 +197,22 @@ def probe_weights(Lp, Lm, L0: float, eps: float, delta: float):
     bad = lib().ora_probe_weights(_ptr(Lp, ctypes.c_double), _ptr(Lm, ctypes.c_double),
                                   float(L0), n, float(eps), float(delta),
                                   _ptr(c, ctypes.c_float))
+    return c, int(bad)
+
+
+WEIGHTS_PRECOND, WEIGHTS_POWER, WEIGHTS_SPSA_MEAN = 0, 1, 2
+
+
+def probe_weights_ex(Lp, Lm, L0: float, eps: float, delta: float, mode: int,
+                     power: float = 1.0):
+    """The weight forms of the pages: preconditioned, curvature power, plain SPSA mean."""
+    Lp = np.ascontiguousarray(Lp, dtype=np.float64)
+    Lm = np.ascontiguousarray(Lm, dtype=np.float64)
+    n = Lp.size
+    c = np.zeros(n, dtype=np.float32)
+    bad = lib().ora_probe_weights_ex(_ptr(Lp, ctypes.c_double), _ptr(Lm, ctypes.c_double),
+                                     float(L0), n, float(eps), float(delta), int(mode),
+                                     float(power), _ptr(c, ctypes.c_float))
     return c, int(bad)
 
 

@@ -251,6 +251,38 @@ uint32_t ora_probe_weights(const double *Lp, const double *Lm, double L0, uint32
     return bad;
 }
 
+/* Other weight forms of the pages, in double, one rounding to fp32:
+ *  mode 0  c_i = g_i / max(|h_i|, delta)            (as ora_probe_weights)
+ *  mode 1  c_i = g_i / max(|h_i|, delta)^power      ("Probe-Space Preconditioning": a
+ *          curvature weight |c_hat_i|^alpha from the clean and perturbed losses that
+ *          shrinks high-curvature probes; the pages' alpha is 0.1)
+ *  mode 2  c_i = g_i / n                            (plain 1SPSA mean of "How 1.5-SPSA
+ *          Works": no clean pass; L0 is not read)
+ * A probe with a non-finite loss it reads gets c_i = 0 and is counted. */
+uint32_t ora_probe_weights_ex(const double *Lp, const double *Lm, double L0, uint32_t n,
+                              double eps, double delta, int mode, double power, float *c)
+{
+    uint32_t bad = 0;
+    for (uint32_t i = 0; i < n; ++i) {
+        int uses_l0 = (mode != 2);
+        if (!isfinite(Lp[i]) || !isfinite(Lm[i]) || (uses_l0 && !isfinite(L0))) {
+            c[i] = 0.0f;
+            ++bad;
+            continue;
+        }
+        double g = (Lp[i] - Lm[i]) / (2.0 * eps);
+        if (mode == 2) {
+            c[i] = (float)(g / (double)n);
+            continue;
+        }
+        double h = ((Lp[i] + Lm[i]) - 2.0 * L0) / (eps * eps);
+        double den = fabs(h) > delta ? fabs(h) : delta;
+        if (mode == 1) den = pow(den, power);
+        c[i] = (float)(g / den);
+    }
+    return bad;
+}
+
 /* ---------------------------------------------------------------------------------- */
 /* Multi-probe update theta <- theta - eta * sum_i c_i z_i (the loop's update box in   */
 /* the ZOO training-loop flowchart; "How 1.5-SPSA Works" for the probe sum).          */

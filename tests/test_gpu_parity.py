@@ -423,3 +423,26 @@ def test_bf16_synthetic_two_pass_step_small(ctx):
                      delta=cfg.delta, losses=(L0, Lp, Lm), schedule="S2f")
     # eta = 0: the passes alone, which are bit-exact
     assert np.array_equal(bf16_bits(t), h)
+
+
+# ------------------------------------------------------------------------------------
+# the other weight forms of the pages
+# ------------------------------------------------------------------------------------
+@pytest.mark.parametrize("mode,power", [(0, 1.0), (1, 0.1), (1, 0.5), (1, 0.0), (2, 1.0)])
+@pytest.mark.parametrize("n", [16, 160, 300])
+def test_probe_weights_ex(ctx, mode, power, n):
+    L0, Lp, Lm = gen.synthetic_losses(3, n, n)
+    Lp[2] = np.inf
+    eps = float(np.float32(1e-3))
+    zo.zo_reset_nonfinite(ctx)
+    L0d = None if mode == 2 else torch.tensor([L0], dtype=torch.float64).cuda()
+    c = zo.zo_probe_weights_ex(ctx, torch.from_numpy(Lp).cuda(), torch.from_numpy(Lm).cuda(),
+                               L0d, eps, 1e-6, mode, power).cpu().numpy()
+    ref, bad = oracle.probe_weights_ex(Lp, Lm, L0, eps, 1e-6, mode, power)
+    assert zo.zo_nonfinite_count(ctx) == bad == 1
+    if mode == 1 and power not in (0.0, 1.0):
+        # pow() of the device library and of libm may differ in the last bit of the double;
+        # after rounding to fp32 the weights agree to one ulp
+        assert np.all(np.abs(c.astype(np.float64) - ref) <= np.spacing(np.abs(ref)))
+    else:
+        assert np.array_equal(c.view(np.uint32), ref.view(np.uint32))

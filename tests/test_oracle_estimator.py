@@ -344,3 +344,52 @@ def test_bf16_s4_drift_is_bounded():
             oracle.perturb(h3, 0, 0, 0, i, s)
     assert np.all(np.abs(oracle.bf16_to_f32(h4) - x0) <= ulp)
     assert np.max(np.abs(oracle.bf16_to_f32(h3) - x0) / ulp) > 4
+
+
+# ------------------------------------------------------------------------------------
+# the other weight forms of the pages
+# ------------------------------------------------------------------------------------
+def _losses(n, seed):
+    L0, Lp, Lm = gen.synthetic_losses(seed, 0, n)
+    return L0, Lp, Lm
+
+
+def test_weights_power_one_is_the_preconditioned_form():
+    L0, Lp, Lm = _losses(64, 1)
+    a, _ = oracle.probe_weights(Lp, Lm, L0, 1e-3, 1e-6)
+    b, _ = oracle.probe_weights_ex(Lp, Lm, L0, 1e-3, 1e-6, oracle.WEIGHTS_POWER, 1.0)
+    c, _ = oracle.probe_weights_ex(Lp, Lm, L0, 1e-3, 1e-6, oracle.WEIGHTS_PRECOND)
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+
+
+def test_weights_power_special_exponents():
+    L0, Lp, Lm = _losses(64, 2)
+    eps = 1e-3
+    g = (Lp - Lm) / (2 * eps)
+    h = (Lp + Lm - 2 * L0) / eps ** 2
+    d = np.maximum(np.abs(h), 1e-6)
+    c0, _ = oracle.probe_weights_ex(Lp, Lm, L0, eps, 1e-6, oracle.WEIGHTS_POWER, 0.0)
+    assert np.array_equal(c0, g.astype(np.float32))            # d^0 = 1: plain central difference
+    c5, _ = oracle.probe_weights_ex(Lp, Lm, L0, eps, 1e-6, oracle.WEIGHTS_POWER, 0.5)
+    ref = g / np.sqrt(d)                                        # library square root
+    assert np.all(np.abs(c5 - ref) <= np.spacing(np.abs(ref).astype(np.float32)))
+    c01, _ = oracle.probe_weights_ex(Lp, Lm, L0, eps, 1e-6, oracle.WEIGHTS_POWER, 0.1)
+    # shrinks high-curvature probes less than the full preconditioner does
+    ratio = np.abs(c01 / g)
+    assert np.all(np.abs(ratio - d ** -0.1) <= 1e-6 * d ** -0.1)
+
+
+def test_weights_spsa_mean_on_quadratic_is_exact():
+    # c_i = g_i / n with exact binary losses: (z_i^T A theta) / n, no clean pass read
+    M, n = 4096, 16
+    th0, a = _dyadic_quadratic(M, 17)
+    th = th0.copy()
+    out = oracle.spsa_step(th, seed=4, step=0, npert=n, eps=2.0 ** -8, eta=0.0, delta=1e-6,
+                           loss_fn=lambda t: oracle.quad_loss(t, a))
+    c, bad = oracle.probe_weights_ex(out["Lp"], out["Lm"], np.nan, 2.0 ** -8, 1e-6,
+                                     oracle.WEIGHTS_SPSA_MEAN)
+    assert bad == 0                                             # L0 is not read
+    Z = np.stack([oracle.signs_from_plane(oracle.gen_plane(4, 0, i, 0, M), M) for i in range(n)])
+    g = Z @ (a.astype(np.float64) * th0.astype(np.float64))
+    for i in range(n):
+        assert c[i] == _nearest_f32(Fraction(g[i]) / n)
