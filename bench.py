@@ -49,7 +49,7 @@ def parse_args(argv=None):
     p.add_argument("--steps", type=int, default=None, help="timed steps (default: config's)")
     p.add_argument("--warmup", type=int, default=1)
     p.add_argument("--config", default="opt30b",
-                   choices=["tiny", "flat125m", "mlp", "opt13b", "opt30b"])
+                   choices=["tiny", "flat125m", "mlp", "lowrank", "opt13b", "opt30b"])
     p.add_argument("--schedule", default="S2f", choices=["S2f", "S4"],
                    help="S2f: two passes per probe (restore fused with the next probe's "
                         "move); S4: four passes per probe")
@@ -166,7 +166,7 @@ def main(argv=None):
 
     # CPU oracle leg first (host only; keeps the GPU phase uninterrupted).
     cpu = None
-    if not args.no_cpu_baseline and cfg.loss != "mlp":
+    if not args.no_cpu_baseline and cfg.loss in ("synthetic", "quad"):
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         log(f"[bench] cpu baseline: {threads} threads x {args.cpu_params_per_thread} params")
         cpu = cpu_baseline(cfg, args.cpu_params_per_thread, threads, args.schedule)
@@ -195,6 +195,12 @@ def main(argv=None):
         theta.copy_(torch.from_numpy(th0))
         a_dev = torch.from_numpy(a).to(dev)
         del th0, a
+    elif cfg.loss == "lowrank":
+        th0, a, U = gen.lowrank_problem(cfg)
+        theta.copy_(torch.from_numpy(th0))
+        a_dev = torch.from_numpy(a).to(dev)
+        U_dev = torch.from_numpy(U).to(dev)
+        del th0, a, U
     else:
         gen.device_normal_(theta, cfg.theta_std, cfg.seed)
     torch.cuda.synchronize()
@@ -229,6 +235,9 @@ def main(argv=None):
     def loss_into(out, record):
         if cfg.loss == "quad":
             timed("loss", lambda: zo.zo_quad_loss(ctx, theta, a_dev, out=out), record)
+        elif cfg.loss == "lowrank":
+            timed("loss", lambda: zo.zo_lowrank_quad_loss(ctx, theta, a_dev, U_dev, out=out),
+                  record)
 
     def mlp_loss(out, probe, alpha, s, record):
         if probe is None:
@@ -314,6 +323,18 @@ def main(argv=None):
     else:
         achieved = pass_bytes / (pert_ms * 1e-3) / 1e9
         roofline = None
+        loss_times = times(["loss"])
+        if loss_times and sum(loss_times) > sum(times(["perturb", "perturb2"])):
+            # the loss evaluations dominate: theta, a (and U) read once per evaluation
+            r = cfg.extra.get("rank", 0) if cfg.loss == "lowrank" else 0
+            loss_bytes = float(esize + 4 + 4 * r) * M
+            la = loss_bytes / (sum(loss_times) / len(loss_times) * 1e-3) / 1e9
+            roofline = {"kernel": ("k_lowrank_partial" if r else "k_quad_loss_partial") +
+                                  " (loss evaluation, fp64 accumulation)",
+                        "bound": "hbm", "achieved": la, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                        "frac": la / PEAK_HBM_GBPS, "traffic": None,
+                        "note": f"{loss_bytes / 1e6:.0f} MB per evaluation; partly resident in "
+                                f"the 256 MB last-level cache"}
     traffic = stored_traffic(f"{cfg.name}/{args.schedule}", pass_bytes)
     result = {
         "metric": "probe*params/s and HBM GB/s (% peak) per 1.5-SPSA step, n_pert=160, 1 GPU",

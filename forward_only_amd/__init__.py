@@ -26,7 +26,8 @@ from ._lib import (ZO_BF16, ZO_EHIP, ZO_EINVAL, ZO_ENOMEM, ZO_EUNSUPPORTED, ZO_F
 __all__ = [
     "Context", "ZOError", "zo_init", "zo_destroy", "zo_bits_stride", "zo_gen_probes",
     "zo_perturb", "zo_perturb2", "zo_probe_weights", "zo_probe_weights_ex", "zo_update", "zo_nonfinite_count",
-    "zo_reset_nonfinite", "zo_quad_loss", "zo_mlp_workspace_bytes", "zo_mlp_loss",
+    "zo_reset_nonfinite", "zo_quad_loss", "zo_lowrank_quad_loss", "zo_mlp_workspace_bytes",
+    "zo_mlp_loss",
     "zo_mlp_loss_perturbed", "library_path",
 ]
 
@@ -214,6 +215,23 @@ def zo_quad_loss(ctx: Context, theta: torch.Tensor, a: torch.Tensor,
                                        _dev(a, "a", torch.float32), theta.numel(),
                                        _dev(out, "out", torch.float64), _stream(stream)),
                "zo_quad_loss")
+    return out
+
+
+def zo_lowrank_quad_loss(ctx: Context, theta: torch.Tensor, a: torch.Tensor, U: torch.Tensor,
+                         out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """1/2 sum a_j theta_j^2 + 1/2 ||U theta||^2 (U: [r, n] float32) into a float64 tensor."""
+    n = theta.numel()
+    if a.numel() != n or (U.numel() and U.shape[-1] != n):
+        raise ValueError("a must have n entries and U shape (r, n)")
+    r = U.numel() // n if n else 0
+    if out is None:
+        out = torch.empty(1, dtype=torch.float64, device="cuda")
+    up = _dev(U, "U", torch.float32) if U.numel() else None
+    _lib.check(_lib.lib().zo_lowrank_quad_loss(ctx.handle, _dev(theta, "theta"),
+                                               _dtype_code(theta), _dev(a, "a", torch.float32),
+                                               up, r, n, _dev(out, "out", torch.float64),
+                                               _stream(stream)), "zo_lowrank_quad_loss")
     return out
 
 

@@ -39,6 +39,7 @@ SIGNATURES = {
     "zo_nonfinite_count": (_int, [_vp, _vp, ctypes.POINTER(_u32)]),
     "zo_reset_nonfinite": (_int, [_vp, _vp]),
     "zo_quad_loss": (_int, [_vp, _vp, _int, _vp, _u64, _vp, _vp]),
+    "zo_lowrank_quad_loss": (_int, [_vp, _vp, _int, _vp, _vp, _u32, _u64, _vp, _vp]),
     "zo_mlp_workspace_bytes": (_u64, [_u32, _u32, _u32, _u32]),
     "zo_mlp_loss": (_int, [_vp, _vp, _vp, _vp, _u32, _u32, _u32, _u32, _vp, _u64, _vp, _vp]),
     "zo_mlp_loss_perturbed": (_int, [_vp, _vp, _u64, _u32, _u32, _f32, _vp, _vp, _vp, _u32,

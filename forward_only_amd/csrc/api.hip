@@ -10,7 +10,7 @@ struct zo_ctx {
     int device;
     int num_cus;
     uint32_t *d_counter;   // non-finite probe counter
-    double *d_partials;    // quadratic-loss partial sums (zo::kLossPartials doubles)
+    double *d_partials;    // loss partial sums (zo::kLossPartials * (kLowRankMax + 1) doubles)
 };
 
 namespace {
@@ -68,8 +68,8 @@ zo_status zo_init(uint64_t seed, zo_ctx **out)
         (void)hipGetLastError();
         return ZO_ENOMEM;
     }
-    if (hipMalloc(reinterpret_cast<void **>(&c->d_partials), zo::kLossPartials * sizeof(double)) !=
-        hipSuccess) {
+    if (hipMalloc(reinterpret_cast<void **>(&c->d_partials),
+                  (size_t)zo::kLossPartials * (zo::kLowRankMax + 1) * sizeof(double)) != hipSuccess) {
         (void)hipFree(c->d_counter);
         delete c;
         (void)hipGetLastError();
@@ -210,6 +210,19 @@ zo_status zo_quad_loss(zo_ctx *c, const void *d_theta, zo_dtype dtype, const flo
     if (n > 0 && (!d_theta || !d_a || !aligned16(d_theta) || !aligned16(d_a))) return ZO_EINVAL;
     return from_hip(zo::launch_quad_loss(d_theta, dtype == ZO_BF16, d_a, n, c->d_partials, d_out,
                                          as_stream(stream)));
+}
+
+zo_status zo_lowrank_quad_loss(zo_ctx *c, const void *d_theta, zo_dtype dtype,
+                               const float *d_a, const float *d_U, uint32_t r, uint64_t n,
+                               double *d_out, void *stream)
+{
+    if (!c || !d_out) return ZO_EINVAL;
+    if (dtype != ZO_FP32 && dtype != ZO_BF16) return ZO_EINVAL;
+    if (r > zo::kLowRankMax) return ZO_EUNSUPPORTED;
+    if (n > 0 && (!d_theta || !d_a || !aligned16(d_theta) || !aligned16(d_a))) return ZO_EINVAL;
+    if (n > 0 && r > 0 && (!d_U || !aligned16(d_U))) return ZO_EINVAL;
+    return from_hip(zo::launch_lowrank_loss(d_theta, dtype == ZO_BF16, d_a, d_U, r, n,
+                                            c->d_partials, d_out, as_stream(stream)));
 }
 
 uint64_t zo_mlp_workspace_bytes(uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out)

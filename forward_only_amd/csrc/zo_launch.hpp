@@ -47,6 +47,13 @@ constexpr uint32_t kLossPartials = 1024;
 hipError_t launch_quad_loss(const void *theta, bool bf16, const float *a, uint64_t n,
                             double *partials, double *out, hipStream_t stream);
 
+// 1/2 sum a_j theta_j^2 + 1/2 ||U theta||^2, U row-major [r][n], r <= kLowRankMax;
+// `partials` holds kLossPartials * (kLowRankMax + 1) doubles.
+constexpr uint32_t kLowRankMax = 16;
+hipError_t launch_lowrank_loss(const void *theta, bool bf16, const float *a, const float *U,
+                               uint32_t r, uint64_t n, double *partials, double *out,
+                               hipStream_t stream);
+
 // Two-layer MLP classifier loss (fp32 parameters, MFMA GEMM, fp64 reduction); with
 // `pert` the parameters are read as theta + alpha * z_probe without being written.
 struct MlpPerturb {

@@ -175,6 +175,18 @@ zo_status zo_reset_nonfinite(zo_ctx *ctx, void *stream);
 zo_status zo_quad_loss(zo_ctx *ctx, const void *d_theta, zo_dtype dtype, const float *d_a,
                        uint64_t n, double *d_out, void *stream);
 
+/* Low-rank-plus-diagonal quadratic loss L = 1/2 sum_j a_j theta_j^2 + 1/2 ||U theta||^2,
+ * fp64 accumulation, deterministic.  A synthetic model whose curvature along a probe,
+ * sum_j a_j + ||U z||^2, differs from probe to probe -- the landscape on which the clean-pass
+ * preconditioner is said to pay off with the condition number ("Probe-Space
+ * Preconditioning" on "Stanford's 1.5-SPSA Trains OPT-30B Without Backpropagation").
+ * d_U: device fp32, r rows of n (row-major, each row contiguous), 16-byte aligned; r = 0
+ * gives the diagonal loss.  Errors: ZO_EINVAL as zo_quad_loss or d_U NULL/misaligned with
+ * r > 0; ZO_EUNSUPPORTED if r > 16. */
+zo_status zo_lowrank_quad_loss(zo_ctx *ctx, const void *d_theta, zo_dtype dtype,
+                               const float *d_a, const float *d_U, uint32_t r, uint64_t n,
+                               double *d_out, void *stream);
+
 /* Loss of a two-layer MLP classifier -- the model forward of the ZOO loop ("N forward
  * passes, loss only" box of the flowchart in "Pretraining Transformers Without Backprop:
  * What Two Zero-Order Papers Actually Measure") for the small real-model workload:

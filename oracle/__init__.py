@@ -257,5 +257,6 @@ def quad_loss(theta: np.ndarray, a: np.ndarray) -> float:
     raise TypeError(theta.dtype)
 
 
+from .lowrank import lowrank_quad_loss  # noqa: E402  (plain fp64 numpy)
 from .mlp import mlp_loss, mlp_unflatten  # noqa: E402  (plain fp64 numpy)
 from .step import spsa_step  # noqa: E402

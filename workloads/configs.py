@@ -48,6 +48,8 @@ CONFIGS = {
                        "quad", 0.02, (-3.0, 3.0), bits="regen"),
     "mlp": Config("mlp", 768 * 3072 + 3072 + 2 * 3072 + 2, "fp32", 64, 1e-3, 1e-3, 1e-6, 50,
                   "mlp", 0.02, bits="read", extra=dict(MLP_SHAPE)),
+    "lowrank": Config("lowrank", 1 << 20, "fp32", 16, 2.0 ** -10, 1e-2, 1e-6, 100, "lowrank",
+                      1.0, bits="regen", extra={"rank": 4, "spike": 1e4, "diag": 1.0}),
     "opt13b": Config("opt13b", opt_param_count(40, 5120, 20480, 50272), "bf16", 160, 1e-3,
                      1e-3, 1e-6, 5, "synthetic", 0.02, bits="regen",
                      extra={"layers": 40, "d": 5120, "ffn": 20480, "vocab": 50272}),

@@ -32,6 +32,25 @@ def theta_and_a(cfg: Config):
     return theta, a
 
 
+def lowrank_problem(cfg: Config, M: int | None = None, rank: int | None = None,
+                    spike: float | None = None):
+    """(theta float32 [M], a float32 [M], U float32 [rank, M]) for the low-rank-plus-
+    diagonal quadratic: theta ~ N(0, theta_std), a_j = diag, and U's rows orthogonal
+    directions scaled so that the curvature along row k is `spike` (times 1, 2, ...)."""
+    e = cfg.extra
+    M = M or cfg.M
+    rank = rank if rank is not None else e["rank"]
+    spike = spike if spike is not None else e["spike"]
+    rng = np.random.Generator(np.random.PCG64(cfg.seed + 101))
+    theta = (rng.standard_normal(M) * cfg.theta_std).astype(np.float32)
+    a = np.full(M, e["diag"], dtype=np.float32)
+    G = rng.standard_normal((rank, M))
+    Q, _ = np.linalg.qr(G.T)                              # orthonormal columns
+    scales = np.sqrt(spike * (np.arange(rank) + 1.0))
+    U = np.ascontiguousarray((Q.T * scales[:, None]).astype(np.float32))
+    return theta, a, U
+
+
 def synthetic_losses(seed: int, step: int, n: int):
     """(L0, Lp[n], Lm[n]) float64 for the synthetic-loss workloads."""
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, step])))
