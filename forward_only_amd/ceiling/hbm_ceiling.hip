@@ -1,7 +1,7 @@
 // hbm_ceiling.hip -- attainable HBM bandwidth of plain streaming kernels on this GPU:
 // read-only, write-only, copy and in-place read-modify-write over one large buffer.
 // These are the ceilings the perturb pass (an in-place read-modify-write of every
-// parameter) is judged against besides the datasheet peak.
+// parameter) is compared with, besides the datasheet peak.
 //
 //   hbm_ceiling [GB]      (default 59.92 GB, the OPT-30B-shaped bf16 parameter set)
 //
