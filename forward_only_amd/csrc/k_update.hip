@@ -34,25 +34,32 @@ namespace zo {
 constexpr int kUpdWavesPerWG = 8;
 constexpr int kUpdThreads = kUpdWavesPerWG * kWave;
 constexpr int kUpdBlocksPerWave = 8;
-constexpr uint32_t kXchWordsPerWave = 256;  // 8 octets x 8 lanes x 4 words
+// 8 octets x (8 lanes x 4 words), octet slices 40 words apart so that the eight octets'
+// stores of one word fall in distinct LDS banks (a 32-word stride would put the even and
+// the odd octets on the same banks).
+constexpr uint32_t kOctetStride = 40;
+constexpr uint32_t kXchWordsPerWave = 8 * kOctetStride;
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // In-register transpose of an 8x8 bit matrix held as two dwords (rows 0-3 in L, rows
 // 4-7 in H, row k = byte k, column b = bit b): afterwards byte b holds column b.
 // Three masked delta swaps (distances 7, 14, 28 in the 64-bit view).
+// Each swap is t = (x ^ (x >> d)) & mask; x ^= t ^ (t << d): two shifts and two
+// three-input bit ops.
+__device__ __forceinline__ uint32_t delta_swap(uint32_t x, int d, uint32_t mask)
+{
+    const uint32_t t = ZO_BITOP3(x, x >> d, mask, kXorAnd);
+    return ZO_BITOP3(x, t, t << d, kXor3);
+}
+
 __device__ __forceinline__ void transpose8x8(uint32_t &L, uint32_t &H)
 {
-    uint32_t t;
-    t = (L ^ (L >> 7)) & 0x00AA00AAu;
-    L = L ^ t ^ (t << 7);
-    t = (H ^ (H >> 7)) & 0x00AA00AAu;
-    H = H ^ t ^ (t << 7);
-    t = (L ^ (L >> 14)) & 0x0000CCCCu;
-    L = L ^ t ^ (t << 14);
-    t = (H ^ (H >> 14)) & 0x0000CCCCu;
-    H = H ^ t ^ (t << 14);
-    t = (L ^ (H << 4)) & 0xF0F0F0F0u;
+    L = delta_swap(L, 7, 0x00AA00AAu);
+    H = delta_swap(H, 7, 0x00AA00AAu);
+    L = delta_swap(L, 14, 0x0000CCCCu);
+    H = delta_swap(H, 14, 0x0000CCCCu);
+    const uint32_t t = ZO_BITOP3(L, H << 4, 0xF0F0F0F0u, kXorAnd);
     L = L ^ t;
     H = H ^ (t >> 4);
 }
@@ -155,7 +162,7 @@ __global__ __launch_bounds__(kUpdThreads) void k_update(void *__restrict__ theta
     const int lane = threadIdx.x & (kWave - 1);
     const int oct = lane >> 3;
     const int r = lane & 7;
-    uint32_t *oxch = xch + oct * 32;
+    uint32_t *oxch = xch + oct * kOctetStride;
     const uint32_t beta = 2u * (uint32_t)(r & 1);
     // byte beta of x, byte beta of y, byte beta+1 of x, byte beta+1 of y
     const uint32_t sel = beta | ((4u + beta) << 8) | ((beta + 1u) << 16) | ((5u + beta) << 24);

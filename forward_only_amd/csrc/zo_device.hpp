@@ -10,10 +10,16 @@ namespace zo {
 constexpr int kWave = 64;           // CDNA wavefront width
 constexpr int kBlockParams = 128;   // params covered by one Philox4x32-10 call
 
+// Three-input bitwise function (gfx950 v_bitop3_b32); `tt` is the truth table over the
+// canonical inputs a = 0xF0, b = 0xCC, c = 0xAA.
+constexpr uint32_t kXor3 = 0x96;          // a ^ b ^ c
+constexpr uint32_t kXorAnd = 0x28;        // (a ^ b) & c
+#define ZO_BITOP3(a, b, c, tt) __builtin_amdgcn_bitop3_b32((a), (b), (c), (tt))
+
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2,
 // 3", SC'11, section 4).  Per round two 32x32->64 products (one v_mad_u64_u32 each on
-// gfx950) and two three-way xors; the key schedule is uniform across the wave, so the
-// compiler keeps it in scalar registers.
+// gfx950) and two three-way xors (one v_bitop3_b32 each); the key schedule is uniform
+// across the wave, so the compiler keeps it in scalar registers.
 struct U32x4 {
     uint32_t x, y, z, w;
 };
@@ -25,8 +31,8 @@ __device__ __forceinline__ U32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     for (int r = 0; r < 10; ++r) {
         const uint64_t p0 = (uint64_t)0xD2511F53u * (uint64_t)c0;
         const uint64_t p1 = (uint64_t)0xCD9E8D57u * (uint64_t)c2;
-        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n0 = ZO_BITOP3((uint32_t)(p1 >> 32), c1, k0, kXor3);
+        const uint32_t n2 = ZO_BITOP3((uint32_t)(p0 >> 32), c3, k1, kXor3);
         c1 = (uint32_t)p1;
         c3 = (uint32_t)p0;
         c0 = n0;
