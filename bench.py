@@ -37,6 +37,8 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, vendor figure
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix, vendor figure
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_perturb.json")
 PERTURB_SOURCES = ["forward_only_amd/csrc/k_perturb.hip", "forward_only_amd/csrc/zo_device.hpp"]
+PHILOX_FILE = os.path.join(ROOT, "profiles", "philox_ceiling.json")
+PHILOX_SOURCES = ["forward_only_amd/csrc/zo_device.hpp", "forward_only_amd/ceiling/philox_ceiling.hip"]
 
 
 def log(*a):
@@ -83,6 +85,30 @@ def stored_traffic(workload: str, nbytes_alg: float):
     return float(t["bytes_per_dispatch"])
 
 
+def stored_philox_peak():
+    """Measured Philox4x32-10 calls/s of the generator alone (the ceiling microbenchmark),
+    if it was taken on the current generator source; else None."""
+    try:
+        with open(PHILOX_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_hash(PHILOX_SOURCES):
+        return None
+    return float(t["calls_per_s"])
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 # ------------------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, on a bounded slice of the same workload
 # ------------------------------------------------------------------------------------
@@ -116,11 +142,22 @@ def cpu_baseline(cfg, params_per_thread: int, threads: int, schedule: str):
         t.join()
     dt = time.perf_counter() - t0
     work = cfg.npert * params_per_thread * threads
+
+    # the same oracle on one core, over a quarter of one window
+    n1 = max(128, params_per_thread // 4)
+    w1 = windows[0][:n1].copy()
+    t1 = time.perf_counter()
+    oracle.spsa_step(w1, seed=cfg.seed, step=0, npert=cfg.npert, eps=cfg.eps, eta=cfg.eta,
+                     delta=cfg.delta, losses=(L0, Lp, Lm), offset=offsets[0], schedule=schedule)
+    dt1 = time.perf_counter() - t1
     return {
         "value": work / dt, "unit": "probe*params/s", "cores": threads, "kind": "oracle",
         "sample": (f"{threads} windows x {params_per_thread} {cfg.dtype} params of the "
                    f"{cfg.name} workload, one full step (n_pert={cfg.npert}, schedule "
                    f"{schedule}, weights, update), one window per thread; {dt:.1f} s"),
+        "single_core_value": cfg.npert * n1 / dt1,
+        "single_core_sample": f"{n1} params of the first window on one thread; {dt1:.1f} s",
+        "cpu_model": cpu_model(),
     }
 
 
@@ -135,6 +172,21 @@ def copy_calibration():
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes,
                       "dispatches": 3}), flush=True)
+
+
+def update_roofline(M: int, n: int, pass_bytes: float, upd_ms):
+    """The update kernel beside its two ceilings: HBM bytes (one read and one write of theta)
+    and the Philox calls it makes to regenerate n probes' bits (n / 128 per parameter)."""
+    if not upd_ms:
+        return None
+    calls = M * n / 128.0 / (upd_ms * 1e-3)
+    peak = stored_philox_peak()
+    return {"kernel": "k_update", "bound": "lds",
+            "achieved_GBps": pass_bytes / (upd_ms * 1e-3) / 1e9,
+            "hbm_frac": pass_bytes / (upd_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "probe_params_per_s": n * M / (upd_ms * 1e-3),
+            "philox_calls_per_s": calls, "philox_peak_calls_per_s": peak,
+            "philox_frac": (calls / peak) if peak else None}
 
 
 def main(argv=None):
@@ -370,8 +422,7 @@ def main(argv=None):
                                  "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
                                  "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                                  "traffic": traffic},
-        "update_roofline": {"achieved_GBps": pass_bytes / (upd_ms * 1e-3) / 1e9,
-                            "probe_params_per_s": n * M / (upd_ms * 1e-3)},
+        "update_roofline": update_roofline(M, n, pass_bytes, upd_ms),
         "nonfinite_probes": nonfinite,
         "cpu_baseline": cpu,
     }

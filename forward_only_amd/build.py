@@ -23,6 +23,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libzo.so")
 CEILING_SRC = os.path.join(HERE, "ceiling", "hbm_ceiling.hip")
 CEILING_BIN = os.path.join(HERE, "hbm_ceiling")
+PHILOX_SRC = os.path.join(HERE, "ceiling", "philox_ceiling.hip")
+PHILOX_BIN = os.path.join(HERE, "philox_ceiling")
 ARCH = os.environ.get("ZO_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -67,15 +69,17 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
 
 def build_ceiling(verbose: bool = False) -> str:
-    """The standalone HBM-ceiling microbenchmark (read, write, copy, in-place RMW)."""
-    tmp = CEILING_BIN + f".tmp{os.getpid()}"
-    cmd = [HIPCC, *CFLAGS, "-o", tmp, CEILING_SRC]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {CEILING_SRC}:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, CEILING_BIN)
+    """The standalone ceiling microbenchmarks: HBM (read, write, copy, in-place RMW) and
+    Philox4x32-10 calls per second."""
+    for src, out in ((CEILING_SRC, CEILING_BIN), (PHILOX_SRC, PHILOX_BIN)):
+        tmp = out + f".tmp{os.getpid()}"
+        cmd = [HIPCC, *CFLAGS, "-o", tmp, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, out)
     return CEILING_BIN
 
 
