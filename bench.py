@@ -272,7 +272,8 @@ def main(argv=None):
     a = applied_eps(cfg.eps)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    per = {"perturb": [], "perturb2": [], "weights": [], "update": [], "loss": [], "mlp": []}
+    per = {"perturb": [], "perturb2": [], "weights": [], "update": [], "loss": [], "mlp": [],
+           "mlp_pair": []}
 
     def timed(kind, fn, record):
         if record:
@@ -301,14 +302,19 @@ def main(argv=None):
                 ctx, theta, 0, s, probe, alpha, mlp["X"], mlp["y"], mlp["d_hid"],
                 mlp["d_out"], workspace=mlp["ws"], out=out), record)
 
+    def mlp_pair(op, om, probe, s, record):
+        timed("mlp_pair", lambda: zo.zo_mlp_loss_pair(
+            ctx, theta, 0, s, probe, a, mlp["X"], mlp["y"], mlp["d_hid"], mlp["d_out"],
+            workspace=mlp["ws"], out_plus=op, out_minus=om), record)
+
     def one_step(s, record):
         L0, Lp, Lm = L0s[s], Lps[s], Lms[s]
         if mlp is not None:
-            # the forward applies each probe while reading the weights: no passes over theta
+            # the forward applies each probe while reading the weights: no passes over
+            # theta; one paired launch sequence gives both losses of a probe
             mlp_loss(L0, None, 0.0, s, record)
             for i in range(n):
-                mlp_loss(Lp[i:i + 1], i, +a, s, record)
-                mlp_loss(Lm[i:i + 1], i, -a, s, record)
+                mlp_pair(Lp[i:i + 1], Lm[i:i + 1], i, s, record)
             timed("weights", lambda: zo.zo_probe_weights(ctx, Lp, Lm, L0, a, cfg.delta,
                                                          out=c_buf), record)
             timed("update", lambda: zo.zo_update(ctx, theta, 0, s, c_buf, cfg.eta), record)
@@ -366,9 +372,10 @@ def main(argv=None):
     pass_bytes = 2.0 * esize * M                      # one read + one write of theta
     step_bytes = (passes + 1) * pass_bytes            # the passes + the update
     if mlp is not None:
-        mlp_ms = avg_ms("mlp")
-        achieved = mlp["flop"] / (mlp_ms * 1e-3) / 1e12
-        roofline = {"kernel": "k_mlp_tiles (MFMA fp32 GEMM of the MLP forward, fused probe)",
+        mlp_ms = avg_ms("mlp_pair")
+        achieved = 2.0 * mlp["flop"] / (mlp_ms * 1e-3) / 1e12
+        roofline = {"kernel": "k_mlp_tiles (MFMA fp32 GEMM of the MLP forward, both signs of "
+                              "a probe per launch; time of the whole loss chain)",
                     "bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS,
                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
                     "traffic": None}
@@ -403,8 +410,8 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": (f"{cfg.name}: {M} {cfg.dtype} params in one flat buffer, "
                                 f"n_pert={n}, eps={cfg.eps}, eta={cfg.eta}, " +
-                                ("probes applied inside the MFMA forward (no passes over "
-                                 "theta) + update" if mlp is not None else
+                                ("probes applied inside the MFMA forward, both signs per "
+                                 "launch (no passes over theta) + update" if mlp is not None else
                                  f"schedule {args.schedule} ({passes} passes + update)") +
                                 ", probes regenerated, losses " +
                                 ("synthetic" if cfg.loss == "synthetic" else cfg.loss)),
@@ -416,7 +423,8 @@ def main(argv=None):
         "kernels_ms": {"pass_avg": pert_ms, "perturb_avg": avg_ms("perturb"),
                        "perturb2_avg": avg_ms("perturb2"), "update_avg": upd_ms,
                        "weights_avg": w_ms, "loss_avg": avg_ms("loss"),
-                       "mlp_forward_avg": avg_ms("mlp")},
+                       "mlp_forward_avg": avg_ms("mlp"),
+                       "mlp_pair_avg": avg_ms("mlp_pair")},
         "roofline": roofline or {"kernel": f"k_perturb_chunks ({cfg.dtype}, probes regenerated; "
                                            f"every zo_perturb / zo_perturb2 pass)",
                                  "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,

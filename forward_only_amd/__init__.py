@@ -28,7 +28,7 @@ __all__ = [
     "zo_perturb", "zo_perturb2", "zo_probe_weights", "zo_probe_weights_ex", "zo_update", "zo_nonfinite_count",
     "zo_reset_nonfinite", "zo_quad_loss", "zo_lowrank_quad_loss", "zo_mlp_workspace_bytes",
     "zo_mlp_loss",
-    "zo_mlp_loss_perturbed", "library_path",
+    "zo_mlp_loss_perturbed", "zo_mlp_loss_pair", "library_path",
 ]
 
 
@@ -286,3 +286,26 @@ def zo_mlp_loss_perturbed(ctx: Context, params: torch.Tensor, offset: int, step:
         d_out, pw, wbytes, _dev(out, "out", torch.float64), _stream(stream)),
         "zo_mlp_loss_perturbed")
     return out
+
+
+def zo_mlp_loss_pair(ctx: Context, params: torch.Tensor, offset: int, step: int, probe: int,
+                     alpha: float, X: torch.Tensor, labels: torch.Tensor, d_hid: int,
+                     d_out: int, bits: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None, out_plus: torch.Tensor | None = None,
+                     out_minus: torch.Tensor | None = None, stream=None):
+    """The MLP losses at params + alpha * z_probe and params - alpha * z_probe, in one
+    launch sequence, without writing params; returns (out_plus, out_minus)."""
+    batch, d_in, pp, px, pl, ws, pw, wbytes, out_plus = _mlp_args(params, X, labels, d_hid,
+                                                                  d_out, workspace, out_plus)
+    if out_minus is None:
+        out_minus = torch.empty(1, dtype=torch.float64, device="cuda")
+    bp = None
+    if bits is not None:
+        bp = _dev(bits, "bits", torch.uint8)
+        if bits.numel() < zo_bits_stride(params.numel()):
+            raise ValueError("bits row is too short")
+    _lib.check(_lib.lib().zo_mlp_loss_pair(
+        ctx.handle, pp, offset, step, probe, float(alpha), bp, px, pl, batch, d_in, d_hid,
+        d_out, pw, wbytes, _dev(out_plus, "out_plus", torch.float64),
+        _dev(out_minus, "out_minus", torch.float64), _stream(stream)), "zo_mlp_loss_pair")
+    return out_plus, out_minus

@@ -44,6 +44,8 @@ SIGNATURES = {
     "zo_mlp_loss": (_int, [_vp, _vp, _vp, _vp, _u32, _u32, _u32, _u32, _vp, _u64, _vp, _vp]),
     "zo_mlp_loss_perturbed": (_int, [_vp, _vp, _u64, _u32, _u32, _f32, _vp, _vp, _vp, _u32,
                                      _u32, _u32, _u32, _vp, _u64, _vp, _vp]),
+    "zo_mlp_loss_pair": (_int, [_vp, _vp, _u64, _u32, _u32, _f32, _vp, _vp, _vp, _u32,
+                                _u32, _u32, _u32, _vp, _u64, _vp, _vp, _vp]),
 }
 
 _lock = threading.Lock()

@@ -228,7 +228,8 @@ zo_status zo_lowrank_quad_loss(zo_ctx *c, const void *d_theta, zo_dtype dtype,
 uint64_t zo_mlp_workspace_bytes(uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out)
 {
     (void)d_in;
-    return ((uint64_t)(d_hid / 16u) * batch * d_out + batch) * sizeof(double);
+    // partial logits and row losses of two signs (zo_mlp_loss_pair); one-sign calls use half
+    return 2u * ((uint64_t)(d_hid / 16u) * batch * d_out + batch) * sizeof(double);
 }
 
 static zo_status mlp_checks(zo_ctx *c, const float *d_params, const float *d_X,
@@ -275,6 +276,25 @@ zo_status zo_mlp_loss_perturbed(zo_ctx *c, const float *d_params, uint64_t offse
     return from_hip(zo::launch_mlp_loss(d_params, d_X, d_labels, batch, d_in, d_hid, d_out,
                                         static_cast<double *>(d_workspace), d_loss, &pert,
                                         key_of(c), as_stream(stream)));
+}
+
+zo_status zo_mlp_loss_pair(zo_ctx *c, const float *d_params, uint64_t offset, uint32_t step,
+                           uint32_t probe, float alpha, const uint8_t *d_bits, const float *d_X,
+                           const int64_t *d_labels, uint32_t batch, uint32_t d_in,
+                           uint32_t d_hid, uint32_t d_out, void *d_workspace,
+                           uint64_t workspace_bytes, double *d_loss_plus, double *d_loss_minus,
+                           void *stream)
+{
+    const zo_status st = mlp_checks(c, d_params, d_X, d_labels, batch, d_in, d_hid, d_out,
+                                    d_workspace, workspace_bytes, d_loss_plus);
+    if (st != ZO_OK) return st;
+    if (!d_loss_minus) return ZO_EINVAL;
+    const uint64_t nparams = (uint64_t)d_hid * d_in + d_hid + (uint64_t)d_out * d_hid + d_out;
+    if (!range_ok(offset, nparams)) return ZO_EINVAL;
+    const zo::MlpPerturb pert{offset, step, probe, alpha, d_bits};
+    return from_hip(zo::launch_mlp_loss(d_params, d_X, d_labels, batch, d_in, d_hid, d_out,
+                                        static_cast<double *>(d_workspace), d_loss_plus, &pert,
+                                        key_of(c), as_stream(stream), d_loss_minus));
 }
 
 }  // extern "C"

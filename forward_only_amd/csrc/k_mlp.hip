@@ -21,6 +21,11 @@
 // Perturbation-fused variant (kPert): every parameter is read as the fp32 value
 // theta_j + (bit ? alpha : -alpha) of probe `probe` at `step` -- the value an in-place
 // zo_perturb would have stored -- so the loss at theta +/- eps*z_i needs no pass over theta.
+// Paired variant (kPair): the losses at +alpha and -alpha in one launch sequence; each W1
+// operand is loaded once and feeds two accumulators (the second sees theta_j + (bit ?
+// -alpha : alpha)), each with exactly the MFMA sequence of a single fused launch, so both
+// losses equal the single fused results bit for bit.  Sign s (0: +alpha, 1: -alpha) writes
+// its partial logits, row losses and loss to its own slots.
 #include <stdlib.h>
 
 #include "zo_device.hpp"
@@ -70,7 +75,7 @@ __device__ __forceinline__ float gelu_exact(float x)
     return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
 }
 
-template <bool kPert>
+template <bool kPert, bool kPair>
 __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
                                                   const float *__restrict__ params,
                                                   uint32_t batch, uint32_t d_in, uint32_t d_hid,
@@ -90,11 +95,12 @@ __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
     const float *wptr = params + wrow;
 
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4_t acc2 = {0.0f, 0.0f, 0.0f, 0.0f};   // kPair: the -alpha accumulator
     uint64_t cached_blk = ~(uint64_t)0;
     U32x4 cw = {0u, 0u, 0u, 0u};
 
-    // Apply the probe to one loaded float4 of W1 (flat index j, a multiple of 4).
-    auto perturb4 = [&](f32x4_t &b, uint64_t j) {
+    // Sign bits of the 4 params j .. j+3 of W1 (j a multiple of 4) in the low 4 bits.
+    auto bits4 = [&](uint64_t j) -> uint32_t {
         uint32_t q;
         if (pa.bits) {
             q = (uint32_t)(pa.bits[j >> 3] >> (j & 4)) & 0xFu;
@@ -108,16 +114,31 @@ __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
             const uint32_t word = sel == 0 ? cw.x : sel == 1 ? cw.y : sel == 2 ? cw.z : cw.w;
             q = (word >> (g & 31)) & 0xFu;
         }
-        b[0] = with_sign(b[0], q & 1u, pa.alpha);
-        b[1] = with_sign(b[1], (q >> 1) & 1u, pa.alpha);
-        b[2] = with_sign(b[2], (q >> 2) & 1u, pa.alpha);
-        b[3] = with_sign(b[3], (q >> 3) & 1u, pa.alpha);
+        return q;
     };
-    auto mfma4 = [&](const f32x4_t &a, const f32x4_t &b) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
+    auto mfma4 = [](f32x4_t &c, const f32x4_t &a, const f32x4_t &b) {
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+    };
+    // One 16-k group: operand a of X, operand b of W1 at flat index j.
+    auto group = [&](const f32x4_t &a, const f32x4_t &b, uint64_t j) {
+        if constexpr (!kPert) {
+            mfma4(acc, a, b);
+        } else {
+            const uint32_t q = bits4(j);
+            f32x4_t bp;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) bp[t] = with_sign(b[t], (q >> t) & 1u, pa.alpha);
+            mfma4(acc, a, bp);
+            if constexpr (kPair) {
+                f32x4_t bm;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) bm[t] = with_sign(b[t], (q >> t) & 1u, -pa.alpha);
+                mfma4(acc2, a, bm);
+            }
+        }
     };
 
     // Stages of kStage K-groups (16 k each): the loads of stage s+1 are in flight while
@@ -135,10 +156,7 @@ __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
     };
     auto run_stage = [&](f32x4_t (&a)[kStage], f32x4_t (&b)[kStage], uint32_t kb) {
 #pragma unroll
-        for (uint32_t g = 0; g < kStage; ++g) {
-            if constexpr (kPert) perturb4(b[g], wrow + kb + 16u * g);
-            mfma4(a[g], b[g]);
-        }
+        for (uint32_t g = 0; g < kStage; ++g) group(a[g], b[g], wrow + kb + 16u * g);
     };
     if (kfull > 0) {
         load_stage(a0, b0, 0);
@@ -158,34 +176,41 @@ __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
     }
     for (uint32_t k0 = kfull; k0 < d_in; k0 += 16) {      // K not a multiple of 128
         const f32x4_t a = *reinterpret_cast<const f32x4_t *>(xrow + k0);
-        f32x4_t b = *reinterpret_cast<const f32x4_t *>(wptr + k0);
-        if constexpr (kPert) perturb4(b, wrow + k0);
-        mfma4(a, b);
+        const f32x4_t b = *reinterpret_cast<const f32x4_t *>(wptr + k0);
+        group(a, b, wrow + k0);
     }
 
     // epilogue: column n = n0 + li, rows m0 + 4*kq + r
     const uint64_t b1_at = (uint64_t)d_hid * d_in;
     const uint64_t w2_at = b1_at + d_hid;
+    const uint64_t pset = (uint64_t)n_tiles * batch * d_out;   // one sign's partial logits
     const uint32_t n = n0 + li;
-    const float bias = param(params, b1_at + n, pa, kPert);
-    float g[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) g[r] = gelu_exact(acc[r] + bias);
-    for (uint32_t o = 0; o < d_out; ++o) {
-        const float w2 = param(params, w2_at + (uint64_t)o * d_hid + n, pa, kPert);
-        float p[4];
+    for (int sgn = 0; sgn < (kPair ? 2 : 1); ++sgn) {
+        PertArgs ps = pa;
+        if (sgn) ps.alpha = -pa.alpha;
+        const f32x4_t &c = sgn ? acc2 : acc;
+        double *out = partial + (uint64_t)sgn * pset;
+        const float bias = param(params, b1_at + n, ps, kPert);
+        float g[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = g[r] * w2;
-        // sum over the 16 columns of the tile (lanes with equal kq), fixed butterfly
+        for (int r = 0; r < 4; ++r) g[r] = gelu_exact(c[r] + bias);
+        for (uint32_t o = 0; o < d_out; ++o) {
+            const float w2 = param(params, w2_at + (uint64_t)o * d_hid + n, ps, kPert);
+            float p[4];
 #pragma unroll
-        for (int s = 8; s >= 1; s >>= 1) {
+            for (int r = 0; r < 4; ++r) p[r] = g[r] * w2;
+            // sum over the 16 columns of the tile (lanes with equal kq), fixed butterfly
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p[r] = p[r] + __shfl_xor(p[r], s, 16);
-        }
-        if (li == 0) {
+            for (int s = 8; s >= 1; s >>= 1) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                partial[((uint64_t)(m0 + 4u * kq + (uint32_t)r) * d_out + o) * n_tiles + nt] = (double)p[r];
+                for (int r = 0; r < 4; ++r) p[r] = p[r] + __shfl_xor(p[r], s, 16);
+            }
+            if (li == 0) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    out[((uint64_t)(m0 + 4u * kq + (uint32_t)r) * d_out + o) * n_tiles + nt] = (double)p[r];
+            }
         }
     }
 }
@@ -202,6 +227,10 @@ __global__ __launch_bounds__(256) void k_mlp_rows(const double *__restrict__ par
     const uint32_t m = blockIdx.x * 4u + (threadIdx.x >> 6);
     if (m >= batch) return;
     const uint32_t n_tiles = d_hid / 16;
+    // sign slot blockIdx.y (paired launch: 1 is the -alpha loss)
+    if (blockIdx.y) pa.alpha = -pa.alpha;
+    partial += (uint64_t)blockIdx.y * n_tiles * batch * d_out;
+    rowloss += (uint64_t)blockIdx.y * batch;
     const uint64_t b2_at = (uint64_t)d_hid * d_in + d_hid + (uint64_t)d_out * d_hid;
     double z[16];
     double zmax = -__builtin_inf();
@@ -225,9 +254,13 @@ __global__ __launch_bounds__(256) void k_mlp_rows(const double *__restrict__ par
 }
 
 __global__ __launch_bounds__(256) void k_mlp_mean(const double *__restrict__ rowloss,
-                                                  uint32_t batch, double *__restrict__ out)
+                                                  uint32_t batch, double *__restrict__ out,
+                                                  double *__restrict__ out2)
 {
     __shared__ double red[256];
+    // sign slot blockIdx.x (paired launch: 1 is the -alpha loss, written to out2)
+    rowloss += (uint64_t)blockIdx.x * batch;
+    if (blockIdx.x) out = out2;
     double acc = 0.0;
     for (uint32_t m = threadIdx.x; m < batch; m += blockDim.x) acc += rowloss[m];
     red[threadIdx.x] = acc;
@@ -239,13 +272,27 @@ __global__ __launch_bounds__(256) void k_mlp_mean(const double *__restrict__ row
     if (threadIdx.x == 0) *out = red[0] / (double)batch;
 }
 
+template <bool kPert, bool kPair>
+static void launch_chain(const float *params, const float *X, const int64_t *labels,
+                         uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out,
+                         double *partial, double *out, double *out2, const PertArgs &pa,
+                         hipStream_t stream)
+{
+    const uint32_t tiles = (batch / 16) * (d_hid / 16);
+    const uint32_t nsign = kPair ? 2u : 1u;
+    double *rowloss = partial + (uint64_t)nsign * (d_hid / 16) * batch * d_out;
+    hipLaunchKernelGGL((k_mlp_tiles<kPert, kPair>), dim3(tiles), dim3(64), 0, stream, X, params,
+                       batch, d_in, d_hid, d_out, partial, pa);
+    hipLaunchKernelGGL(k_mlp_rows<kPert>, dim3((batch + 3) / 4, nsign), dim3(256), 0, stream,
+                       partial, params, labels, batch, d_in, d_hid, d_out, rowloss, pa);
+    hipLaunchKernelGGL(k_mlp_mean, dim3(nsign), dim3(256), 0, stream, rowloss, batch, out, out2);
+}
+
 hipError_t launch_mlp_loss(const float *params, const float *X, const int64_t *labels,
                            uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out,
                            double *partial, double *out, const MlpPerturb *pert, Key key,
-                           hipStream_t stream)
+                           hipStream_t stream, double *out_minus)
 {
-    const uint32_t tiles = (batch / 16) * (d_hid / 16);
-    double *rowloss = partial + (uint64_t)(d_hid / 16) * batch * d_out;
     PertArgs pa{0, 0, 0, key.k0, key.k1, 0.0f, nullptr};
     if (pert) {
         pa.offset = pert->offset;
@@ -253,17 +300,16 @@ hipError_t launch_mlp_loss(const float *params, const float *X, const int64_t *l
         pa.probe = pert->probe;
         pa.alpha = pert->alpha;
         pa.bits = pert->bits;
-        hipLaunchKernelGGL(k_mlp_tiles<true>, dim3(tiles), dim3(64), 0, stream, X, params, batch,
-                           d_in, d_hid, d_out, partial, pa);
-        hipLaunchKernelGGL(k_mlp_rows<true>, dim3((batch + 3) / 4), dim3(256), 0, stream, partial,
-                           params, labels, batch, d_in, d_hid, d_out, rowloss, pa);
+        if (out_minus)
+            launch_chain<true, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, out,
+                                     out_minus, pa, stream);
+        else
+            launch_chain<true, false>(params, X, labels, batch, d_in, d_hid, d_out, partial, out,
+                                      nullptr, pa, stream);
     } else {
-        hipLaunchKernelGGL(k_mlp_tiles<false>, dim3(tiles), dim3(64), 0, stream, X, params, batch,
-                           d_in, d_hid, d_out, partial, pa);
-        hipLaunchKernelGGL(k_mlp_rows<false>, dim3((batch + 3) / 4), dim3(256), 0, stream, partial,
-                           params, labels, batch, d_in, d_hid, d_out, rowloss, pa);
+        launch_chain<false, false>(params, X, labels, batch, d_in, d_hid, d_out, partial, out,
+                                   nullptr, pa, stream);
     }
-    hipLaunchKernelGGL(k_mlp_mean, dim3(1), dim3(256), 0, stream, rowloss, batch, out);
     return hipGetLastError();
 }
 

@@ -55,7 +55,9 @@ hipError_t launch_lowrank_loss(const void *theta, bool bf16, const float *a, con
                                hipStream_t stream);
 
 // Two-layer MLP classifier loss (fp32 parameters, MFMA GEMM, fp64 reduction); with
-// `pert` the parameters are read as theta + alpha * z_probe without being written.
+// `pert` the parameters are read as theta + alpha * z_probe without being written, and with
+// `pert` and `out_minus` the loss at theta - alpha * z_probe goes to out_minus as well (the
+// workspace then holds both signs' partials).
 struct MlpPerturb {
     uint64_t offset;
     uint32_t step, probe;
@@ -65,6 +67,6 @@ struct MlpPerturb {
 hipError_t launch_mlp_loss(const float *params, const float *X, const int64_t *labels,
                            uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out,
                            double *partial, double *out, const MlpPerturb *pert, Key key,
-                           hipStream_t stream);
+                           hipStream_t stream, double *out_minus = nullptr);
 
 }  // namespace zo

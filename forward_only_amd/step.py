@@ -85,12 +85,14 @@ def spsa_step(ctx, theta: torch.Tensor, *, step: int, npert: int, eps: float, et
 
 def spsa_step_fused(ctx, theta: torch.Tensor, *, step: int, npert: int, eps: float, eta: float,
                     delta: float, loss_at, offset: int = 0, bits=None,
-                    buffers: dict | None = None) -> dict:
+                    buffers: dict | None = None, loss_pair_at=None) -> dict:
     """One step whose forward applies each probe while reading the parameters.
 
     loss_at(probe, alpha, row, out) writes the loss at theta + alpha * z_probe (probe None:
     the clean loss) into `out`; theta itself is only written by the update.  Used with
-    zo_mlp_loss_perturbed: no perturb or restore pass over the parameters at all.
+    zo_mlp_loss_perturbed: no perturb or restore pass over the parameters at all.  With
+    loss_pair_at(probe, alpha, row, out_plus, out_minus) (zo_mlp_loss_pair) each probe's two
+    losses come from one call.
     """
     a = applied_eps(eps)
     b = buffers if buffers is not None else {}
@@ -101,8 +103,11 @@ def spsa_step_fused(ctx, theta: torch.Tensor, *, step: int, npert: int, eps: flo
     loss_at(None, 0.0, None, L0)
     for i in range(npert):
         row = None if bits is None else bits[i]
-        loss_at(i, +a, row, Lp[i:i + 1])
-        loss_at(i, -a, row, Lm[i:i + 1])
+        if loss_pair_at is not None:
+            loss_pair_at(i, +a, row, Lp[i:i + 1], Lm[i:i + 1])
+        else:
+            loss_at(i, +a, row, Lp[i:i + 1])
+            loss_at(i, -a, row, Lm[i:i + 1])
     c = zo_probe_weights(ctx, Lp, Lm, L0, a, delta, out=b.get("c"))
     zo_update(ctx, theta, offset, step, c, eta, bits)
     return {"L0": L0, "Lp": Lp, "Lm": Lm, "c": c}

@@ -197,7 +197,8 @@ zo_status zo_lowrank_quad_loss(zo_ctx *ctx, const void *d_theta, zo_dtype dtype,
  * [0, d_out) (an out-of-range label makes the loss NaN).  The GEMM runs on MFMA in fp32;
  * the partial logits and the cross-entropy are reduced in fp64 in a fixed order
  * (deterministic).  d_workspace: device, 8-byte aligned, at least
- * zo_mlp_workspace_bytes(...) bytes, owned by the caller.  d_loss: device, one double.
+ * zo_mlp_workspace_bytes(...) bytes (enough for every MLP call, zo_mlp_loss_pair
+ * included), owned by the caller.  d_loss: device, one double.
  * Limits: batch, d_in, d_hid multiples of 16; 1 <= d_out <= 16.
  * Errors (ZO_EINVAL): NULL pointers, shapes outside the limits, misalignment, a workspace
  * that is too small. */
@@ -220,6 +221,21 @@ zo_status zo_mlp_loss_perturbed(zo_ctx *ctx, const float *d_params, uint64_t off
                                 const int64_t *d_labels, uint32_t batch, uint32_t d_in,
                                 uint32_t d_hid, uint32_t d_out, void *d_workspace,
                                 uint64_t workspace_bytes, double *d_loss, void *stream);
+
+/* Both losses of one probe, at theta + alpha * z_probe (into d_loss_plus) and at
+ * theta - alpha * z_probe (into d_loss_minus), in one launch sequence: each parameter is
+ * loaded once and read with both signs.  Each result equals zo_mlp_loss_perturbed with
+ * +alpha resp. -alpha bit for bit (the two accumulations are independent and ordered as
+ * in the single call), so a step's central differences cost n_pert forward launches
+ * instead of 2*n_pert.  d_loss_plus, d_loss_minus: device, one double each.  Other
+ * arguments as zo_mlp_loss_perturbed; errors as there, plus ZO_EINVAL for a NULL
+ * d_loss_minus. */
+zo_status zo_mlp_loss_pair(zo_ctx *ctx, const float *d_params, uint64_t offset, uint32_t step,
+                           uint32_t probe, float alpha, const uint8_t *d_bits, const float *d_X,
+                           const int64_t *d_labels, uint32_t batch, uint32_t d_in,
+                           uint32_t d_hid, uint32_t d_out, void *d_workspace,
+                           uint64_t workspace_bytes, double *d_loss_plus, double *d_loss_minus,
+                           void *stream);
 
 #ifdef __cplusplus
 }

@@ -87,6 +87,47 @@ def test_fused_perturbation_equals_perturb_then_forward(ctx, shape, mode):
     assert np.array_equal(t.cpu().numpy(), theta)          # parameters untouched
 
 
+@pytest.mark.parametrize("shape", [(16, 16, 16, 2), (32, 48, 64, 3), (48, 144, 128, 16),
+                                   (128, 768, 3072, 2)])
+@pytest.mark.parametrize("mode", ["regen", "bits"])
+def test_pair_equals_two_fused_calls(ctx, shape, mode):
+    """zo_mlp_loss_pair gives exactly the two single fused losses (+alpha, -alpha), in
+    both bit modes and with K not a multiple of the kernel's 128-wide stages; the
+    parameters stay untouched."""
+    batch, d_in, d_hid, d_out = shape
+    theta, X, y = _problem(*shape, seed=31 + sum(shape))
+    t, x, yl = _dev(theta, X, y)
+    M = theta.size
+    for probe, alpha in ((0, 1e-3), (6, 2.0 ** -7), (9, -3e-3)):
+        bits = zo.zo_gen_probes(ctx, 4, probe, 1, 0, M)[0] if mode == "bits" else None
+        lp, lm = zo.zo_mlp_loss_pair(ctx, t, 0, 4, probe, alpha, x, yl, d_hid, d_out,
+                                     bits=bits)
+        sp = zo.zo_mlp_loss_perturbed(ctx, t, 0, 4, probe, alpha, x, yl, d_hid, d_out,
+                                      bits=bits).item()
+        sm = zo.zo_mlp_loss_perturbed(ctx, t, 0, 4, probe, -alpha, x, yl, d_hid, d_out,
+                                      bits=bits).item()
+        assert (lp.item(), lm.item()) == (sp, sm), (probe, alpha, lp.item(), lm.item(), sp, sm)
+    assert np.array_equal(t.cpu().numpy(), theta)
+
+
+def test_pair_argument_checks(ctx):
+    theta, X, y = _problem(16, 16, 16, 2, seed=1)
+    t, x, yl = _dev(theta, X, y)
+    M = theta.size
+    L = zo._lib.lib()
+    ws = torch.empty(zo.zo_mlp_workspace_bytes(16, 16, 16, 2), dtype=torch.uint8, device="cuda")
+    out = torch.empty(2, dtype=torch.float64, device="cuda")
+    args = lambda minus, offset=0, wbytes=ws.numel(): L.zo_mlp_loss_pair(  # noqa: E731
+        ctx.handle, t.data_ptr(), offset, 0, 0, 1e-3, None, x.data_ptr(), yl.data_ptr(), 16, 16,
+        16, 2, ws.data_ptr(), wbytes, out.data_ptr(), minus, None)
+    assert args(None) == zo.ZO_EINVAL                                    # no -alpha output
+    assert args(out.data_ptr() + 8, offset=64) == zo.ZO_EINVAL           # offset % 128 != 0
+    assert args(out.data_ptr() + 8, wbytes=ws.numel() // 2 - 8) == zo.ZO_EINVAL  # workspace
+    assert args(out.data_ptr() + 8) == zo.ZO_OK
+    torch.cuda.synchronize()
+    assert M == t.numel()
+
+
 def test_mlp_argument_checks(ctx):
     theta8, X8, y8 = _problem(16, 8, 16, 2, seed=2)
     with pytest.raises(zo.ZOError) as e:
@@ -100,6 +141,43 @@ def test_mlp_argument_checks(ctx):
     ws = torch.empty(8, dtype=torch.uint8, device="cuda")
     with pytest.raises(zo.ZOError):
         zo.zo_mlp_loss(ctx, t, x, yl, 16, 2, workspace=ws)             # workspace too small
+
+
+def test_pair_step_equals_single_call_step():
+    """A whole MLP-workload step with paired forwards equals the step with single fused
+    forwards bit for bit: losses, weights and the updated parameters."""
+    cfg = CONFIGS["mlp"]
+    e = cfg.extra
+    npert, step = 32, 3
+    theta, _ = gen.theta_and_a(cfg)
+    X, y = gen.mlp_data(cfg)
+    x, yl = to_dev_f32(X), torch.from_numpy(y).cuda()
+    results = []
+    for paired in (False, True):
+        local = zo.zo_init(cfg.seed)
+        t = to_dev_f32(theta)
+        ws = torch.empty(zo.zo_mlp_workspace_bytes(e["batch"], e["d_in"], e["d_hid"],
+                                                   e["d_out"]), dtype=torch.uint8, device="cuda")
+
+        def loss_at(probe, alpha, row, out):
+            if probe is None:
+                zo.zo_mlp_loss(local, t, x, yl, e["d_hid"], e["d_out"], workspace=ws, out=out)
+            else:
+                zo.zo_mlp_loss_perturbed(local, t, 0, step, probe, alpha, x, yl, e["d_hid"],
+                                         e["d_out"], bits=row, workspace=ws, out=out)
+
+        def pair_at(probe, alpha, row, op, om):
+            zo.zo_mlp_loss_pair(local, t, 0, step, probe, alpha, x, yl, e["d_hid"], e["d_out"],
+                                bits=row, workspace=ws, out_plus=op, out_minus=om)
+
+        out = spsa_step_fused(local, t, step=step, npert=npert, eps=cfg.eps, eta=cfg.eta,
+                              delta=cfg.delta, loss_at=loss_at,
+                              loss_pair_at=pair_at if paired else None)
+        results.append((out["Lp"].cpu().numpy(), out["Lm"].cpu().numpy(),
+                        out["c"].cpu().numpy(), t.cpu().numpy()))
+        local.close()
+    for a, b in zip(*results):
+        assert np.array_equal(a, b)
 
 
 @pytest.mark.parametrize("mode", ["bits", "regen"])
