@@ -21,6 +21,14 @@ inline zo::Key key_of(const zo_ctx *c) { return {(uint32_t)c->seed, (uint32_t)(c
 
 inline hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
 
+// A usable context: non-null, and its device is the current one (its counter and scratch
+// live there; a launch on another device would address them on the wrong GPU).
+inline bool ctx_ok(const zo_ctx *c)
+{
+    int dev = -1;
+    return c && hipGetDevice(&dev) == hipSuccess && dev == c->device;
+}
+
 inline zo_status from_hip(hipError_t e) { return e == hipSuccess ? ZO_OK : ZO_EHIP; }
 
 // Common checks for a parameter range [offset, offset + n).
@@ -101,7 +109,7 @@ uint64_t zo_get_seed(const zo_ctx *c) { return c ? c->seed : 0; }
 zo_status zo_gen_probes(zo_ctx *c, uint32_t step, uint32_t probe0, uint32_t n_probes,
                         uint64_t offset, uint64_t n, uint8_t *d_bits, void *stream)
 {
-    if (!c) return ZO_EINVAL;
+    if (!ctx_ok(c)) return ZO_EINVAL;
     if (!range_ok(offset, n)) return ZO_EINVAL;
     if (n == 0 || n_probes == 0) return ZO_OK;
     if (!d_bits || !aligned16(d_bits)) return ZO_EINVAL;
@@ -113,7 +121,7 @@ zo_status zo_perturb(zo_ctx *c, void *d_theta, zo_dtype dtype, uint64_t offset, 
                      uint32_t step, uint32_t probe, float alpha, const uint8_t *d_bits,
                      void *stream)
 {
-    if (!c) return ZO_EINVAL;
+    if (!ctx_ok(c)) return ZO_EINVAL;
     if (dtype != ZO_FP32 && dtype != ZO_BF16) return ZO_EINVAL;
     if (!range_ok(offset, n)) return ZO_EINVAL;
     if (n == 0) return ZO_OK;
@@ -128,7 +136,7 @@ zo_status zo_perturb2(zo_ctx *c, void *d_theta, zo_dtype dtype, uint64_t offset,
                       float alpha_b, const uint8_t *d_bits_a, const uint8_t *d_bits_b,
                       void *stream)
 {
-    if (!c) return ZO_EINVAL;
+    if (!ctx_ok(c)) return ZO_EINVAL;
     if (dtype != ZO_FP32 && dtype != ZO_BF16) return ZO_EINVAL;
     if (!range_ok(offset, n)) return ZO_EINVAL;
     if ((d_bits_a == nullptr) != (d_bits_b == nullptr)) return ZO_EINVAL;
@@ -144,7 +152,7 @@ zo_status zo_probe_weights(zo_ctx *c, const double *d_Lp, const double *d_Lm,
                            const double *d_L0, uint32_t n_pert, double eps, double delta,
                            float *d_c, void *stream)
 {
-    if (!c) return ZO_EINVAL;
+    if (!ctx_ok(c)) return ZO_EINVAL;
     if (!(eps == eps) || eps == 0.0 || eps - eps != 0.0) return ZO_EINVAL;       // NaN/0/inf
     if (!(delta >= 0.0) || delta - delta != 0.0) return ZO_EINVAL;               // <0/NaN/inf
     if (n_pert == 0) return ZO_OK;
@@ -157,7 +165,7 @@ zo_status zo_probe_weights_ex(zo_ctx *c, const double *d_Lp, const double *d_Lm,
                               const double *d_L0, uint32_t n_pert, double eps, double delta,
                               zo_weights_mode mode, double power, float *d_c, void *stream)
 {
-    if (!c) return ZO_EINVAL;
+    if (!ctx_ok(c)) return ZO_EINVAL;
     if (mode != ZO_WEIGHTS_PRECOND && mode != ZO_WEIGHTS_POWER && mode != ZO_WEIGHTS_SPSA_MEAN)
         return ZO_EINVAL;
     if (!(eps == eps) || eps == 0.0 || eps - eps != 0.0) return ZO_EINVAL;
@@ -174,7 +182,7 @@ zo_status zo_update(zo_ctx *c, void *d_theta, zo_dtype dtype, uint64_t offset, u
                     uint32_t step, const float *d_c, uint32_t n_pert, float eta,
                     const uint8_t *d_bits, void *stream)
 {
-    if (!c) return ZO_EINVAL;
+    if (!ctx_ok(c)) return ZO_EINVAL;
     if (dtype != ZO_FP32 && dtype != ZO_BF16) return ZO_EINVAL;
     if (!range_ok(offset, n)) return ZO_EINVAL;
     if (n_pert > ZO_MAX_NPERT) return ZO_EUNSUPPORTED;
@@ -187,7 +195,7 @@ zo_status zo_update(zo_ctx *c, void *d_theta, zo_dtype dtype, uint64_t offset, u
 
 zo_status zo_nonfinite_count(zo_ctx *c, void *stream, uint32_t *out)
 {
-    if (!c || !out) return ZO_EINVAL;
+    if (!ctx_ok(c) || !out) return ZO_EINVAL;
     if (hipStreamSynchronize(as_stream(stream)) != hipSuccess) return ZO_EHIP;
     uint32_t v = 0;
     if (hipMemcpy(&v, c->d_counter, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess)
@@ -198,14 +206,14 @@ zo_status zo_nonfinite_count(zo_ctx *c, void *stream, uint32_t *out)
 
 zo_status zo_reset_nonfinite(zo_ctx *c, void *stream)
 {
-    if (!c) return ZO_EINVAL;
+    if (!ctx_ok(c)) return ZO_EINVAL;
     return from_hip(zo::launch_zero_u32(c->d_counter, 1, as_stream(stream)));
 }
 
 zo_status zo_quad_loss(zo_ctx *c, const void *d_theta, zo_dtype dtype, const float *d_a,
                        uint64_t n, double *d_out, void *stream)
 {
-    if (!c || !d_out) return ZO_EINVAL;
+    if (!ctx_ok(c) || !d_out) return ZO_EINVAL;
     if (dtype != ZO_FP32 && dtype != ZO_BF16) return ZO_EINVAL;
     if (n > 0 && (!d_theta || !d_a || !aligned16(d_theta) || !aligned16(d_a))) return ZO_EINVAL;
     return from_hip(zo::launch_quad_loss(d_theta, dtype == ZO_BF16, d_a, n, c->d_partials, d_out,
@@ -216,7 +224,7 @@ zo_status zo_lowrank_quad_loss(zo_ctx *c, const void *d_theta, zo_dtype dtype,
                                const float *d_a, const float *d_U, uint32_t r, uint64_t n,
                                double *d_out, void *stream)
 {
-    if (!c || !d_out) return ZO_EINVAL;
+    if (!ctx_ok(c) || !d_out) return ZO_EINVAL;
     if (dtype != ZO_FP32 && dtype != ZO_BF16) return ZO_EINVAL;
     if (r > zo::kLowRankMax) return ZO_EUNSUPPORTED;
     if (n > 0 && (!d_theta || !d_a || !aligned16(d_theta) || !aligned16(d_a))) return ZO_EINVAL;
@@ -237,7 +245,8 @@ static zo_status mlp_checks(zo_ctx *c, const float *d_params, const float *d_X,
                             uint32_t d_hid, uint32_t d_out, void *d_workspace,
                             uint64_t workspace_bytes, double *d_loss)
 {
-    if (!c || !d_params || !d_X || !d_labels || !d_workspace || !d_loss) return ZO_EINVAL;
+    if (!ctx_ok(c) || !d_params || !d_X || !d_labels || !d_workspace || !d_loss)
+        return ZO_EINVAL;
     if (batch == 0 || d_in == 0 || d_hid == 0 || batch % 16u || d_in % 16u || d_hid % 16u)
         return ZO_EINVAL;
     if (d_out == 0 || d_out > 16u) return ZO_EINVAL;
