@@ -181,7 +181,7 @@ def update_roofline(M: int, n: int, pass_bytes: float, upd_ms):
         return None
     calls = M * n / 128.0 / (upd_ms * 1e-3)
     peak = stored_philox_peak()
-    return {"kernel": "k_update", "bound": "lds",
+    return {"kernel": "k_update", "bound": "valu+lds",
             "achieved_GBps": pass_bytes / (upd_ms * 1e-3) / 1e9,
             "hbm_frac": pass_bytes / (upd_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
             "probe_params_per_s": n * M / (upd_ms * 1e-3),
