@@ -2,9 +2,9 @@
 
 A thin Python face over libzo.so (include/zo.h).  Each function below has the name of the
 C entry point it calls and only marshals arguments: it checks that tensors live on the
-GPU with the expected dtype, contiguity and alignment, then passes their device pointers
-and torch's current HIP stream.  All arithmetic runs in the library's HIP kernels;
-there is no CPU path.
+current GPU with the expected dtype and are contiguous, then passes their device pointers
+and torch's current HIP stream (the library itself rejects misaligned pointers and bad
+sizes).  All arithmetic runs in the library's HIP kernels; there is no CPU path.
 
     ctx = zo_init(seed)
     zo_perturb(ctx, theta, offset, step, probe, +eps)      # theta + eps*z_probe, in place
@@ -25,10 +25,10 @@ from ._lib import (ZO_BF16, ZO_EHIP, ZO_EINVAL, ZO_ENOMEM, ZO_EUNSUPPORTED, ZO_F
 
 __all__ = [
     "Context", "ZOError", "zo_init", "zo_destroy", "zo_bits_stride", "zo_gen_probes",
-    "zo_perturb", "zo_perturb2", "zo_probe_weights", "zo_probe_weights_ex", "zo_update", "zo_nonfinite_count",
-    "zo_reset_nonfinite", "zo_quad_loss", "zo_lowrank_quad_loss", "zo_mlp_workspace_bytes",
-    "zo_mlp_loss",
-    "zo_mlp_loss_perturbed", "zo_mlp_loss_pair", "library_path",
+    "zo_perturb", "zo_perturb2", "zo_probe_weights", "zo_probe_weights_ex", "zo_update",
+    "zo_nonfinite_count", "zo_reset_nonfinite", "zo_quad_loss", "zo_lowrank_quad_loss",
+    "zo_mlp_workspace_bytes", "zo_mlp_loss", "zo_mlp_loss_perturbed", "zo_mlp_loss_pair",
+    "library_path",
 ]
 
 
@@ -79,6 +79,9 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if t.device.index is not None and t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, not on the current device "
+                         f"cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
