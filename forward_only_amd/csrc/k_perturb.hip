@@ -5,7 +5,13 @@
 //
 // Layout and mapping (gfx950, wave64):
 //  * A wave owns a chunk of 64 Philox blocks = 8192 consecutive params per iteration
-//    (16 KiB of bf16, 32 KiB of fp32) and walks the buffer grid-stride.
+//    (16 KiB of bf16, 32 KiB of fp32).  The chunks are split into eight contiguous
+//    ranges, one per XCD: workgroups are dispatched to the XCDs round-robin, so workgroup
+//    b (on XCD b % 8) walks range b % 8 grid-stride with the other workgroups of its XCD.
+//    Each XCD then streams through its own eighth of the buffer (its L2 and address
+//    translation see one compact window instead of every XCD touching every window);
+//    on MI355X this is worth 3-5% of in-place bandwidth.  The split is a plain partition
+//    of the chunks, so results do not depend on where workgroups actually run.
 //  * Each lane issues its 16 (bf16) or 32 (fp32) global_load_dwordx4 first; load k of
 //    lane L covers 16 bytes at chunk + 1 KiB*k + 16*L, so every load instruction moves
 //    one contiguous KiB per wave.
@@ -56,9 +62,13 @@ __global__ __launch_bounds__(256) void k_perturb_chunks(u32x4_t *__restrict__ th
     u32x4_t *xb = xch_all[wv][kProbes - 1];
     const uint8_t *ba = reinterpret_cast<const uint8_t *>(xa);
     const uint8_t *bb = reinterpret_cast<const uint8_t *>(xb);
-    const uint64_t nwaves = (uint64_t)gridDim.x * kWavesPerWG;
+    // XCD range of this workgroup (gridDim.x is a multiple of 8)
+    const uint32_t xcd = blockIdx.x & 7u;
+    const uint64_t nwaves = (uint64_t)(gridDim.x >> 3) * kWavesPerWG;
+    const uint64_t ch_end = nchunks * (xcd + 1) / 8;
 
-    for (uint64_t ch = (uint64_t)blockIdx.x * kWavesPerWG + wv; ch < nchunks; ch += nwaves) {
+    for (uint64_t ch = nchunks * xcd / 8 + (uint64_t)(blockIdx.x >> 3) * kWavesPerWG + wv;
+         ch < ch_end; ch += nwaves) {
         u32x4_t *base = theta + ch * (uint64_t)(kChunkParams / kPerLoad) + lane;
         u32x4_t v[kLoads];
 #pragma unroll
@@ -174,10 +184,12 @@ static hipError_t perturb_impl(void *theta, uint64_t n, uint64_t blk0, uint32_t 
     const uint64_t nchunks = n / kChunkParams;
     if (nchunks) {
         // Persistent grid: a few resident workgroups per CU, each wave loops over chunks.
+        // The grid is a multiple of 8 (one share per XCD range); workgroups past the work
+        // of their range exit at once.
         static const int wg_per_cu = env_int("ZO_PERTURB_WG_PER_CU", 8);
         const uint64_t want = (nchunks + kWavesPerWG - 1) / kWavesPerWG;
         const uint64_t cap = (uint64_t)num_cus * wg_per_cu;
-        const uint32_t grid = (uint32_t)(want < cap ? want : cap);
+        const uint32_t grid = (uint32_t)(((want < cap ? want : cap) + 7) / 8 * 8);
         hipLaunchKernelGGL((k_perturb_chunks<kBF16, kBits, kTwo>), dim3(grid), dim3(256), 0,
                            stream, static_cast<u32x4_t *>(theta), nchunks, blk0, step, probe_a,
                            probe_b, key.k0, key.k1, abits, bbits,
