@@ -343,6 +343,21 @@ def main(argv=None):
               record)
         timed("update", lambda: zo.zo_update(ctx, theta, 0, s, c_buf, cfg.eta), record)
 
+    # The in-place ceiling of the memory theta landed on (a large buffer's bandwidth depends
+    # on its physical placement): a pass that reads and writes back theta unchanged, in the
+    # perturb kernel's order, timed before the warmup.
+    placement_gbps = None
+    if mlp is None:
+        zo.zo_stream_rmw(ctx, theta)
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(3):
+            zo.zo_stream_rmw(ctx, theta)
+        e1.record()
+        torch.cuda.synchronize()
+        placement_gbps = 2.0 * esize * M / (e0.elapsed_time(e1) / 3 * 1e-3) / 1e9
+        log(f"[bench] in-place ceiling of theta's memory: {placement_gbps:.0f} GB/s")
+
     for s in range(W):
         one_step(s, False)
         torch.cuda.synchronize()
@@ -429,7 +444,10 @@ def main(argv=None):
                                            f"every zo_perturb / zo_perturb2 pass)",
                                  "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
                                  "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                                 "traffic": traffic},
+                                 "traffic": traffic,
+                                 "placement_ceiling": placement_gbps,
+                                 "frac_of_placement_ceiling": (achieved / placement_gbps
+                                                               if placement_gbps else None)},
         "update_roofline": update_roofline(M, n, pass_bytes, upd_ms),
         "nonfinite_probes": nonfinite,
         "cpu_baseline": cpu,

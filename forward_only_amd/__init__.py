@@ -28,7 +28,7 @@ __all__ = [
     "zo_perturb", "zo_perturb2", "zo_probe_weights", "zo_probe_weights_ex", "zo_update",
     "zo_nonfinite_count", "zo_reset_nonfinite", "zo_quad_loss", "zo_lowrank_quad_loss",
     "zo_mlp_workspace_bytes", "zo_mlp_loss", "zo_mlp_loss_perturbed", "zo_mlp_loss_pair",
-    "library_path",
+    "zo_stream_rmw", "library_path",
 ]
 
 
@@ -312,3 +312,12 @@ def zo_mlp_loss_pair(ctx: Context, params: torch.Tensor, offset: int, step: int,
         d_out, pw, wbytes, _dev(out_plus, "out_plus", torch.float64),
         _dev(out_minus, "out_minus", torch.float64), _stream(stream)), "zo_mlp_loss_pair")
     return out_plus, out_minus
+
+
+def zo_stream_rmw(ctx: Context, buf: torch.Tensor, mask: int = 0, stream=None) -> None:
+    """Diagnostic: every 32-bit word of `buf` <- word ^ mask in place, in the perturb
+    kernel's streaming order (mask 0: unchanged; timed, the in-place bandwidth ceiling of
+    the memory `buf` occupies)."""
+    nbytes = buf.numel() * buf.element_size()
+    _lib.check(_lib.lib().zo_stream_rmw(ctx.handle, _dev(buf, "buf"), nbytes, int(mask) & 0xFFFFFFFF,
+                                        _stream(stream)), "zo_stream_rmw")

@@ -46,6 +46,7 @@ SIGNATURES = {
                                      _u32, _u32, _u32, _vp, _u64, _vp, _vp]),
     "zo_mlp_loss_pair": (_int, [_vp, _vp, _u64, _u32, _u32, _f32, _vp, _vp, _vp, _u32,
                                 _u32, _u32, _u32, _vp, _u64, _vp, _vp, _vp]),
+    "zo_stream_rmw": (_int, [_vp, _vp, _u64, _u32, _vp]),
 }
 
 _lock = threading.Lock()

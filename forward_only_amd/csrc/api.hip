@@ -306,4 +306,12 @@ zo_status zo_mlp_loss_pair(zo_ctx *c, const float *d_params, uint64_t offset, ui
                                         key_of(c), as_stream(stream), d_loss_minus));
 }
 
+zo_status zo_stream_rmw(zo_ctx *c, void *d_buf, uint64_t bytes, uint32_t mask, void *stream)
+{
+    if (!ctx_ok(c)) return ZO_EINVAL;
+    if (bytes == 0) return ZO_OK;
+    if (!d_buf || !aligned16(d_buf) || bytes % 16u) return ZO_EINVAL;
+    return from_hip(zo::launch_stream_rmw(d_buf, bytes, mask, c->num_cus, as_stream(stream)));
+}
+
 }  // extern "C"

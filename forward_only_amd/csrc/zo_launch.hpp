@@ -69,4 +69,8 @@ hipError_t launch_mlp_loss(const float *params, const float *X, const int64_t *l
                            double *partial, double *out, const MlpPerturb *pert, Key key,
                            hipStream_t stream, double *out_minus = nullptr);
 
+// Diagnostic: every 16-byte word of buf (bytes % 16 == 0) <- word ^ mask, in place.
+hipError_t launch_stream_rmw(void *buf, uint64_t bytes, uint32_t mask, int num_cus,
+                             hipStream_t stream);
+
 }  // namespace zo

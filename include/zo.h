@@ -242,6 +242,17 @@ zo_status zo_mlp_loss_pair(zo_ctx *ctx, const float *d_params, uint64_t offset, 
                            uint64_t workspace_bytes, double *d_loss_plus, double *d_loss_minus,
                            void *stream);
 
+/* Diagnostic, not a step of the method: every 32-bit word of d_buf becomes word ^ mask,
+ * in place, streaming in the same order as zo_perturb (mask = 0 leaves the buffer
+ * unchanged; a non-zero mask makes the pass checkable).  The bandwidth of this call on a
+ * parameter buffer (2 * bytes / time) is the in-place read-modify-write ceiling of the
+ * physical memory that buffer occupies; a large buffer's ceiling varies with where the
+ * allocation lands, so a benchmark can judge zo_perturb against it on the very buffer it
+ * times.  d_buf: device, 16-byte aligned, bytes a multiple of 16 (other kernels must not
+ * use d_buf concurrently).  Errors (ZO_EINVAL): NULL ctx, NULL or misaligned d_buf with
+ * bytes > 0, bytes not a multiple of 16. */
+zo_status zo_stream_rmw(zo_ctx *ctx, void *d_buf, uint64_t bytes, uint32_t mask, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

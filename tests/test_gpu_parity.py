@@ -446,3 +446,31 @@ def test_probe_weights_ex(ctx, mode, power, n):
         assert np.all(np.abs(c.astype(np.float64) - ref) <= np.spacing(np.abs(ref)))
     else:
         assert np.array_equal(c.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("nbytes", [16, 16384 - 16, 16384, (1 << 20) + 48, (64 << 20) + 16])
+def test_stream_rmw(ctx, nbytes):
+    """The diagnostic in-place streaming pass touches every word exactly once: a non-zero
+    mask flips every word of whole chunks and the ragged tail alike, flipping again restores
+    them, and mask 0 leaves arbitrary bit patterns (NaN payloads, denormals, negative zero)
+    identical."""
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(0, 2 ** 32, nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    host[:4] = [0x7FC00001, 0x80000000, 0x00000001, 0xFF800000]
+    buf = torch.from_numpy(host.view(np.int32).copy()).cuda()
+    mask = 0xA5C3F00F
+    zo.zo_stream_rmw(ctx, buf, mask)
+    torch.cuda.synchronize()
+    assert np.array_equal(buf.cpu().numpy().view(np.uint32), host ^ np.uint32(mask))
+    zo.zo_stream_rmw(ctx, buf, mask)
+    zo.zo_stream_rmw(ctx, buf)
+    torch.cuda.synchronize()
+    assert np.array_equal(buf.cpu().numpy().view(np.uint32), host)
+
+
+def test_stream_rmw_argument_checks(ctx):
+    L = zo._lib.lib()
+    t = torch.zeros(64, dtype=torch.int32, device="cuda")
+    assert L.zo_stream_rmw(ctx.handle, t.data_ptr(), 20, 0, None) == zo.ZO_EINVAL      # size % 16
+    assert L.zo_stream_rmw(ctx.handle, t.data_ptr() + 4, 16, 0, None) == zo.ZO_EINVAL  # alignment
+    assert L.zo_stream_rmw(ctx.handle, None, 0, 0, None) == zo.ZO_OK                    # empty

@@ -59,6 +59,9 @@ def test_null_context_and_arguments_are_rejected():
     assert L.zo_probe_weights(None, None, None, None, 1, 1e-3, 0.0, None, None) == _lib.ZO_EINVAL
     v = ctypes.c_uint32()
     assert L.zo_nonfinite_count(None, None, ctypes.byref(v)) == _lib.ZO_EINVAL
+    assert L.zo_stream_rmw(None, None, 16, 0, None) == _lib.ZO_EINVAL
+    assert L.zo_mlp_loss_pair(None, None, 0, 0, 0, 1.0, None, None, None, 16, 16, 16, 2, None,
+                              0, None, None, None) == _lib.ZO_EINVAL
 
 
 def test_init_without_gpu_fails_cleanly():
