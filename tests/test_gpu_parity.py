@@ -69,8 +69,13 @@ def test_gen_probes_plane_125m(ctx):
 # ------------------------------------------------------------------------------------
 # perturb
 # ------------------------------------------------------------------------------------
+# 8192 params form one chunk of the streaming kernel, and the chunks are split into eight
+# per-XCD ranges: the cases cover no whole chunk, 1, 3, 7, 9 and 13 chunks (ranges left
+# empty, a grid rounded up to a multiple of 8), 512, and 8205 chunks (more than the 8192
+# waves of the grid, not a multiple of 8), each with and without a ragged tail.
 PERTURB_CASES = [(4096, 0), (8192, 128), (8192 * 3 + 1000, 0), (1, 256), (127, 0),
-                 (8192 * 9 + 8191, 128 * 5), (1 << 22, 0)]
+                 (8192 * 7, 128 * 3), (8192 * 9 + 8191, 128 * 5), (8192 * 13 + 5, 0),
+                 (1 << 22, 0), (8192 * 8205 + 77, 128)]
 
 
 @pytest.mark.parametrize("kind", ["f32", "bf16"])
@@ -448,7 +453,8 @@ def test_probe_weights_ex(ctx, mode, power, n):
         assert np.array_equal(c.view(np.uint32), ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("nbytes", [16, 16384 - 16, 16384, (1 << 20) + 48, (64 << 20) + 16])
+@pytest.mark.parametrize("nbytes", [16, 16384 - 16, 16384, 16384 * 13 + 32, (1 << 20) + 48,
+                                    (64 << 20) + 16, 16384 * 8205 + 48])
 def test_stream_rmw(ctx, nbytes):
     """The diagnostic in-place streaming pass touches every word exactly once: a non-zero
     mask flips every word of whole chunks and the ragged tail alike, flipping again restores
