@@ -247,7 +247,7 @@ zo_status zo_mlp_loss_pair(zo_ctx *ctx, const float *d_params, uint64_t offset, 
  * unchanged; a non-zero mask makes the pass checkable).  The bandwidth of this call on a
  * parameter buffer (2 * bytes / time) is the in-place read-modify-write ceiling of the
  * physical memory that buffer occupies; a large buffer's ceiling varies with where the
- * allocation lands, so a benchmark can judge zo_perturb against it on the very buffer it
+ * allocation lands, so a benchmark can compare zo_perturb with it on the very buffer it
  * times.  d_buf: device, 16-byte aligned, bytes a multiple of 16 (other kernels must not
  * use d_buf concurrently).  Errors (ZO_EINVAL): NULL ctx, NULL or misaligned d_buf with
  * bytes > 0, bytes not a multiple of 16. */
