@@ -7,9 +7,10 @@ parameters and at theta +/- eps*z_i for each of n_pert probes, moving the parame
 place between evaluations, then forms the probe weights from the 2 n_pert + 1 losses and
 makes one update pass theta <- theta - eta * sum_i c_i z_i.  Schedules of the in-place
 moves: S2f (default) -- +eps z_0, then per probe -2 eps z_i and one fused pass restoring
-probe i and applying +eps z_(i+1): 2 n_pert + 1 passes; S4 -- +eps, restore, -eps,
-restore per probe: 4 n_pert passes.  Probes are regenerated from the counter-based
-generator in every pass (nothing stored).
+probe i and applying +eps z_(i+1), the last probe's restore folded into the update pass:
+2 n_pert passes + the update; S4 -- +eps, restore, -eps, restore per probe: 4 n_pert
+passes + the update.  Probes are regenerated from the counter-based generator in every
+pass (nothing stored).
 
 Default workload: an OPT-30B-shaped bf16 parameter set (48 layers, d = 7168, FFN 28672,
 vocab 50272: 29,959,831,552 params, 59.9 GB) updated in place, n_pert = 160, eps = 1e-3;
@@ -337,11 +338,14 @@ def main(argv=None):
                 if i + 1 < n:
                     timed("perturb2",
                           lambda: zo.zo_perturb2(ctx, theta, 0, s, i, +a, i + 1, +a), record)
-                else:
-                    timed("perturb", lambda: zo.zo_perturb(ctx, theta, 0, s, i, +a), record)
         timed("weights", lambda: zo.zo_probe_weights(ctx, Lp, Lm, L0, a, cfg.delta, out=c_buf),
               record)
-        timed("update", lambda: zo.zo_update(ctx, theta, 0, s, c_buf, cfg.eta), record)
+        if args.schedule == "S2f":
+            # the last probe's restore rides on the update pass
+            timed("update", lambda: zo.zo_restore_update(ctx, theta, 0, s, n - 1, +a, c_buf,
+                                                         cfg.eta), record)
+        else:
+            timed("update", lambda: zo.zo_update(ctx, theta, 0, s, c_buf, cfg.eta), record)
 
     # The in-place ceiling of the memory theta landed on (a large buffer's bandwidth depends
     # on its physical placement): a pass that reads and writes back theta unchanged, in the
@@ -383,7 +387,7 @@ def main(argv=None):
     value = n * M / T
     # every pass of either perturb entry point runs k_perturb_chunks (one or two probes)
     pert_ms, upd_ms, w_ms = avg_ms("perturb", "perturb2"), avg_ms("update"), avg_ms("weights")
-    passes = 0 if mlp is not None else (4 * n if args.schedule == "S4" else 2 * n + 1)
+    passes = 0 if mlp is not None else (4 * n if args.schedule == "S4" else 2 * n)
     pass_bytes = 2.0 * esize * M                      # one read + one write of theta
     step_bytes = (passes + 1) * pass_bytes            # the passes + the update
     if mlp is not None:
@@ -427,7 +431,9 @@ def main(argv=None):
                                 f"n_pert={n}, eps={cfg.eps}, eta={cfg.eta}, " +
                                 ("probes applied inside the MFMA forward, both signs per "
                                  "launch (no passes over theta) + update" if mlp is not None else
-                                 f"schedule {args.schedule} ({passes} passes + update)") +
+                                 f"schedule {args.schedule} ({passes} passes + update" +
+                                 (" carrying the last restore)" if args.schedule == "S2f"
+                                  else ")")) +
                                 ", probes regenerated, losses " +
                                 ("synthetic" if cfg.loss == "synthetic" else cfg.loss)),
                    "params": M, "n_pert": n,

@@ -26,9 +26,9 @@ from ._lib import (ZO_BF16, ZO_EHIP, ZO_EINVAL, ZO_ENOMEM, ZO_EUNSUPPORTED, ZO_F
 __all__ = [
     "Context", "ZOError", "zo_init", "zo_destroy", "zo_bits_stride", "zo_gen_probes",
     "zo_perturb", "zo_perturb2", "zo_probe_weights", "zo_probe_weights_ex", "zo_update",
-    "zo_nonfinite_count", "zo_reset_nonfinite", "zo_quad_loss", "zo_lowrank_quad_loss",
-    "zo_mlp_workspace_bytes", "zo_mlp_loss", "zo_mlp_loss_perturbed", "zo_mlp_loss_pair",
-    "zo_stream_rmw", "library_path",
+    "zo_restore_update", "zo_nonfinite_count", "zo_reset_nonfinite", "zo_quad_loss",
+    "zo_lowrank_quad_loss", "zo_mlp_workspace_bytes", "zo_mlp_loss", "zo_mlp_loss_perturbed",
+    "zo_mlp_loss_pair", "zo_stream_rmw", "library_path",
 ]
 
 
@@ -194,6 +194,23 @@ def zo_update(ctx: Context, theta: torch.Tensor, offset: int, step: int, c: torc
     _lib.check(_lib.lib().zo_update(ctx.handle, _dev(theta, "theta"), _dtype_code(theta),
                                     offset, theta.numel(), step, _dev(c, "c", torch.float32),
                                     npert, float(eta), bp, _stream(stream)), "zo_update")
+
+
+def zo_restore_update(ctx: Context, theta: torch.Tensor, offset: int, step: int,
+                      restore_probe: int, restore_alpha: float, c: torch.Tensor, eta: float,
+                      bits: torch.Tensor | None = None, stream=None) -> None:
+    """zo_perturb(restore_probe, restore_alpha) then zo_update, in one pass (bit-identical
+    to the two calls)."""
+    npert = c.numel()
+    bp = None
+    if bits is not None:
+        bp = _dev(bits, "bits", torch.uint8)
+        if bits.numel() < npert * zo_bits_stride(theta.numel()):
+            raise ValueError("bits must hold n_pert rows")
+    _lib.check(_lib.lib().zo_restore_update(
+        ctx.handle, _dev(theta, "theta"), _dtype_code(theta), offset, theta.numel(), step,
+        int(restore_probe), float(restore_alpha), _dev(c, "c", torch.float32), npert,
+        float(eta), bp, _stream(stream)), "zo_restore_update")
 
 
 def zo_nonfinite_count(ctx: Context, stream=None) -> int:

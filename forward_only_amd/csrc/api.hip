@@ -193,6 +193,24 @@ zo_status zo_update(zo_ctx *c, void *d_theta, zo_dtype dtype, uint64_t offset, u
                                       n_pert, eta, d_bits, c->num_cus, as_stream(stream)));
 }
 
+zo_status zo_restore_update(zo_ctx *c, void *d_theta, zo_dtype dtype, uint64_t offset,
+                            uint64_t n, uint32_t step, uint32_t restore_probe,
+                            float restore_alpha, const float *d_c, uint32_t n_pert, float eta,
+                            const uint8_t *d_bits, void *stream)
+{
+    if (!ctx_ok(c)) return ZO_EINVAL;
+    if (dtype != ZO_FP32 && dtype != ZO_BF16) return ZO_EINVAL;
+    if (!range_ok(offset, n)) return ZO_EINVAL;
+    if (n_pert > ZO_MAX_NPERT) return ZO_EUNSUPPORTED;
+    if (restore_probe >= n_pert) return ZO_EINVAL;
+    if (n == 0) return ZO_OK;
+    if (!d_theta || !aligned16(d_theta) || !d_c) return ZO_EINVAL;
+    if (d_bits && !aligned16(d_bits)) return ZO_EINVAL;
+    return from_hip(zo::launch_restore_update(d_theta, dtype == ZO_BF16, offset, n, key_of(c),
+                                              step, restore_probe, restore_alpha, d_c, n_pert,
+                                              eta, d_bits, c->num_cus, as_stream(stream)));
+}
+
 zo_status zo_nonfinite_count(zo_ctx *c, void *stream, uint32_t *out)
 {
     if (!ctx_ok(c) || !out) return ZO_EINVAL;

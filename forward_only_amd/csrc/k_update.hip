@@ -24,6 +24,13 @@
 //  * Each lane keeps 16 fp64 sums (tables in ascending group order), then reads its 16
 //    params once, forms and rounds the new values, and writes them once.
 //  * Deterministic: every sum is taken in a fixed order independent of the grid.
+//  * Restore variant (kRestore): before the update, each parameter first gets the in-place
+//    move theta + (bit ? alpha_r : -alpha_r) of one of the step's probes, rounded exactly
+//    as zo_perturb rounds it -- the last restore of the two-pass schedule, which nothing
+//    reads before the update, folded into the update's single pass over theta.  That
+//    probe's bits are produced by the update anyway: after the octet exchange of its group,
+//    lane r holds word r/2 of every probe of the group, whose half r%2 is the 16 sign bits
+//    of the lane's own params, so the fold costs no extra Philox call.
 #include <stdlib.h>
 
 #include "zo_device.hpp"
@@ -82,15 +89,38 @@ __device__ __forceinline__ uint32_t bf16pair_from_f64(double lo, double hi)
     return pack_bf16x2(f64_to_f32_round_odd(lo), f64_to_f32_round_odd(hi));
 }
 
-template <bool kBF16>
+// The restore move of parameter e0 + q: +alpha_r if bit q of rmask is set, else -alpha_r
+// (the sign bit of alpha_r flipped where the bit is clear; q is a constant after unrolling).
+__device__ __forceinline__ float restore_step(uint32_t rmask, int q, uint32_t rabits)
+{
+    return __uint_as_float(rabits ^ ((~rmask << (31 - q)) & 0x80000000u));
+}
+
+// theta_j + d rounded as zo_perturb rounds it, for a packed bf16 pair (lo = param 2j).
+__device__ __forceinline__ uint32_t restore_bf16_pair(uint32_t w, float dlo, float dhi)
+{
+    return pack_bf16x2(bf16lo_to_f32(w) + dlo, bf16hi_to_f32(w) + dhi);
+}
+
+template <bool kBF16, bool kRestore>
 __device__ __forceinline__ void apply_update(void *theta, uint64_t e0, uint64_t n,
-                                             const double (&s)[16], double eta)
+                                             const double (&s)[16], double eta, uint32_t rmask,
+                                             uint32_t rabits)
 {
     if (e0 + 16 <= n) {
         if constexpr (kBF16) {
             u32x4_t *p = reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(theta) + e0);
             u32x4_t t0 = __builtin_nontemporal_load(p);
             u32x4_t t1 = __builtin_nontemporal_load(p + 1);
+            if constexpr (kRestore) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    t0[j] = restore_bf16_pair(t0[j], restore_step(rmask, 2 * j, rabits),
+                                              restore_step(rmask, 2 * j + 1, rabits));
+                    t1[j] = restore_bf16_pair(t1[j], restore_step(rmask, 8 + 2 * j, rabits),
+                                              restore_step(rmask, 9 + 2 * j, rabits));
+                }
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 t0[j] = bf16pair_from_f64((double)bf16lo_to_f32(t0[j]) - eta * s[2 * j],
@@ -105,6 +135,12 @@ __device__ __forceinline__ void apply_update(void *theta, uint64_t e0, uint64_t 
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 u32x4_t t = __builtin_nontemporal_load(p + v);
+                if constexpr (kRestore) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        t[j] = __float_as_uint(__uint_as_float(t[j]) +
+                                               restore_step(rmask, 4 * v + j, rabits));
+                }
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     t[j] = __float_as_uint(
@@ -119,26 +155,36 @@ __device__ __forceinline__ void apply_update(void *theta, uint64_t e0, uint64_t 
             if (e < n) {
                 if constexpr (kBF16) {
                     uint16_t *t = static_cast<uint16_t *>(theta);
-                    const double v = (double)__uint_as_float((uint32_t)t[e] << 16) - eta * s[q];
+                    uint32_t w = t[e];
+                    if constexpr (kRestore)
+                        w = restore_bf16_pair(w, restore_step(rmask, q, rabits), 0.0f) & 0xFFFFu;
+                    const double v = (double)__uint_as_float(w << 16) - eta * s[q];
                     t[e] = (uint16_t)(bf16pair_from_f64(v, 0.0) & 0xFFFFu);
                 } else {
                     float *t = static_cast<float *>(theta);
-                    t[e] = (float)((double)t[e] - eta * s[q]);
+                    float x = t[e];
+                    if constexpr (kRestore) x = x + restore_step(rmask, q, rabits);
+                    t[e] = (float)((double)x - eta * s[q]);
                 }
             }
         }
     }
 }
 
-template <bool kBF16, bool kBits>
-__global__ __launch_bounds__(kUpdThreads) void k_update(void *__restrict__ theta, uint64_t n,
+// Occupancy is bounded by the dynamic LDS (sign tables + exchange, ~42 KiB per 512-thread
+// workgroup at n_pert = 160: three workgroups, six waves per SIMD), which the compiler
+// cannot see; telling it so lets it keep several table lookups in flight instead of
+// squeezing registers for an occupancy the LDS never allows.
+template <bool kBF16, bool kBits, bool kRestore>
+__global__ __launch_bounds__(kUpdThreads) __attribute__((amdgpu_waves_per_eu(6, 6))) void k_update(void *__restrict__ theta, uint64_t n,
                                                         uint64_t blk0, uint32_t step,
                                                         uint32_t k0, uint32_t k1,
                                                         const float *__restrict__ c,
                                                         uint32_t npert, uint32_t ngroups,
                                                         double eta,
                                                         const uint8_t *__restrict__ bits,
-                                                        uint64_t stride)
+                                                        uint64_t stride, uint32_t rprobe,
+                                                        uint32_t rabits)
 {
     extern __shared__ double lds_d[];
     double *tbl = lds_d;
@@ -177,6 +223,7 @@ __global__ __launch_bounds__(kUpdThreads) void k_update(void *__restrict__ theta
         double s[16];
 #pragma unroll
         for (int q = 0; q < 16; ++q) s[q] = 0.0;
+        uint32_t rmask = 0;   // kRestore: bit q = sign bit of probe rprobe at param e0 + q
 
         for (uint32_t g = 0; g < ngroups; ++g) {
             const uint32_t i = g * 8u + (uint32_t)r;
@@ -209,6 +256,14 @@ __global__ __launch_bounds__(kUpdThreads) void k_update(void *__restrict__ theta
             uint32_t Hhi = __builtin_amdgcn_perm(b23, b01, 0x07060302u);
             transpose8x8(Llo, Hlo);
             transpose8x8(Lhi, Hhi);
+            if constexpr (kRestore) {
+                if (g == (rprobe >> 3)) {   // uniform: the restore probe's group
+                    const uint32_t k = rprobe & 3u;
+                    const u32x4_t &wk = (rprobe & 4u) ? b : a;
+                    const uint32_t word = k == 0 ? wk.x : k == 1 ? wk.y : k == 2 ? wk.z : wk.w;
+                    rmask = (word >> (16u * (uint32_t)(r & 1))) & 0xFFFFu;
+                }
+            }
             const double *tg = tbl + g * 256u;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -218,7 +273,7 @@ __global__ __launch_bounds__(kUpdThreads) void k_update(void *__restrict__ theta
                 s[12 + q] += tg[(Hhi >> (8 * q)) & 255u];
             }
         }
-        apply_update<kBF16>(theta, e0, n, s, eta);
+        apply_update<kBF16, kRestore>(theta, e0, n, s, eta, rmask, rabits);
     }
 }
 
@@ -230,44 +285,69 @@ static int env_int(const char *name, int dflt)
     return v > 0 ? v : dflt;
 }
 
-template <bool kBF16, bool kBits>
+template <bool kBF16, bool kBits, bool kRestore>
 static hipError_t update_impl(void *theta, uint64_t n, uint64_t blk0, uint32_t step, Key key,
                               const float *c, uint32_t npert, float eta, const uint8_t *bits,
-                              int num_cus, hipStream_t stream)
+                              uint32_t rprobe, float ralpha, int num_cus, hipStream_t stream)
 {
     const uint32_t ngroups = (npert + 7u) / 8u;
     const size_t lds = (size_t)ngroups * 256u * 8u + (size_t)kUpdWavesPerWG * kXchWordsPerWave * 4u;
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_update<kBF16, kBits>),
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&k_update<kBF16, kBits, kRestore>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     const uint64_t nblk = (n + kBlockParams - 1) / kBlockParams;
     const uint64_t nwc = (nblk + kUpdBlocksPerWave - 1) / kUpdBlocksPerWave;
-    static const int wg_per_cu = env_int("ZO_UPDATE_WG_PER_CU", 4);
+    // Many workgroups per CU: each builds its tables once and the persistent loop's tail
+    // imbalance shrinks with the share per workgroup (measured: 154 ms at 4 per CU, 144 ms
+    // from 16 per CU on, 30B bf16 params, n_pert = 160).
+    static const int wg_per_cu = env_int("ZO_UPDATE_WG_PER_CU", 16);
     const uint64_t want = (nwc + kUpdWavesPerWG - 1) / kUpdWavesPerWG;
     const uint64_t cap = (uint64_t)num_cus * wg_per_cu;
     const uint32_t grid = (uint32_t)(want < cap ? want : cap);
-    hipLaunchKernelGGL((k_update<kBF16, kBits>), dim3(grid), dim3(kUpdThreads), lds, stream,
-                       theta, n, blk0, step, key.k0, key.k1, c, npert, ngroups, (double)eta,
-                       bits, (uint64_t)nblk * 16u);
+    hipLaunchKernelGGL((k_update<kBF16, kBits, kRestore>), dim3(grid), dim3(kUpdThreads), lds,
+                       stream, theta, n, blk0, step, key.k0, key.k1, c, npert, ngroups,
+                       (double)eta, bits, (uint64_t)nblk * 16u, rprobe,
+                       __builtin_bit_cast(uint32_t, ralpha));
     return hipGetLastError();
+}
+
+template <bool kRestore>
+static hipError_t update_dispatch(void *theta, bool bf16, uint64_t offset, uint64_t n, Key key,
+                                  uint32_t step, const float *c, uint32_t npert, float eta,
+                                  const uint8_t *bits, uint32_t rprobe, float ralpha,
+                                  int num_cus, hipStream_t stream)
+{
+    const uint64_t blk0 = offset / kBlockParams;
+    if (bf16)
+        return bits ? update_impl<true, true, kRestore>(theta, n, blk0, step, key, c, npert, eta,
+                                                        bits, rprobe, ralpha, num_cus, stream)
+                    : update_impl<true, false, kRestore>(theta, n, blk0, step, key, c, npert,
+                                                         eta, bits, rprobe, ralpha, num_cus,
+                                                         stream);
+    return bits ? update_impl<false, true, kRestore>(theta, n, blk0, step, key, c, npert, eta,
+                                                     bits, rprobe, ralpha, num_cus, stream)
+                : update_impl<false, false, kRestore>(theta, n, blk0, step, key, c, npert, eta,
+                                                      bits, rprobe, ralpha, num_cus, stream);
 }
 
 hipError_t launch_update(void *theta, bool bf16, uint64_t offset, uint64_t n, Key key,
                          uint32_t step, const float *c, uint32_t npert, float eta,
                          const uint8_t *bits, int num_cus, hipStream_t stream)
 {
-    const uint64_t blk0 = offset / kBlockParams;
-    if (bf16)
-        return bits ? update_impl<true, true>(theta, n, blk0, step, key, c, npert, eta, bits,
-                                              num_cus, stream)
-                    : update_impl<true, false>(theta, n, blk0, step, key, c, npert, eta, bits,
-                                               num_cus, stream);
-    return bits ? update_impl<false, true>(theta, n, blk0, step, key, c, npert, eta, bits,
-                                           num_cus, stream)
-                : update_impl<false, false>(theta, n, blk0, step, key, c, npert, eta, bits,
-                                            num_cus, stream);
+    return update_dispatch<false>(theta, bf16, offset, n, key, step, c, npert, eta, bits, 0u,
+                                  0.0f, num_cus, stream);
+}
+
+hipError_t launch_restore_update(void *theta, bool bf16, uint64_t offset, uint64_t n, Key key,
+                                 uint32_t step, uint32_t rprobe, float ralpha, const float *c,
+                                 uint32_t npert, float eta, const uint8_t *bits, int num_cus,
+                                 hipStream_t stream)
+{
+    return update_dispatch<true>(theta, bf16, offset, n, key, step, c, npert, eta, bits, rprobe,
+                                 ralpha, num_cus, stream);
 }
 
 }  // namespace zo

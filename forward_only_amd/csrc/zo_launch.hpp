@@ -38,6 +38,12 @@ hipError_t launch_probe_weights(const double *Lp, const double *Lm, const double
 hipError_t launch_update(void *theta, bool bf16, uint64_t offset, uint64_t n, Key key,
                          uint32_t step, const float *c, uint32_t npert, float eta,
                          const uint8_t *bits, int num_cus, hipStream_t stream);
+// The update preceded, in the same pass, by the move theta + alpha_r * z_rprobe rounded as
+// launch_perturb rounds it (rprobe < npert).
+hipError_t launch_restore_update(void *theta, bool bf16, uint64_t offset, uint64_t n, Key key,
+                                 uint32_t step, uint32_t rprobe, float ralpha, const float *c,
+                                 uint32_t npert, float eta, const uint8_t *bits, int num_cus,
+                                 hipStream_t stream);
 
 // counter[0] = 0 with a fill kernel (no memset node if the caller captures a graph).
 hipError_t launch_zero_u32(uint32_t *p, uint32_t count, hipStream_t stream);

@@ -8,7 +8,8 @@ a loss after the first and third, then the probe weights, then one update pass.
 
 schedule="S2f" visits the same points with two passes per probe: +eps z_0, then per
 probe a -2 eps z_i pass (to theta - eps z_i) and one fused pass (zo_perturb2) that restores
-probe i and applies +eps z_(i+1); the last fused pass only restores.
+probe i and applies +eps z_(i+1); the last probe's restore is folded into the update pass
+(zo_restore_update), which nothing reads in between (the weights read only the losses).
 
 Python only orders the launches; every pass over the parameters, the weights and the
 update run in libzo's kernels on torch's current stream.  Losses stay on the device.
@@ -18,7 +19,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import zo_perturb, zo_perturb2, zo_probe_weights, zo_update
+from . import zo_perturb, zo_perturb2, zo_probe_weights, zo_restore_update, zo_update
 
 
 def applied_eps(eps: float) -> float:
@@ -74,12 +75,13 @@ def spsa_step(ctx, theta: torch.Tensor, *, step: int, npert: int, eps: float, et
                 loss(theta, Lm[i:i + 1])
             if i + 1 < npert:
                 zo_perturb2(ctx, theta, offset, step, i, +a, i + 1, +a, row(i), row(i + 1))
-            else:
-                zo_perturb(ctx, theta, offset, step, i, +a, row(i))
     else:
         raise ValueError(f"unknown schedule {schedule!r}")
     c = zo_probe_weights(ctx, Lp, Lm, L0, a, delta, out=b.get("c"))
-    zo_update(ctx, theta, offset, step, c, eta, bits)
+    if schedule == "S2f" and npert > 0:
+        zo_restore_update(ctx, theta, offset, step, npert - 1, +a, c, eta, bits)
+    else:
+        zo_update(ctx, theta, offset, step, c, eta, bits)
     return {"L0": L0, "Lp": Lp, "Lm": Lm, "c": c}
 
 

@@ -164,6 +164,20 @@ zo_status zo_update(zo_ctx *ctx, void *d_theta, zo_dtype dtype, uint64_t offset,
                     uint64_t n, uint32_t step, const float *d_c, uint32_t n_pert,
                     float eta, const uint8_t *d_bits, void *stream);
 
+/* zo_perturb(restore_probe, restore_alpha) followed by zo_update, in one pass over the
+ * parameters: theta_j <- round(round(theta_j + restore_alpha * z_{restore_probe,j})
+ * - eta * sum_i c_i z_ij), each rounding exactly the one the two calls make, so the result
+ * equals the two calls bit for bit.  This is the last restore of the two-moves-per-probe
+ * schedule folded into the update that follows it (the probe weights between them read
+ * only the losses), saving one full pass per step; the restore probe's signs come from the
+ * update's own sign generation.  Arguments as zo_update, plus restore_probe (< n_pert, a
+ * probe of the same step; with d_bits, its row is used) and restore_alpha (fp32).
+ * Errors: as zo_update, and ZO_EINVAL if restore_probe >= n_pert. */
+zo_status zo_restore_update(zo_ctx *ctx, void *d_theta, zo_dtype dtype, uint64_t offset,
+                            uint64_t n, uint32_t step, uint32_t restore_probe,
+                            float restore_alpha, const float *d_c, uint32_t n_pert, float eta,
+                            const uint8_t *d_bits, void *stream);
+
 /* Read the non-finite-probe counter: synchronizes `stream`, then copies it to *out. */
 zo_status zo_nonfinite_count(zo_ctx *ctx, void *stream, uint32_t *out);
 

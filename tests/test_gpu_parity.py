@@ -201,6 +201,57 @@ def test_update_parity(ctx, kind, n, offset, npert, mode):
     assert same >= 0.9999, same
 
 
+RESTORE_CASES = [(4096, 0, 16, 15), (1000, 128, 7, 3), (8192 * 3 + 1000, 0, 160, 159),
+                 (1, 0, 1, 0), (33333, 128 * 3, 512, 300), (8192 * 13 + 5, 128, 160, 8)]
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+@pytest.mark.parametrize("n,offset,npert,rprobe", RESTORE_CASES)
+@pytest.mark.parametrize("mode", ["regen", "bits"])
+def test_restore_update_equals_perturb_then_update(ctx, kind, n, offset, npert, rprobe, mode):
+    """zo_restore_update is zo_perturb followed by zo_update, bit for bit, on the GPU; and
+    within the update bar of the oracle's perturb followed by its update.  Restore probes
+    sit in the first, a middle and the last sign group, with ragged sizes and offsets."""
+    step = 6
+    rng = np.random.default_rng(n + npert + rprobe)
+    h = _theta(kind, n, seed=n + 3, scale=0.02, specials=True)
+    c = (rng.standard_normal(npert) * 2.5e-3).astype(np.float32)
+    eta = 1.0 if kind == "bf16" else 1e-2
+    alpha = 1e-3 if kind == "bf16" else 2.0 ** -10
+    bits_h = oracle.gen_planes(SEED, step, 0, npert, offset, n) if mode == "bits" else None
+    bits_d = zo.zo_gen_probes(ctx, step, 0, npert, offset, n) if mode == "bits" else None
+    cd = to_dev_f32(c)
+    fused, seq = _dev(kind, h), _dev(kind, h)
+    zo.zo_restore_update(ctx, fused, offset, step, rprobe, alpha, cd, eta, bits_d)
+    zo.zo_perturb(ctx, seq, offset, step, rprobe, alpha, None if bits_d is None else bits_d[rprobe])
+    zo.zo_update(ctx, seq, offset, step, cd, eta, bits_d)
+    got, want = _host(kind, fused), _host(kind, seq)
+    assert_same_bits_or_nan(got, want, kind)
+    oracle.perturb(h, offset, SEED, step, rprobe, alpha,
+                   None if bits_h is None else bits_h[rprobe])
+    oracle.update(h, offset, SEED, step, c, eta, bits_h)
+    fin = np.isfinite(h.astype(np.float32) if kind == "f32" else
+                      (h.astype(np.uint32) << 16).view(np.float32))
+    if kind == "f32":
+        assert_f32_update_close(got[fin], h[fin], eta, c)
+    else:
+        assert_bf16_within_ulp(got[fin], h[fin])
+
+
+def test_restore_update_argument_checks(ctx):
+    L = zo._lib.lib()
+    t = torch.zeros(256, dtype=torch.float32, device="cuda")
+    c = torch.zeros(8, dtype=torch.float32, device="cuda")
+    args = lambda rp, npert=8: L.zo_restore_update(  # noqa: E731
+        ctx.handle, t.data_ptr(), zo.ZO_FP32, 0, 256, 0, rp, 1e-3, c.data_ptr(), npert, 1e-2,
+        None, None)
+    assert args(8) == zo.ZO_EINVAL                 # restore probe outside the step's probes
+    assert args(0, npert=0) == zo.ZO_EINVAL
+    assert args(0, npert=513) == zo.ZO_EUNSUPPORTED
+    assert args(7) == zo.ZO_OK
+    torch.cuda.synchronize()
+
+
 def test_update_sum_error_within_recursive_summation_bound(ctx):
     # s_j from the GPU (recovered with eta = 1 on theta = 0 in fp32: theta' = -s rounded
     # once to fp32) vs the oracle's fp64 sums: |s_gpu - s| <= half an fp32 ulp of s plus

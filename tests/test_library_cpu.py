@@ -60,6 +60,8 @@ def test_null_context_and_arguments_are_rejected():
     v = ctypes.c_uint32()
     assert L.zo_nonfinite_count(None, None, ctypes.byref(v)) == _lib.ZO_EINVAL
     assert L.zo_stream_rmw(None, None, 16, 0, None) == _lib.ZO_EINVAL
+    assert L.zo_restore_update(None, None, 0, 0, 16, 0, 0, 1.0, None, 1, 1.0, None,
+                               None) == _lib.ZO_EINVAL
     assert L.zo_mlp_loss_pair(None, None, 0, 0, 0, 1.0, None, None, None, 16, 16, 16, 2, None,
                               0, None, None, None) == _lib.ZO_EINVAL
 
