@@ -1,11 +1,12 @@
 """Parity at the full workload sizes, in the launch configuration the benchmark times.
 
 The whole parameter buffer goes through the same calls the benchmark makes (zo_perturb,
-zo_perturb2, zo_update on the full buffer, probes regenerated); sampled windows (random
-ones, the first, the one holding the ragged tail and the last) are copied to the host
-before and after and recomputed by the oracle from their global offsets -- the probe bits
-are counter-based, so a window is an exact sub-problem.  Passes are compared bit for bit,
-the update within the update tolerance (fp32) or one bf16 ulp.
+zo_perturb2, and zo_restore_update -- the update carrying a restore -- on the full buffer,
+probes regenerated); sampled windows (random ones, the first, the one holding the ragged
+tail and the last) are copied to the host before and after and recomputed by the oracle
+from their global offsets -- the probe bits are counter-based, so a window is an exact
+sub-problem.  Passes are compared bit for bit, the update within the update tolerance
+(fp32) or one bf16 ulp.
 """
 import numpy as np
 import pytest
@@ -49,8 +50,8 @@ def _run_and_check(t, M, kind, seed, npert, eps, eta, label):
     zo.zo_perturb2(ctx, t, 0, 1, 0, +a, 1, +a)
     torch.cuda.synchronize()
     after_passes = _take(t, starts, kind)
-    print(f"[fullsize] {label}: update n_pert={npert}", flush=True)
-    zo.zo_update(ctx, t, 0, 1, torch.from_numpy(c).cuda(), eta)
+    print(f"[fullsize] {label}: restore + update n_pert={npert}", flush=True)
+    zo.zo_restore_update(ctx, t, 0, 1, 1, -a, torch.from_numpy(c).cuda(), eta)
     torch.cuda.synchronize()
     after_update = _take(t, starts, kind)
     ctx.close()
@@ -61,6 +62,7 @@ def _run_and_check(t, M, kind, seed, npert, eps, eta, label):
         oracle.perturb2(h, s, seed, 1, 0, +a, 1, +a)
         assert np.array_equal(h.view(np.uint32 if kind == "f32" else np.uint16),
                               hp.view(np.uint32 if kind == "f32" else np.uint16)), (label, s)
+        oracle.perturb(h, s, seed, 1, 1, -a)
         oracle.update(h, s, seed, 1, c, eta)
         if kind == "f32":
             assert_f32_update_close(hu, h, eta, c)
