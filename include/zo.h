@@ -165,7 +165,10 @@ zo_status zo_update(zo_ctx *ctx, void *d_theta, zo_dtype dtype, uint64_t offset,
                     float eta, const uint8_t *d_bits, void *stream);
 
 /* zo_perturb(restore_probe, restore_alpha) followed by zo_update, in one pass over the
- * parameters: theta_j <- round(round(theta_j + restore_alpha * z_{restore_probe,j})
+ * parameters -- the restore after the last probe's evaluations ("How 1.5-SPSA Works" on
+ * "Stanford's 1.5-SPSA Trains OPT-30B Without Backpropagation": parameters moved in place
+ * to theta +/- eps*z_i and back) and the update box of the ZOO loop flowchart ("Pretraining
+ * Transformers Without Backprop: What Two Zero-Order Papers Actually Measure"): theta_j <- round(round(theta_j + restore_alpha * z_{restore_probe,j})
  * - eta * sum_i c_i z_ij), each rounding exactly the one the two calls make, so the result
  * equals the two calls bit for bit.  This is the last restore of the two-moves-per-probe
  * schedule folded into the update that follows it (the probe weights between them read
