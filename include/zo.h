@@ -168,9 +168,11 @@ zo_status zo_update(zo_ctx *ctx, void *d_theta, zo_dtype dtype, uint64_t offset,
  * parameters -- the restore after the last probe's evaluations ("How 1.5-SPSA Works" on
  * "Stanford's 1.5-SPSA Trains OPT-30B Without Backpropagation": parameters moved in place
  * to theta +/- eps*z_i and back) and the update box of the ZOO loop flowchart ("Pretraining
- * Transformers Without Backprop: What Two Zero-Order Papers Actually Measure"): theta_j <- round(round(theta_j + restore_alpha * z_{restore_probe,j})
- * - eta * sum_i c_i z_ij), each rounding exactly the one the two calls make, so the result
- * equals the two calls bit for bit.  This is the last restore of the two-moves-per-probe
+ * Transformers Without Backprop: What Two Zero-Order Papers Actually Measure"):
+ *   theta_j <- round(round(theta_j + restore_alpha * z_{restore_probe,j})
+ *                    - eta * sum_i c_i z_ij),
+ * each rounding exactly the one the two calls make, so the result equals the two calls bit
+ * for bit.  This is the last restore of the two-moves-per-probe
  * schedule folded into the update that follows it (the probe weights between them read
  * only the losses), saving one full pass per step; the restore probe's signs come from the
  * update's own sign generation.  Arguments as zo_update, plus restore_probe (< n_pert, a
