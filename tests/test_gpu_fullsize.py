@@ -89,3 +89,17 @@ def test_opt_shaped_bf16_full_size(name):
     assert n >= 20
     del t
     torch.cuda.empty_cache()
+
+
+def test_opt30b_largest_probe_count():
+    """The update at its largest probe count (ZO_MAX_NPERT = 512: 64 sign tables, 128 KiB of
+    LDS per workgroup) over the whole 30B buffer, with the restore of the last probe
+    folded in, against the oracle on the sampled windows."""
+    cfg = CONFIGS["opt30b"]
+    t = torch.empty(cfg.M, dtype=torch.bfloat16, device="cuda")
+    gen.device_normal_(t, cfg.theta_std, cfg.seed)
+    n = _run_and_check(t, cfg.M, "bf16", cfg.seed, int(zo.ZO_MAX_NPERT), cfg.eps, 1.0,
+                       "opt30b n_pert=512")
+    assert n >= 20
+    del t
+    torch.cuda.empty_cache()
