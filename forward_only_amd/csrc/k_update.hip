@@ -277,12 +277,14 @@ __global__ __launch_bounds__(kUpdThreads) __attribute__((amdgpu_waves_per_eu(6, 
     }
 }
 
+// Launch-shape override from the environment (read once per process): workgroups per CU,
+// accepted in [1, 64], anything else keeps the default.
 static int env_int(const char *name, int dflt)
 {
     const char *s = getenv(name);
     if (!s || !*s) return dflt;
     const int v = atoi(s);
-    return v > 0 ? v : dflt;
+    return (v >= 1 && v <= 64) ? v : dflt;
 }
 
 template <bool kBF16, bool kBits, bool kRestore>

@@ -34,6 +34,9 @@
  *    different streams (the non-finite counter is updated atomically and may be shared).
  *  - Devices: a context belongs to the device that was current at zo_init; every call
  *    on it must be made with that device current, or it returns ZO_EINVAL.
+ *  - Launch shapes: ZO_PERTURB_WG_PER_CU (default 8) and ZO_UPDATE_WG_PER_CU (default 16)
+ *    override the workgroups per CU of the perturb and update kernels, read once per
+ *    process, accepted in [1, 64].  Results do not depend on them.
  */
 #ifndef ZO_H
 #define ZO_H
