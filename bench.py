@@ -369,8 +369,12 @@ def main(argv=None):
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    step_marks = [ev()]
+    step_marks[0].record()
     for s in range(W, total):
         one_step(s, True)
+        step_marks.append(ev())
+        step_marks[-1].record()     # step boundary on the launch stream (no host sync)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     log(f"[bench] {K} timed steps done in {t1 - t0:.2f} s")
@@ -385,6 +389,9 @@ def main(argv=None):
 
     T = (t1 - t0) / K
     value = n * M / T
+    step_ms = sorted(a.elapsed_time(b) for a, b in zip(step_marks, step_marks[1:]))
+    median_ms = (step_ms[K // 2] if K % 2 else 0.5 * (step_ms[K // 2 - 1] + step_ms[K // 2]))
+    kernel_ms_per_step = sum(times(list(per))) / K     # sum of every timed kernel call
     # every pass of either perturb entry point runs k_perturb_chunks (one or two probes)
     pert_ms, upd_ms, w_ms = avg_ms("perturb", "perturb2"), avg_ms("update"), avg_ms("weights")
     passes = 0 if mlp is not None else (4 * n if args.schedule == "S4" else 2 * n)
@@ -422,6 +429,8 @@ def main(argv=None):
         "steps": K,
         "warmup": W,
         "ms_per_step": T * 1e3,
+        "ms_per_step_median": median_ms,
+        "kernel_ms_per_step": kernel_ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
