@@ -159,6 +159,7 @@ def cpu_baseline(cfg, params_per_thread: int, threads: int, schedule: str):
         "single_core_value": cfg.npert * n1 / dt1,
         "single_core_sample": f"{n1} params of the first window on one thread; {dt1:.1f} s",
         "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
     }
 
 

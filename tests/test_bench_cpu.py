@@ -55,3 +55,4 @@ def test_cpu_baseline_record_on_a_tiny_slice():
     assert r["kind"] == "oracle" and r["unit"] == "probe*params/s" and r["cores"] == 2
     assert r["value"] > 0 and r["single_core_value"] > 0
     assert "2 windows x 1024 bf16 params" in r["sample"]
+    assert r["host_cpus"] >= 1 and r["cpu_model"]
