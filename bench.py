@@ -379,6 +379,26 @@ def main(argv=None):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     log(f"[bench] {K} timed steps done in {t1 - t0:.2f} s")
+
+    # The packed-plane generator (the step regenerates bits inline; planes serve callers
+    # that store them): one probe's plane over the whole buffer, timed after the step.
+    gen_probes = None
+    if mlp is None:
+        stride = zo.zo_bits_stride(M)
+        plane = torch.empty((1, stride), dtype=torch.uint8, device=dev)
+        zo.zo_gen_probes(ctx, 0, 0, 1, 0, M, out=plane)
+        g0, g1 = ev(), ev()
+        g0.record()
+        for i in range(3):
+            zo.zo_gen_probes(ctx, 0, i, 1, 0, M, out=plane)
+        g1.record()
+        torch.cuda.synchronize()
+        gen_s = g0.elapsed_time(g1) / 3 * 1e-3
+        gen_probes = {"kernel": "k_gen_probes", "bound": "hbm", "plane_bytes": stride,
+                      "achieved_GBps": stride / gen_s / 1e9,
+                      "frac": stride / gen_s / 1e9 / PEAK_HBM_GBPS,
+                      "philox_calls_per_s": (stride // 16) / gen_s}
+        del plane
     nonfinite = zo.zo_nonfinite_count(ctx)
 
     def times(kinds):
@@ -465,6 +485,7 @@ def main(argv=None):
                                  "frac_of_placement_ceiling": (achieved / placement_gbps
                                                                if placement_gbps else None)},
         "update_roofline": update_roofline(M, n, pass_bytes, upd_ms),
+        "gen_probes": gen_probes,
         "nonfinite_probes": nonfinite,
         "cpu_baseline": cpu,
     }
