@@ -103,3 +103,39 @@ def test_opt30b_largest_probe_count():
     assert n >= 20
     del t
     torch.cuda.empty_cache()
+
+
+def test_opt30b_full_step_drift_without_update():
+    """One whole two-pass step over the 30B buffer (160 probes: 320 passes, then the update
+    carrying the last restore) with eta = 0, so the update adds exactly zero: every bf16
+    parameter must end within one bf16 ulp of |theta| + eps of where it started -- the
+    drift bound of the schedule, checked on all 29,959,831,552 elements rather than on
+    windows.  Each pass is one rounding, so some elements do move."""
+    from forward_only_amd.step import spsa_step
+    cfg = CONFIGS["opt30b"]
+    t = torch.empty(cfg.M, dtype=torch.bfloat16, device="cuda")
+    gen.device_normal_(t, cfg.theta_std, cfg.seed)
+    t0 = t.clone()
+    L0, Lp, Lm = gen.synthetic_losses(cfg.seed, 0, cfg.npert)
+    dl = (torch.tensor([L0], dtype=torch.float64, device="cuda"),
+          torch.from_numpy(Lp).cuda(), torch.from_numpy(Lm).cuda())
+    ctx = zo.zo_init(cfg.seed)
+    print("[fullsize] opt30b: full S2f step, eta = 0", flush=True)
+    spsa_step(ctx, t, step=0, npert=cfg.npert, eps=cfg.eps, eta=0.0, delta=cfg.delta,
+              losses=dl, schedule="S2f")
+    torch.cuda.synchronize()
+    ctx.close()
+    bad = changed = 0
+    chunk = 1 << 30
+    for i in range(0, cfg.M, chunk):
+        a = t0[i:i + chunk].float()
+        b = t[i:i + chunk].float()
+        _, e = torch.frexp(a.abs() + 1e-3)
+        ulp = torch.ldexp(torch.ones_like(a), e - 8)          # bf16 spacing of |theta| + eps
+        bad += int(((b - a).abs() > ulp).sum())
+        changed += int((b != a).sum())
+        del a, b, e, ulp
+    del t, t0
+    torch.cuda.empty_cache()
+    assert bad == 0, bad
+    assert 0.01 * cfg.M < changed < 0.6 * cfg.M, changed / cfg.M
