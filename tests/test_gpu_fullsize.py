@@ -139,3 +139,30 @@ def test_opt30b_full_step_drift_without_update():
     torch.cuda.empty_cache()
     assert bad == 0, bad
     assert 0.01 * cfg.M < changed < 0.6 * cfg.M, changed / cfg.M
+
+
+def test_opt30b_update_and_perturb_signs_agree_everywhere():
+    """Over the whole 30B buffer, the signs the update regenerates equal the signs the
+    perturb pass regenerates: from theta = 0, one-hot weights at probe k with eta = -1
+    give theta = z_k, and so does a perturb by +1 (bf16 holds +/-1 exactly).  Probe k sits
+    in the last sign group of the 160."""
+    cfg = CONFIGS["opt30b"]
+    k = 157
+    ctx = zo.zo_init(cfg.seed)
+    a = torch.zeros(cfg.M, dtype=torch.bfloat16, device="cuda")
+    c = torch.zeros(cfg.npert, dtype=torch.float32, device="cuda")
+    c[k] = 1.0
+    print("[fullsize] opt30b: update signs", flush=True)
+    zo.zo_update(ctx, a, 0, 3, c, -1.0)
+    b = torch.zeros(cfg.M, dtype=torch.bfloat16, device="cuda")
+    print("[fullsize] opt30b: perturb signs", flush=True)
+    zo.zo_perturb(ctx, b, 0, 3, k, 1.0)
+    torch.cuda.synchronize()
+    ctx.close()
+    chunk = 1 << 31
+    same = all(torch.equal(a[i:i + chunk], b[i:i + chunk]) for i in range(0, cfg.M, chunk))
+    ones = int((a[: 1 << 24].float().abs() == 1.0).sum())
+    del a, b
+    torch.cuda.empty_cache()
+    assert same
+    assert ones == 1 << 24                      # every element is +/-1
