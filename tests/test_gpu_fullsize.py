@@ -143,9 +143,10 @@ def test_opt30b_full_step_drift_without_update():
 
 def test_opt30b_update_and_perturb_signs_agree_everywhere():
     """Over the whole 30B buffer, the signs the update regenerates equal the signs the
-    perturb pass regenerates: from theta = 0, one-hot weights at probe k with eta = -1
-    give theta = z_k, and so does a perturb by +1 (bf16 holds +/-1 exactly).  Probe k sits
-    in the last sign group of the 160."""
+    perturb pass regenerates and the bits of the packed plane: from theta = 0, one-hot
+    weights at probe k with eta = -1 give theta = z_k, and so does a perturb by +1 (bf16
+    holds +/-1 exactly); the plane's bit j is 1 exactly where z_k,j = +1.  Probe k sits in
+    the last sign group of the 160."""
     cfg = CONFIGS["opt30b"]
     k = 157
     ctx = zo.zo_init(cfg.seed)
@@ -157,12 +158,23 @@ def test_opt30b_update_and_perturb_signs_agree_everywhere():
     b = torch.zeros(cfg.M, dtype=torch.bfloat16, device="cuda")
     print("[fullsize] opt30b: perturb signs", flush=True)
     zo.zo_perturb(ctx, b, 0, 3, k, 1.0)
+    print("[fullsize] opt30b: plane", flush=True)
+    plane = zo.zo_gen_probes(ctx, 3, k, 1, 0, cfg.M)[0]
     torch.cuda.synchronize()
     ctx.close()
     chunk = 1 << 31
     same = all(torch.equal(a[i:i + chunk], b[i:i + chunk]) for i in range(0, cfg.M, chunk))
     ones = int((a[: 1 << 24].float().abs() == 1.0).sum())
-    del a, b
+    shifts = torch.arange(8, dtype=torch.uint8, device="cuda")
+    plane_ok = True
+    for i in range(0, cfg.M, chunk):             # chunk is a multiple of 8
+        m = min(chunk, cfg.M - i)
+        bytes_ = plane[i // 8:(i + m + 7) // 8]
+        bits = ((bytes_.unsqueeze(1) >> shifts) & 1).reshape(-1)[:m]
+        plane_ok &= torch.equal(bits.bool(), b[i:i + m] > 0)
+        del bits
+    del a, b, plane
     torch.cuda.empty_cache()
     assert same
+    assert plane_ok
     assert ones == 1 << 24                      # every element is +/-1
