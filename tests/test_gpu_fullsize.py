@@ -178,3 +178,28 @@ def test_opt30b_update_and_perturb_signs_agree_everywhere():
     assert same
     assert plane_ok
     assert ones == 1 << 24                      # every element is +/-1
+
+
+def test_opt30b_restore_update_equals_two_calls_everywhere():
+    """zo_restore_update is zo_perturb followed by zo_update bit for bit, on every element
+    of the 30B buffer (n_pert = 160, eta = 1 so that the bf16 update moves parameters)."""
+    cfg = CONFIGS["opt30b"]
+    a = torch.empty(cfg.M, dtype=torch.bfloat16, device="cuda")
+    gen.device_normal_(a, cfg.theta_std, cfg.seed)
+    b = a.clone()
+    c = torch.from_numpy((np.random.default_rng(9).standard_normal(cfg.npert) * 2.5e-3)
+                         .astype(np.float32)).cuda()
+    alpha = float(np.float32(cfg.eps))
+    ctx = zo.zo_init(cfg.seed)
+    print("[fullsize] opt30b: restore + update, fused and as two calls", flush=True)
+    zo.zo_restore_update(ctx, a, 0, 4, cfg.npert - 1, alpha, c, 1.0)
+    zo.zo_perturb(ctx, b, 0, 4, cfg.npert - 1, alpha)
+    zo.zo_update(ctx, b, 0, 4, c, 1.0)
+    torch.cuda.synchronize()
+    ctx.close()
+    chunk = 1 << 31
+    same = all(torch.equal(a[i:i + chunk].view(torch.int16), b[i:i + chunk].view(torch.int16))
+               for i in range(0, cfg.M, chunk))
+    del a, b
+    torch.cuda.empty_cache()
+    assert same
