@@ -7,6 +7,10 @@ tail and the last) are copied to the host before and after and recomputed by the
 from their global offsets -- the probe bits are counter-based, so a window is an exact
 sub-problem.  Passes are compared bit for bit, the update within the update tolerance
 (fp32) or one bf16 ulp.
+
+Properties that hold at any size are checked on every element of the 30B buffer: the
+drift bound of a whole two-pass step, the agreement of the three routes to a probe's signs
+(update, perturb, packed plane), and the restore-carrying update against the two calls.
 """
 import numpy as np
 import pytest
