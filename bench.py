@@ -74,8 +74,8 @@ def source_hash(paths) -> str:
 
 
 def stored_traffic(workload: str, nbytes_alg: float):
-    """HBM bytes per perturb dispatch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source and this workload; else None."""
+    """HBM bytes per perturb pass from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source and this workload; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -83,7 +83,7 @@ def stored_traffic(workload: str, nbytes_alg: float):
         return None
     if t.get("source_sha256") != source_hash(PERTURB_SOURCES) or t.get("workload") != workload:
         return None
-    return float(t["bytes_per_dispatch"])
+    return float(t["bytes_per_pass"])
 
 
 def stored_philox_peak():
@@ -352,7 +352,13 @@ def main(argv=None):
     # on its physical placement): a pass that reads and writes back theta unchanged, in the
     # perturb kernel's order, timed before the warmup.
     placement_gbps = None
+    tune = None
     if mlp is None:
+        # one-time choice, on this very buffer, between one launch per pass and launches per
+        # 512 MiB slice (contents unchanged); the passes below use the faster form
+        tune = zo.zo_tune_placement(ctx, theta)
+        log(f"[bench] placement: one launch {tune['gbps_whole']:.0f} GB/s, 512 MiB slices "
+            f"{tune['gbps_sliced']:.0f} GB/s -> slice_bytes {tune['slice_bytes']}")
         zo.zo_stream_rmw(ctx, theta)
         e0, e1 = ev(), ev()
         e0.record()
@@ -482,6 +488,7 @@ def main(argv=None):
                                  "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                                  "traffic": traffic,
                                  "placement_ceiling": placement_gbps,
+                                 "placement_tuning": tune,
                                  "frac_of_placement_ceiling": (achieved / placement_gbps
                                                                if placement_gbps else None)},
         "update_roofline": update_roofline(M, n, pass_bytes, upd_ms),

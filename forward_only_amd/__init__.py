@@ -28,7 +28,8 @@ __all__ = [
     "zo_perturb", "zo_perturb2", "zo_probe_weights", "zo_probe_weights_ex", "zo_update",
     "zo_restore_update", "zo_nonfinite_count", "zo_reset_nonfinite", "zo_quad_loss",
     "zo_lowrank_quad_loss", "zo_mlp_workspace_bytes", "zo_mlp_loss", "zo_mlp_loss_perturbed",
-    "zo_mlp_loss_pair", "zo_stream_rmw", "library_path",
+    "zo_mlp_loss_pair", "zo_stream_rmw", "zo_tune_placement", "zo_set_slice_bytes",
+    "zo_get_slice_bytes", "library_path",
 ]
 
 
@@ -338,3 +339,23 @@ def zo_stream_rmw(ctx: Context, buf: torch.Tensor, mask: int = 0, stream=None) -
     nbytes = buf.numel() * buf.element_size()
     _lib.check(_lib.lib().zo_stream_rmw(ctx.handle, _dev(buf, "buf"), nbytes, int(mask) & 0xFFFFFFFF,
                                         _stream(stream)), "zo_stream_rmw")
+
+
+def zo_tune_placement(ctx: Context, buf: torch.Tensor, stream=None) -> dict:
+    """Time a pass over `buf` as one launch and as 512 MiB slices (contents unchanged), keep
+    the faster form in the context; returns {"slice_bytes", "gbps_whole", "gbps_sliced"}."""
+    sl, gw, gs = ctypes.c_uint64(), ctypes.c_double(), ctypes.c_double()
+    nbytes = buf.numel() * buf.element_size()
+    _lib.check(_lib.lib().zo_tune_placement(ctx.handle, _dev(buf, "buf"), nbytes,
+                                            _stream(stream), ctypes.byref(sl), ctypes.byref(gw),
+                                            ctypes.byref(gs)), "zo_tune_placement")
+    return {"slice_bytes": int(sl.value), "gbps_whole": gw.value, "gbps_sliced": gs.value}
+
+
+def zo_set_slice_bytes(ctx: Context, slice_bytes: int) -> None:
+    """Issue the context's perturb passes per slice of `slice_bytes` (0: one launch)."""
+    _lib.check(_lib.lib().zo_set_slice_bytes(ctx.handle, int(slice_bytes)), "zo_set_slice_bytes")
+
+
+def zo_get_slice_bytes(ctx: Context) -> int:
+    return int(_lib.lib().zo_get_slice_bytes(ctx.handle))

@@ -47,6 +47,9 @@ SIGNATURES = {
     "zo_mlp_loss_pair": (_int, [_vp, _vp, _u64, _u32, _u32, _f32, _vp, _vp, _vp, _u32,
                                 _u32, _u32, _u32, _vp, _u64, _vp, _vp, _vp]),
     "zo_stream_rmw": (_int, [_vp, _vp, _u64, _u32, _vp]),
+    "zo_tune_placement": (_int, [_vp, _vp, _u64, _vp, _vp, _vp, _vp]),
+    "zo_set_slice_bytes": (_int, [_vp, _u64]),
+    "zo_get_slice_bytes": (_u64, [_vp]),
     "zo_restore_update": (_int, [_vp, _vp, _int, _u64, _u64, _u32, _u32, _f32, _vp, _u32,
                                  _f32, _vp, _vp]),
 }

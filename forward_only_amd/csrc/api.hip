@@ -11,6 +11,7 @@ struct zo_ctx {
     int num_cus;
     uint32_t *d_counter;   // non-finite probe counter
     double *d_partials;    // loss partial sums (zo::kLossPartials * (kLowRankMax + 1) doubles)
+    uint64_t slice_bytes;  // perturb passes issued per slice of this many bytes (0: whole)
 };
 
 namespace {
@@ -30,6 +31,17 @@ inline bool ctx_ok(const zo_ctx *c)
 }
 
 inline zo_status from_hip(hipError_t e) { return e == hipSuccess ? ZO_OK : ZO_EHIP; }
+
+// Params per slice for the context's slice setting and an element size: a whole number of
+// streaming chunks, or 0 (one launch per pass).
+inline uint64_t slice_params(const zo_ctx *c, uint64_t elem)
+{
+    const uint64_t p = c->slice_bytes / elem;
+    return p / zo::kPerturbChunkParams * zo::kPerturbChunkParams;
+}
+
+// Slice size zo_tune_placement tries against one whole launch.
+constexpr uint64_t kTuneSliceBytes = (uint64_t)512 << 20;
 
 // Common checks for a parameter range [offset, offset + n).
 inline bool range_ok(uint64_t offset, uint64_t n)
@@ -128,7 +140,8 @@ zo_status zo_perturb(zo_ctx *c, void *d_theta, zo_dtype dtype, uint64_t offset, 
     if (!d_theta || !aligned16(d_theta)) return ZO_EINVAL;
     if (d_bits && !aligned16(d_bits)) return ZO_EINVAL;
     return from_hip(zo::launch_perturb(d_theta, dtype == ZO_BF16, offset, n, key_of(c), step,
-                                       probe, alpha, d_bits, c->num_cus, as_stream(stream)));
+                                       probe, alpha, d_bits, c->num_cus, as_stream(stream),
+                                       slice_params(c, dtype == ZO_BF16 ? 2 : 4)));
 }
 
 zo_status zo_perturb2(zo_ctx *c, void *d_theta, zo_dtype dtype, uint64_t offset, uint64_t n,
@@ -145,7 +158,8 @@ zo_status zo_perturb2(zo_ctx *c, void *d_theta, zo_dtype dtype, uint64_t offset,
     if (d_bits_a && (!aligned16(d_bits_a) || !aligned16(d_bits_b))) return ZO_EINVAL;
     return from_hip(zo::launch_perturb2(d_theta, dtype == ZO_BF16, offset, n, key_of(c), step,
                                         probe_a, alpha_a, probe_b, alpha_b, d_bits_a, d_bits_b,
-                                        c->num_cus, as_stream(stream)));
+                                        c->num_cus, as_stream(stream),
+                                        slice_params(c, dtype == ZO_BF16 ? 2 : 4)));
 }
 
 zo_status zo_probe_weights(zo_ctx *c, const double *d_Lp, const double *d_Lm,
@@ -329,7 +343,68 @@ zo_status zo_stream_rmw(zo_ctx *c, void *d_buf, uint64_t bytes, uint32_t mask, v
     if (!ctx_ok(c)) return ZO_EINVAL;
     if (bytes == 0) return ZO_OK;
     if (!d_buf || !aligned16(d_buf) || bytes % 16u) return ZO_EINVAL;
-    return from_hip(zo::launch_stream_rmw(d_buf, bytes, mask, c->num_cus, as_stream(stream)));
+    return from_hip(zo::launch_stream_rmw(d_buf, bytes, mask, c->num_cus, as_stream(stream),
+                                          c->slice_bytes));
+}
+
+zo_status zo_set_slice_bytes(zo_ctx *c, uint64_t slice_bytes)
+{
+    if (!ctx_ok(c)) return ZO_EINVAL;
+    if (slice_bytes % ((uint64_t)1 << 20)) return ZO_EINVAL;
+    c->slice_bytes = slice_bytes;
+    return ZO_OK;
+}
+
+uint64_t zo_get_slice_bytes(const zo_ctx *c) { return c ? c->slice_bytes : 0; }
+
+zo_status zo_tune_placement(zo_ctx *c, void *d_buf, uint64_t bytes, void *stream,
+                            uint64_t *out_slice_bytes, double *out_gbps_whole,
+                            double *out_gbps_sliced)
+{
+    if (!ctx_ok(c)) return ZO_EINVAL;
+    if (!d_buf || !aligned16(d_buf) || bytes % 16u) return ZO_EINVAL;
+    const hipStream_t s = as_stream(stream);
+    double gbps[2] = {0.0, 0.0};                 // whole, sliced
+    const bool try_slices = bytes >= 2 * kTuneSliceBytes;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+        if (e0) (void)hipEventDestroy(e0);
+        (void)hipGetLastError();
+        return ZO_EHIP;
+    }
+    zo_status st = ZO_OK;
+    for (int mode = 0; mode < (try_slices ? 2 : 1) && st == ZO_OK; ++mode) {
+        const uint64_t sl = mode ? kTuneSliceBytes : 0;
+        // mask 0: every word is written back unchanged
+        if (zo::launch_stream_rmw(d_buf, bytes, 0u, c->num_cus, s, sl) != hipSuccess ||
+            hipEventRecord(e0, s) != hipSuccess) {
+            st = ZO_EHIP;
+            break;
+        }
+        for (int r = 0; r < 2; ++r)
+            if (zo::launch_stream_rmw(d_buf, bytes, 0u, c->num_cus, s, sl) != hipSuccess)
+                st = ZO_EHIP;
+        float ms = 0.0f;
+        if (st != ZO_OK || hipEventRecord(e1, s) != hipSuccess ||
+            hipEventSynchronize(e1) != hipSuccess ||
+            hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+            st = ZO_EHIP;
+            break;
+        }
+        gbps[mode] = ms > 0.0f ? 2.0 * 2.0 * (double)bytes / (ms * 1e-3) / 1e9 : 0.0;
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (st != ZO_OK) {
+        (void)hipGetLastError();
+        return st;
+    }
+    // slices only when clearly faster than one launch
+    c->slice_bytes = (try_slices && gbps[1] > 1.02 * gbps[0]) ? kTuneSliceBytes : 0;
+    if (out_slice_bytes) *out_slice_bytes = c->slice_bytes;
+    if (out_gbps_whole) *out_gbps_whole = gbps[0];
+    if (out_gbps_sliced) *out_gbps_sliced = gbps[1];
+    return ZO_OK;
 }
 
 }  // extern "C"

@@ -41,8 +41,8 @@ __global__ __launch_bounds__(256) void k_stream_rmw_tail(u32x4_t *__restrict__ p
     if (i < nwords) p[i] = p[i] ^ mask;
 }
 
-hipError_t launch_stream_rmw(void *buf, uint64_t bytes, uint32_t mask, int num_cus,
-                             hipStream_t stream)
+static hipError_t stream_rmw_range(void *buf, uint64_t bytes, uint32_t mask, int num_cus,
+                                   hipStream_t stream)
 {
     const uint64_t nwords = bytes / 16;
     const uint64_t nchunks = nwords / kDiagChunk16;
@@ -60,6 +60,20 @@ hipError_t launch_stream_rmw(void *buf, uint64_t bytes, uint32_t mask, int num_c
                            mask);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_stream_rmw(void *buf, uint64_t bytes, uint32_t mask, int num_cus,
+                             hipStream_t stream, uint64_t slice_bytes)
+{
+    if (slice_bytes == 0 || slice_bytes >= bytes)
+        return stream_rmw_range(buf, bytes, mask, num_cus, stream);
+    for (uint64_t b0 = 0; b0 < bytes; b0 += slice_bytes) {
+        const uint64_t m = (bytes - b0) < slice_bytes ? (bytes - b0) : slice_bytes;
+        const hipError_t e = stream_rmw_range(static_cast<char *>(buf) + b0, m, mask, num_cus,
+                                              stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace zo

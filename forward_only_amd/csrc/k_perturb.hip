@@ -24,6 +24,8 @@
 //  * Apply: flip alpha's sign bit when the param's bit is clear, one fp32 add, and for
 //    bf16 one v_cvt_pk_bf16_f32 (round to nearest even) per pair; store dwordx4.
 //  * The ragged end (fewer than 8192 params) goes to a small per-element kernel.
+//  * A pass may be issued as consecutive launches over slices of the buffer (the context's
+//    slice setting, chosen per buffer by zo_tune_placement); the result is the same.
 //  * Two-probe variant (zo_perturb2): the restore of probe a and the move of probe b in
 //    one pass.  Each lane computes both Philox blocks, both land in LDS, and the step is
 //    d = (+/-alpha_a) + (+/-alpha_b) in fp32 followed by the same add and narrow; this
@@ -178,10 +180,10 @@ static int env_int(const char *name, int dflt)
 }
 
 template <bool kBF16, bool kBits, bool kTwo>
-static hipError_t perturb_impl(void *theta, uint64_t n, uint64_t blk0, uint32_t step,
-                               uint32_t probe_a, uint32_t probe_b, Key key, uint32_t abits,
-                               uint32_t bbits, const uint8_t *bits_a, const uint8_t *bits_b,
-                               int num_cus, hipStream_t stream)
+static hipError_t perturb_range(void *theta, uint64_t n, uint64_t blk0, uint32_t step,
+                                uint32_t probe_a, uint32_t probe_b, Key key, uint32_t abits,
+                                uint32_t bbits, const uint8_t *bits_a, const uint8_t *bits_b,
+                                int num_cus, hipStream_t stream)
 {
     const uint64_t nchunks = n / kChunkParams;
     if (nchunks) {
@@ -208,46 +210,69 @@ static hipError_t perturb_impl(void *theta, uint64_t n, uint64_t blk0, uint32_t 
     return hipGetLastError();
 }
 
+// The pass over [0, n) as one launch, or (slice > 0, a multiple of kChunkParams) as one
+// launch per slice of `slice` params in order: each slice is the same pass over its own
+// range (its block index and plane bytes advanced with it), so the result is identical.
+// Separate launches keep all waves within one slice at a time; on a large buffer whose
+// physical placement slows the single launch's eight far-apart XCD streams, this is
+// faster (the choice is made per buffer by zo_tune_placement).
+template <bool kBF16, bool kBits, bool kTwo>
+static hipError_t perturb_impl(void *theta, uint64_t n, uint64_t blk0, uint32_t step,
+                               uint32_t probe_a, uint32_t probe_b, Key key, uint32_t abits,
+                               uint32_t bbits, const uint8_t *bits_a, const uint8_t *bits_b,
+                               uint64_t slice, int num_cus, hipStream_t stream)
+{
+    if (slice == 0 || slice >= n)
+        return perturb_range<kBF16, kBits, kTwo>(theta, n, blk0, step, probe_a, probe_b, key,
+                                                 abits, bbits, bits_a, bits_b, num_cus, stream);
+    constexpr uint64_t kElem = kBF16 ? 2 : 4;
+    for (uint64_t s0 = 0; s0 < n; s0 += slice) {
+        const uint64_t m = (n - s0) < slice ? (n - s0) : slice;
+        const hipError_t e = perturb_range<kBF16, kBits, kTwo>(
+            static_cast<char *>(theta) + s0 * kElem, m, blk0 + s0 / kBlockParams, step, probe_a,
+            probe_b, key, abits, bbits, bits_a ? bits_a + s0 / 8 : nullptr,
+            bits_b ? bits_b + s0 / 8 : nullptr, num_cus, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_perturb(void *theta, bool bf16, uint64_t offset, uint64_t n, Key key,
                           uint32_t step, uint32_t probe, float alpha, const uint8_t *bits,
-                          int num_cus, hipStream_t stream)
+                          int num_cus, hipStream_t stream, uint64_t slice)
 {
-    const uint32_t abits = __builtin_bit_cast(uint32_t, alpha);
-    const uint64_t blk0 = offset / kBlockParams;
+    const uint32_t ab = __builtin_bit_cast(uint32_t, alpha);
+    const uint64_t b0 = offset / kBlockParams;
     if (bf16)
-        return bits ? perturb_impl<true, true, false>(theta, n, blk0, step, probe, probe, key,
-                                                      abits, 0u, bits, nullptr, num_cus, stream)
-                    : perturb_impl<true, false, false>(theta, n, blk0, step, probe, probe, key,
-                                                       abits, 0u, nullptr, nullptr, num_cus,
+        return bits ? perturb_impl<true, true, false>(theta, n, b0, step, probe, probe, key, ab,
+                                                      0u, bits, nullptr, slice, num_cus, stream)
+                    : perturb_impl<true, false, false>(theta, n, b0, step, probe, probe, key, ab,
+                                                       0u, nullptr, nullptr, slice, num_cus,
                                                        stream);
-    return bits ? perturb_impl<false, true, false>(theta, n, blk0, step, probe, probe, key,
-                                                   abits, 0u, bits, nullptr, num_cus, stream)
-                : perturb_impl<false, false, false>(theta, n, blk0, step, probe, probe, key,
-                                                    abits, 0u, nullptr, nullptr, num_cus,
-                                                    stream);
+    return bits ? perturb_impl<false, true, false>(theta, n, b0, step, probe, probe, key, ab, 0u,
+                                                   bits, nullptr, slice, num_cus, stream)
+                : perturb_impl<false, false, false>(theta, n, b0, step, probe, probe, key, ab, 0u,
+                                                    nullptr, nullptr, slice, num_cus, stream);
 }
 
 hipError_t launch_perturb2(void *theta, bool bf16, uint64_t offset, uint64_t n, Key key,
                            uint32_t step, uint32_t probe_a, float alpha_a, uint32_t probe_b,
                            float alpha_b, const uint8_t *bits_a, const uint8_t *bits_b,
-                           int num_cus, hipStream_t stream)
+                           int num_cus, hipStream_t stream, uint64_t slice)
 {
-    const uint32_t abits = __builtin_bit_cast(uint32_t, alpha_a);
-    const uint32_t bbits = __builtin_bit_cast(uint32_t, alpha_b);
-    const uint64_t blk0 = offset / kBlockParams;
+    const uint32_t ab = __builtin_bit_cast(uint32_t, alpha_a);
+    const uint32_t bb = __builtin_bit_cast(uint32_t, alpha_b);
+    const uint64_t b0 = offset / kBlockParams;
+    const uint32_t pa = probe_a, pb = probe_b;
     if (bf16)
-        return bits_a ? perturb_impl<true, true, true>(theta, n, blk0, step, probe_a, probe_b,
-                                                       key, abits, bbits, bits_a, bits_b,
-                                                       num_cus, stream)
-                      : perturb_impl<true, false, true>(theta, n, blk0, step, probe_a, probe_b,
-                                                        key, abits, bbits, nullptr, nullptr,
-                                                        num_cus, stream);
-    return bits_a ? perturb_impl<false, true, true>(theta, n, blk0, step, probe_a, probe_b, key,
-                                                    abits, bbits, bits_a, bits_b, num_cus,
-                                                    stream)
-                  : perturb_impl<false, false, true>(theta, n, blk0, step, probe_a, probe_b,
-                                                     key, abits, bbits, nullptr, nullptr,
-                                                     num_cus, stream);
+        return bits_a ? perturb_impl<true, true, true>(theta, n, b0, step, pa, pb, key, ab, bb,
+                                                       bits_a, bits_b, slice, num_cus, stream)
+                      : perturb_impl<true, false, true>(theta, n, b0, step, pa, pb, key, ab, bb,
+                                                        nullptr, nullptr, slice, num_cus, stream);
+    return bits_a ? perturb_impl<false, true, true>(theta, n, b0, step, pa, pb, key, ab, bb,
+                                                    bits_a, bits_b, slice, num_cus, stream)
+                  : perturb_impl<false, false, true>(theta, n, b0, step, pa, pb, key, ab, bb,
+                                                     nullptr, nullptr, slice, num_cus, stream);
 }
 
 }  // namespace zo

@@ -16,17 +16,22 @@ hipError_t launch_gen_probes(Key key, uint32_t step, uint32_t probe0, uint32_t n
                              uint64_t offset, uint64_t n, uint8_t *bits, int num_cus,
                              hipStream_t stream);
 
-// theta[0..n) += alpha * z (fp32 or bf16), bits == nullptr regenerates.
+// Params per streaming chunk of the perturb kernel; slice lengths are multiples of it.
+constexpr uint64_t kPerturbChunkParams = 8192;
+
+// theta[0..n) += alpha * z (fp32 or bf16), bits == nullptr regenerates.  slice > 0 (a
+// multiple of kPerturbChunkParams) issues the pass as one launch per slice of that many
+// params; 0 is one launch.
 hipError_t launch_perturb(void *theta, bool bf16, uint64_t offset, uint64_t n, Key key,
                           uint32_t step, uint32_t probe, float alpha, const uint8_t *bits,
-                          int num_cus, hipStream_t stream);
+                          int num_cus, hipStream_t stream, uint64_t slice = 0);
 
 // theta[0..n) += (+/-alpha_a) + (+/-alpha_b) in one pass (probes a and b); bits_a and
-// bits_b are both given or both nullptr.
+// bits_b are both given or both nullptr.  slice as launch_perturb.
 hipError_t launch_perturb2(void *theta, bool bf16, uint64_t offset, uint64_t n, Key key,
                            uint32_t step, uint32_t probe_a, float alpha_a, uint32_t probe_b,
                            float alpha_b, const uint8_t *bits_a, const uint8_t *bits_b,
-                           int num_cus, hipStream_t stream);
+                           int num_cus, hipStream_t stream, uint64_t slice = 0);
 
 // c[i] from (L+, L-, L0) in fp64; non-finite probes counted into *counter.
 // mode 0: g / max(|h|, delta); 1: g / max(|h|, delta)^power; 2: g / npert (L0 unused).
@@ -75,8 +80,9 @@ hipError_t launch_mlp_loss(const float *params, const float *X, const int64_t *l
                            double *partial, double *out, const MlpPerturb *pert, Key key,
                            hipStream_t stream, double *out_minus = nullptr);
 
-// Diagnostic: every 16-byte word of buf (bytes % 16 == 0) <- word ^ mask, in place.
+// Diagnostic: every 16-byte word of buf (bytes % 16 == 0) <- word ^ mask, in place;
+// slice_bytes > 0 (a multiple of 16 KiB) issues it as one launch per slice of that size.
 hipError_t launch_stream_rmw(void *buf, uint64_t bytes, uint32_t mask, int num_cus,
-                             hipStream_t stream);
+                             hipStream_t stream, uint64_t slice_bytes = 0);
 
 }  // namespace zo

@@ -275,6 +275,27 @@ zo_status zo_mlp_loss_pair(zo_ctx *ctx, const float *d_params, uint64_t offset, 
  * bytes > 0, bytes not a multiple of 16. */
 zo_status zo_stream_rmw(zo_ctx *ctx, void *d_buf, uint64_t bytes, uint32_t mask, void *stream);
 
+/* Placement of a large parameter buffer, a property of MI355X's HBM rather than of the
+ * method (the callers are those who stream a buffer in place many times, as every pass of
+ * a step does): the bandwidth one launch reaches over a large buffer depends on where the
+ * allocation's physical memory lies -- the eight XCDs each stream their own eighth of the
+ * buffer, and on some placements those far-apart streams hold writes well below what the
+ * memory allows -- while a pass issued as consecutive launches over 512 MiB slices runs
+ * at the same rate on every placement.  zo_tune_placement times both forms on the
+ * caller's buffer (a read and write-back of every word, contents unchanged; synchronizes
+ * `stream`), keeps the faster in the context, and reports both (GB/s of in-place traffic;
+ * the sliced figure is 0 for buffers under 1 GiB, which always use one launch).  From then
+ * on zo_perturb, zo_perturb2 and zo_stream_rmw on this context issue their passes in that
+ * form; results do not depend on it.  zo_set_slice_bytes sets the form directly (0: one
+ * launch per pass; otherwise a multiple of 1 MiB), zo_get_slice_bytes reads it.
+ * Errors (ZO_EINVAL): NULL ctx, NULL or misaligned d_buf, bytes not a multiple of 16,
+ * slice bytes not a multiple of 1 MiB; ZO_EHIP if the runtime reports an error. */
+zo_status zo_tune_placement(zo_ctx *ctx, void *d_buf, uint64_t bytes, void *stream,
+                            uint64_t *out_slice_bytes, double *out_gbps_whole,
+                            double *out_gbps_sliced);
+zo_status zo_set_slice_bytes(zo_ctx *ctx, uint64_t slice_bytes);
+uint64_t zo_get_slice_bytes(const zo_ctx *ctx);
+
 #ifdef __cplusplus
 }
 #endif

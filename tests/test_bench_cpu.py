@@ -21,7 +21,7 @@ def test_stored_traffic_is_used_only_for_its_source_and_workload():
     with open(bench.TRAFFIC_FILE) as f:
         t = json.load(f)
     if t["source_sha256"] == bench.source_hash(bench.PERTURB_SOURCES):
-        assert bench.stored_traffic(t["workload"], 0.0) == float(t["bytes_per_dispatch"])
+        assert bench.stored_traffic(t["workload"], 0.0) == float(t["bytes_per_pass"])
     else:
         assert bench.stored_traffic(t["workload"], 0.0) is None
     assert bench.stored_traffic("some/other-workload", 0.0) is None

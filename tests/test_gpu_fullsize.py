@@ -42,10 +42,11 @@ def _take(t, starts, kind):
     return out
 
 
-def _run_and_check(t, M, kind, seed, npert, eps, eta, label):
-    starts = _windows(M, 24, seed=M % 1000)
+def _run_and_check(t, M, kind, seed, npert, eps, eta, label, slice_bytes=0, extra_starts=()):
+    starts = sorted(set(_windows(M, 24, seed=M % 1000)) | set(extra_starts))
     before = _take(t, starts, kind)
     ctx = zo.zo_init(seed)
+    zo.zo_set_slice_bytes(ctx, slice_bytes)
     a = float(np.float32(eps))
     c = (np.random.default_rng(7).standard_normal(npert) * 2.5e-3).astype(np.float32)
     print(f"[fullsize] {label}: M={M} passes", flush=True)
@@ -207,3 +208,19 @@ def test_opt30b_restore_update_equals_two_calls_everywhere():
     del a, b
     torch.cuda.empty_cache()
     assert same
+
+
+def test_opt30b_passes_in_slices():
+    """The bench's calls with the passes issued per 512 MiB slice (the form zo_tune_placement
+    picks on slow placements), with windows straddling slice boundaries."""
+    cfg = CONFIGS["opt30b"]
+    t = torch.empty(cfg.M, dtype=torch.bfloat16, device="cuda")
+    gen.device_normal_(t, cfg.theta_std, cfg.seed)
+    per = (512 << 20) // 2                                  # params per slice
+    extra = [per - WIN // 2, 17 * per - WIN // 2, (cfg.M // per) * per - WIN // 2]
+    n = _run_and_check(t, cfg.M, "bf16", cfg.seed, cfg.npert, cfg.eps, 1.0, "opt30b sliced",
+                       slice_bytes=512 << 20, extra_starts=extra)
+    assert n >= 20
+    del t
+    torch.cuda.empty_cache()
+

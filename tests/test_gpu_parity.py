@@ -531,3 +531,50 @@ def test_stream_rmw_argument_checks(ctx):
     assert L.zo_stream_rmw(ctx.handle, t.data_ptr(), 20, 0, None) == zo.ZO_EINVAL      # size % 16
     assert L.zo_stream_rmw(ctx.handle, t.data_ptr() + 4, 16, 0, None) == zo.ZO_EINVAL  # alignment
     assert L.zo_stream_rmw(ctx.handle, None, 0, 0, None) == zo.ZO_OK                    # empty
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["regen", "bits"])
+def test_sliced_passes_equal_the_oracle(kind, mode):
+    """Passes issued per 1 MiB slice (seven slices and a ragged tail, at a non-zero offset):
+    zo_perturb and zo_perturb2 stay bit-exact with the oracle, slice boundaries included."""
+    n = 3_300_001 if kind == "bf16" else 1_700_003
+    offset, step = 128 * 5, 8
+    local = zo.zo_init(SEED)
+    zo.zo_set_slice_bytes(local, 1 << 20)
+    assert zo.zo_get_slice_bytes(local) == 1 << 20
+    h = _theta(kind, n, seed=n, scale=0.02, specials=True)
+    t = _dev(kind, h)
+    if mode == "bits":
+        bh = [oracle.gen_plane(SEED, step, p, offset, n) for p in (2, 3)]
+        bd = zo.zo_gen_probes(local, step, 2, 2, offset, n)
+        rows = (bd[0], bd[1])
+    else:
+        bh, rows = [None, None], (None, None)
+    zo.zo_perturb(local, t, offset, step, 2, 1e-3, rows[0])
+    oracle.perturb(h, offset, SEED, step, 2, 1e-3, bh[0])
+    zo.zo_perturb2(local, t, offset, step, 2, 1e-3, 3, -2e-3, rows[0], rows[1])
+    oracle.perturb2(h, offset, SEED, step, 2, 1e-3, 3, -2e-3, bh[0], bh[1])
+    assert_same_bits_or_nan(_host(kind, t), h, kind)
+    local.close()
+
+
+def test_tune_placement_keeps_the_buffer_and_chooses_a_form():
+    local = zo.zo_init(SEED)
+    rng = np.random.default_rng(4)
+    host = rng.integers(0, 2 ** 16, 1 << 30, dtype=np.uint16)           # 2 GiB of bf16 bits
+    t = torch.from_numpy(host.view(np.int16)).cuda()
+    r = zo.zo_tune_placement(local, t)
+    assert r["slice_bytes"] in (0, 512 << 20)
+    assert r["gbps_whole"] > 100 and r["gbps_sliced"] > 100
+    assert zo.zo_get_slice_bytes(local) == r["slice_bytes"]
+    assert np.array_equal(t.cpu().numpy().view(np.uint16), host)        # contents unchanged
+    small = torch.zeros(1 << 20, dtype=torch.int32, device="cuda")      # 4 MiB: one launch
+    r2 = zo.zo_tune_placement(local, small)
+    assert r2["slice_bytes"] == 0 and r2["gbps_sliced"] == 0.0
+    with pytest.raises(zo.ZOError):
+        zo.zo_set_slice_bytes(local, 1000)                               # not a multiple of 1 MiB
+    zo.zo_set_slice_bytes(local, 0)
+    assert zo.zo_get_slice_bytes(local) == 0
+    local.close()
+

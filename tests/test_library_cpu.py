@@ -62,6 +62,9 @@ def test_null_context_and_arguments_are_rejected():
     assert L.zo_stream_rmw(None, None, 16, 0, None) == _lib.ZO_EINVAL
     assert L.zo_restore_update(None, None, 0, 0, 16, 0, 0, 1.0, None, 1, 1.0, None,
                                None) == _lib.ZO_EINVAL
+    assert L.zo_set_slice_bytes(None, 0) == _lib.ZO_EINVAL
+    assert L.zo_get_slice_bytes(None) == 0
+    assert L.zo_tune_placement(None, None, 16, None, None, None, None) == _lib.ZO_EINVAL
     assert L.zo_mlp_loss_pair(None, None, 0, 0, 0, 1.0, None, None, None, 16, 16, 16, 2, None,
                               0, None, None, None) == _lib.ZO_EINVAL
 
