@@ -30,7 +30,11 @@
 //    reads before the update, folded into the update's single pass over theta.  That
 //    probe's bits are produced by the update anyway: after the octet exchange of its group,
 //    lane r holds word r/2 of every probe of the group, whose half r%2 is the 16 sign bits
-//    of the lane's own params, so the fold costs no extra Philox call.
+//    of the lane's own params, so the fold costs no extra Philox call.  (The unrolled
+//    form below takes them from one Philox call of their own per lane and block instead.)
+//  * Unrolled form.  At the group counts of the usual probe counts (2, 4, 8, 20 groups) the
+//    group loop is unrolled and the tables sit at fixed LDS addresses, so each lookup's
+//    table offset is an immediate of the LDS read and its index one byte-select shift.
 #include <stdlib.h>
 
 #include "zo_device.hpp"
@@ -171,11 +175,16 @@ __device__ __forceinline__ void apply_update(void *theta, uint64_t e0, uint64_t 
     }
 }
 
-// Occupancy is bounded by the dynamic LDS (sign tables + exchange, ~42 KiB per 512-thread
+// Occupancy is bounded by the LDS (sign tables + exchange, ~50 KiB per 512-thread
 // workgroup at n_pert = 160: three workgroups, six waves per SIMD), which the compiler
-// cannot see; telling it so lets it keep several table lookups in flight instead of
-// squeezing registers for an occupancy the LDS never allows.
-template <bool kBF16, bool kBits, bool kRestore>
+// cannot see for the dynamic-LDS form; telling it so lets it keep several table lookups in
+// flight instead of squeezing registers for an occupancy the LDS never allows.
+//
+// kNG > 0: the group count is a compile-time constant; the tables and the exchange slices
+// are static LDS at known addresses and the group loop is unrolled, so every table read
+// carries its group's table offset as the instruction's immediate offset and the lookup
+// index costs a single byte-select shift.  kNG == 0: any group count, tables in dynamic LDS.
+template <bool kBF16, bool kBits, bool kRestore, int kNG>
 __global__ __launch_bounds__(kUpdThreads) __attribute__((amdgpu_waves_per_eu(6, 6))) void k_update(void *__restrict__ theta, uint64_t n,
                                                         uint64_t blk0, uint32_t step,
                                                         uint32_t k0, uint32_t k1,
@@ -186,13 +195,17 @@ __global__ __launch_bounds__(kUpdThreads) __attribute__((amdgpu_waves_per_eu(6, 
                                                         uint64_t stride, uint32_t rprobe,
                                                         uint32_t rabits)
 {
+    __shared__ double stbl[kNG > 0 ? kNG * 256 : 1];
+    __shared__ uint32_t sxch[kNG > 0 ? kUpdWavesPerWG * kXchWordsPerWave : 1];
     extern __shared__ double lds_d[];
-    double *tbl = lds_d;
+    const uint32_t ng = kNG > 0 ? (uint32_t)kNG : ngroups;
+    double *tbl = kNG > 0 ? stbl : lds_d;
     const int wv = threadIdx.x / kWave;
-    uint32_t *xch = reinterpret_cast<uint32_t *>(lds_d + ngroups * 256u) + wv * kXchWordsPerWave;
+    uint32_t *xch = (kNG > 0 ? sxch : reinterpret_cast<uint32_t *>(lds_d + ngroups * 256u)) +
+                    wv * kXchWordsPerWave;
 
     // Signed partial-sum tables, probes ascending within each group.
-    for (uint32_t e = threadIdx.x; e < ngroups * 256u; e += blockDim.x) {
+    for (uint32_t e = threadIdx.x; e < ng * 256u; e += blockDim.x) {
         const uint32_t g = e >> 8, b = e & 255u;
         double acc = 0.0;
 #pragma unroll
@@ -224,18 +237,38 @@ __global__ __launch_bounds__(kUpdThreads) __attribute__((amdgpu_waves_per_eu(6, 
 #pragma unroll
         for (int q = 0; q < 16; ++q) s[q] = 0.0;
         uint32_t rmask = 0;   // kRestore: bit q = sign bit of probe rprobe at param e0 + q
+        // The lane's probe slot, opaque to the optimiser inside this loop: with the group
+        // loop unrolled, everything derived from it per group (the probe's first Philox
+        // product, its bit-row address) would otherwise be hoisted out of the block loop and
+        // held in registers for all groups at once.
+        uint32_t rr = (uint32_t)r;
+        if constexpr (kNG > 0) {
+            asm volatile("" : "+v"(rr));
+            if constexpr (kRestore) {
+                // The restore probe's bits for the lane's 16 params from their own Philox
+                // call (word r/2, half r%2), instead of picking them out of whichever
+                // unrolled group holds that probe.
+                const U32x4 q = probe_block_bits(blk0 + lb, rprobe, step, k0, k1);
+                const uint32_t h = rr >> 1;
+                const uint32_t word = h == 0 ? q.x : h == 1 ? q.y : h == 2 ? q.z : q.w;
+                rmask = (word >> (16u * (rr & 1u))) & 0xFFFFu;
+            }
+        }
 
-        for (uint32_t g = 0; g < ngroups; ++g) {
-            const uint32_t i = g * 8u + (uint32_t)r;
+        auto group = [&](uint32_t g) {
+            const uint32_t i = g * 8u + rr;
             u32x4_t w = {0u, 0u, 0u, 0u};
-            if (i < npert) {
-                if constexpr (kBits) {
-                    if (lb < nblk)
-                        w = *reinterpret_cast<const u32x4_t *>(bits + (uint64_t)i * stride + lb * 16u);
-                } else {
-                    const U32x4 q = probe_block_bits(blk0 + lb, i, step, k0, k1);
-                    w = u32x4_t{q.x, q.y, q.z, q.w};
-                }
+            if constexpr (kBits) {
+                if (i < npert && lb < nblk)
+                    w = *reinterpret_cast<const u32x4_t *>(bits + (uint64_t)i * stride + lb * 16u);
+            } else if (kNG > 0) {
+                // Probes past n_pert carry c = 0: their table entries do not depend on the
+                // bits, so they are generated unconditionally (no divergent branch).
+                const U32x4 q = probe_block_bits(blk0 + lb, i, step, k0, k1);
+                w = u32x4_t{q.x, q.y, q.z, q.w};
+            } else if (i < npert) {
+                const U32x4 q = probe_block_bits(blk0 + lb, i, step, k0, k1);
+                w = u32x4_t{q.x, q.y, q.z, q.w};
             }
             wave_lds_sync();  // previous group's reads precede these writes
             oxch[0 * 8 + r] = w.x;
@@ -256,7 +289,7 @@ __global__ __launch_bounds__(kUpdThreads) __attribute__((amdgpu_waves_per_eu(6, 
             uint32_t Hhi = __builtin_amdgcn_perm(b23, b01, 0x07060302u);
             transpose8x8(Llo, Hlo);
             transpose8x8(Lhi, Hhi);
-            if constexpr (kRestore) {
+            if constexpr (kRestore && kNG == 0) {
                 if (g == (rprobe >> 3)) {   // uniform: the restore probe's group
                     const uint32_t k = rprobe & 3u;
                     const u32x4_t &wk = (rprobe & 4u) ? b : a;
@@ -272,6 +305,17 @@ __global__ __launch_bounds__(kUpdThreads) __attribute__((amdgpu_waves_per_eu(6, 
                 s[8 + q] += tg[(Lhi >> (8 * q)) & 255u];
                 s[12 + q] += tg[(Hhi >> (8 * q)) & 255u];
             }
+        };
+        if constexpr (kNG > 0) {
+#pragma unroll
+            for (int g = 0; g < kNG; ++g) {
+                group((uint32_t)g);
+                // Keep each group's work together: interleaving groups only raises the
+                // register demand past the occupancy budget (and spills).
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            for (uint32_t g = 0; g < ngroups; ++g) group(g);
         }
         apply_update<kBF16, kRestore>(theta, e0, n, s, eta, rmask, rabits);
     }
@@ -287,17 +331,19 @@ static int env_int(const char *name, int dflt)
     return (v >= 1 && v <= 64) ? v : dflt;
 }
 
-template <bool kBF16, bool kBits, bool kRestore>
-static hipError_t update_impl(void *theta, uint64_t n, uint64_t blk0, uint32_t step, Key key,
-                              const float *c, uint32_t npert, float eta, const uint8_t *bits,
-                              uint32_t rprobe, float ralpha, int num_cus, hipStream_t stream)
+template <bool kBF16, bool kBits, bool kRestore, int kNG>
+static hipError_t update_launch(void *theta, uint64_t n, uint64_t blk0, uint32_t step, Key key,
+                                const float *c, uint32_t npert, float eta, const uint8_t *bits,
+                                uint32_t rprobe, float ralpha, int num_cus, hipStream_t stream)
 {
     const uint32_t ngroups = (npert + 7u) / 8u;
-    const size_t lds = (size_t)ngroups * 256u * 8u + (size_t)kUpdWavesPerWG * kXchWordsPerWave * 4u;
+    const size_t lds = kNG > 0 ? 0
+                               : (size_t)ngroups * 256u * 8u +
+                                     (size_t)kUpdWavesPerWG * kXchWordsPerWave * 4u;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&k_update<kBF16, kBits, kRestore>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            reinterpret_cast<const void *>(&k_update<kBF16, kBits, kRestore, kNG>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     const uint64_t nblk = (n + kBlockParams - 1) / kBlockParams;
@@ -309,11 +355,39 @@ static hipError_t update_impl(void *theta, uint64_t n, uint64_t blk0, uint32_t s
     const uint64_t want = (nwc + kUpdWavesPerWG - 1) / kUpdWavesPerWG;
     const uint64_t cap = (uint64_t)num_cus * wg_per_cu;
     const uint32_t grid = (uint32_t)(want < cap ? want : cap);
-    hipLaunchKernelGGL((k_update<kBF16, kBits, kRestore>), dim3(grid), dim3(kUpdThreads), lds,
-                       stream, theta, n, blk0, step, key.k0, key.k1, c, npert, ngroups,
+    hipLaunchKernelGGL((k_update<kBF16, kBits, kRestore, kNG>), dim3(grid), dim3(kUpdThreads),
+                       lds, stream, theta, n, blk0, step, key.k0, key.k1, c, npert, ngroups,
                        (double)eta, bits, (uint64_t)nblk * 16u, rprobe,
                        __builtin_bit_cast(uint32_t, ralpha));
     return hipGetLastError();
+}
+
+// Group counts with an unrolled kernel (probes regenerated): those of n_pert = 16, 32, 64 and
+// 160.  Other counts, and stored bits (a streaming read that the unrolled form does not
+// speed up), take the general kernel.  ZO_UPDATE_GENERIC=1 forces the general kernel.
+template <bool kBF16, bool kBits, bool kRestore>
+static hipError_t update_impl(void *theta, uint64_t n, uint64_t blk0, uint32_t step, Key key,
+                              const float *c, uint32_t npert, float eta, const uint8_t *bits,
+                              uint32_t rprobe, float ralpha, int num_cus, hipStream_t stream)
+{
+    static const bool generic = env_int("ZO_UPDATE_GENERIC", 0) == 1;
+    const uint32_t ngroups = (npert + 7u) / 8u;
+#define ZO_UPD(NG)                                                                           \
+    update_launch<kBF16, kBits, kRestore, NG>(theta, n, blk0, step, key, c, npert, eta, bits, \
+                                              rprobe, ralpha, num_cus, stream)
+    if constexpr (!kBits) {
+        if (!generic) {
+            switch (ngroups) {
+            case 2: return ZO_UPD(2);
+            case 4: return ZO_UPD(4);
+            case 8: return ZO_UPD(8);
+            case 20: return ZO_UPD(20);
+            default: break;
+            }
+        }
+    }
+    return ZO_UPD(0);
+#undef ZO_UPD
 }
 
 template <bool kRestore>

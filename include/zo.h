@@ -36,7 +36,8 @@
  *    on it must be made with that device current, or it returns ZO_EINVAL.
  *  - Launch shapes: ZO_PERTURB_WG_PER_CU (default 8) and ZO_UPDATE_WG_PER_CU (default 16)
  *    override the workgroups per CU of the perturb and update kernels, read once per
- *    process, accepted in [1, 64].  Results do not depend on them.
+ *    process, accepted in [1, 64].  Results do not depend on them.  ZO_UPDATE_GENERIC=1
+ *    makes the update use its general kernel at every probe count (same results).
  */
 #ifndef ZO_H
 #define ZO_H

@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import forward_only_amd as zo
+from forward_only_amd import placement
 import oracle
 from forward_only_amd.step import spsa_step
 from gpu_util import (assert_bf16_within_ulp, assert_f32_update_close, assert_same_bits_or_nan,
@@ -172,8 +173,11 @@ def test_probe_weights_nonfinite_clean_loss(ctx):
 # ------------------------------------------------------------------------------------
 # update
 # ------------------------------------------------------------------------------------
+# n_pert 16, 29-32, 64 and 153-160 take the unrolled kernel (group counts 2, 4, 8, 20; 153
+# and 29 with zero-weight padding probes), the others the general one.
 UPDATE_CASES = [(4096, 0, 16), (1000, 128, 7), (8192 * 3 + 1000, 0, 160), (1, 0, 1),
-                (2_368_514, 0, 64), (33333, 128 * 3, 512), (8192, 0, 9)]
+                (2_368_514, 0, 64), (33333, 128 * 3, 512), (8192, 0, 9),
+                (8192 * 2 + 77, 128, 153), (50000, 0, 32), (3000, 128 * 2, 29)]
 
 
 @pytest.mark.parametrize("kind", ["f32", "bf16"])
@@ -202,7 +206,8 @@ def test_update_parity(ctx, kind, n, offset, npert, mode):
 
 
 RESTORE_CASES = [(4096, 0, 16, 15), (1000, 128, 7, 3), (8192 * 3 + 1000, 0, 160, 159),
-                 (1, 0, 1, 0), (33333, 128 * 3, 512, 300), (8192 * 13 + 5, 128, 160, 8)]
+                 (1, 0, 1, 0), (33333, 128 * 3, 512, 300), (8192 * 13 + 5, 128, 160, 8),
+                 (8192 * 2 + 77, 128, 153, 152), (50000, 0, 32, 20)]
 
 
 @pytest.mark.parametrize("kind", ["f32", "bf16"])
@@ -557,6 +562,32 @@ def test_sliced_passes_equal_the_oracle(kind, mode):
     oracle.perturb2(h, offset, SEED, step, 2, 1e-3, 3, -2e-3, bh[0], bh[1])
     assert_same_bits_or_nan(_host(kind, t), h, kind)
     local.close()
+
+
+def test_relocate_keeps_the_contents_on_the_fastest_allocation():
+    """placement.relocate: the buffer it returns holds the original contents, is the fastest
+    of the allocations it tried (or the original when none beat it), and the context's pass
+    form is the one tuned for it.  The search is forced (no placement counts as fast) so that
+    a candidate is usually kept and the copy path runs."""
+    local = zo.zo_init(SEED)
+    rng = np.random.default_rng(5)
+    host = rng.integers(0, 2 ** 16, 1 << 30, dtype=np.uint16)           # 2 GiB of bf16 bits
+    t = torch.from_numpy(host.view(np.int16)).cuda()
+    out, rep = placement.relocate(local, t, tries=2, fast_ratio=100.0, min_gain=0.0)
+    assert not rep["skipped"]
+    assert 1 <= len(rep["tried"]) <= 3
+    rates = [max(r["gbps_whole"], r["gbps_sliced"]) for r in rep["tried"]]
+    assert rates[rep["kept"]] == max(rates)
+    assert rep["copied"] == (rep["kept"] != 0)
+    assert (out is t) == (rep["kept"] == 0)
+    assert out.shape == t.shape and out.dtype == t.dtype
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), host)
+    assert zo.zo_get_slice_bytes(local) == rep["final"]["slice_bytes"]
+    small = torch.zeros(1000, dtype=torch.float32, device="cuda")
+    o2, r2 = placement.relocate(local, small)
+    assert o2 is small and r2["skipped"]
+    del out, t
+    torch.cuda.empty_cache()
 
 
 def test_tune_placement_keeps_the_buffer_and_chooses_a_form():
