@@ -5,6 +5,9 @@
 //
 //   hbm_ceiling [GB] [rounds]   (default 59.92 GB, the OPT-30B-shaped bf16 parameter set;
 //                                3 rounds)
+//   hbm_ceiling --allocations [GB] [count]   in-place RMW speed of successive allocations:
+//                                count rounds of allocate / measure / free, then up to count
+//                                allocations held at once (default 59.92 GB, 6)
 //
 // Each kernel walks 16 KiB chunks per wave (16 dwordx4 per lane, one contiguous KiB per
 // instruction) in the same order as the perturb kernel: the buffer is split into eight
@@ -19,6 +22,7 @@
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -126,8 +130,57 @@ static float time_ms(F launch, int iters)
     return ms / iters;
 }
 
+// In-place RMW bandwidth of one buffer, one launch of 8 workgroups per CU (the perturb
+// kernel's default shape).
+static double rmw_gbps(char *buf, uint64_t nchunks, int cus)
+{
+    u32x4_t *p = reinterpret_cast<u32x4_t *>(buf);
+    const int grid = cus * 8;
+    return 2.0 * nchunks * kChunk16 * 16 /
+           (time_ms([&] { hipLaunchKernelGGL(k_rmw, dim3(grid), dim3(256), 0, 0, p, nchunks); }, 3) * 1e6);
+}
+
+// --allocations mode: the placement of successive allocations of one size.  First `count`
+// rounds of allocate / measure / free, then up to `count` allocations held at once (while
+// free memory stays above the size plus 4 GiB), each measured as it is made.
+static int allocations(double gb, int count)
+{
+    int cus = 0;
+    CHECK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0));
+    const uint64_t chunk_bytes = kChunk16 * 16;
+    const uint64_t nchunks = (uint64_t)(gb * 1e9) / chunk_bytes;
+    const uint64_t bytes = nchunks * chunk_bytes;
+    size_t fr, tot;
+    CHECK(hipMemGetInfo(&fr, &tot));
+    printf("allocations of %.3f GB; device memory free %.1f of %.1f GB; in-place RMW, 8 "
+           "workgroups per CU\n", bytes / 1e9, fr / 1e9, tot / 1e9);
+    for (int r = 0; r < count; ++r) {
+        char *buf;
+        CHECK(hipMalloc(&buf, bytes));
+        CHECK(hipMemset(buf, 0, bytes));
+        printf("allocate-measure-free %d: %.0f GB/s\n", r, rmw_gbps(buf, nchunks, cus));
+        fflush(stdout);
+        CHECK(hipFree(buf));
+    }
+    char *held[16];
+    int nh = 0;
+    while (nh < count && nh < 16) {
+        CHECK(hipMemGetInfo(&fr, &tot));
+        if (fr < bytes + (4ull << 30)) break;
+        CHECK(hipMalloc(&held[nh], bytes));
+        CHECK(hipMemset(held[nh], 0, bytes));
+        printf("held %d: %.0f GB/s\n", nh, rmw_gbps(held[nh], nchunks, cus));
+        fflush(stdout);
+        ++nh;
+    }
+    for (int i = 0; i < nh; ++i) CHECK(hipFree(held[i]));
+    return 0;
+}
+
 int main(int argc, char **argv)
 {
+    if (argc > 1 && strcmp(argv[1], "--allocations") == 0)
+        return allocations(argc > 2 ? atof(argv[2]) : 59.919663104, argc > 3 ? atoi(argv[3]) : 6);
     const double gb = argc > 1 ? atof(argv[1]) : 59.919663104;
     const int rounds = argc > 2 ? atoi(argv[2]) : 3;
     int cus = 0;
