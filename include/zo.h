@@ -22,7 +22,11 @@
  *    first (the four Philox words of each 128-param block, little-endian).  Bits past n in
  *    the last block are Philox bits and are never applied.
  *  - Every compute call is asynchronous on `stream` (a hipStream_t; NULL = the null
- *    stream).  The caller owns every buffer; hot-path calls allocate nothing.
+ *    stream).  The caller owns every buffer; hot-path calls allocate nothing.  The step's
+ *    calls (zo_perturb, zo_perturb2, zo_probe_weights, zo_update, zo_restore_update) only
+ *    launch kernels -- no allocation, host synchronisation or memset node (counters are
+ *    cleared by a kernel) -- so they can be recorded into a HIP graph and replayed.
+ *    zo_nonfinite_count and zo_tune_placement synchronise and cannot.
  *  - Return values report argument and launch errors only: ZO_EINVAL is returned before
  *    anything is launched, ZO_EHIP when the HIP runtime reports an error.  Numeric
  *    trouble is not an error (see zo_probe_weights).  n == 0 (or n_pert == 0) is a

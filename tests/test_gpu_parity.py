@@ -486,6 +486,52 @@ def test_bf16_synthetic_two_pass_step_small(ctx):
     assert np.array_equal(bf16_bits(t), h)
 
 
+@pytest.mark.parametrize("kind,npert", [("bf16", 16), ("f32", 160)])
+def test_step_calls_replay_from_a_captured_graph(ctx, kind, npert):
+    """The library's calls of one two-pass step (passes, fused passes, weights, the update
+    carrying the last restore) captured into a HIP graph: no allocation, synchronisation or
+    memset node in them, so each replay equals the same calls made eagerly, replay after
+    replay, with eager work and synchronisations in between."""
+    n, step = 8192 * 5 + 77, 4
+    h = _theta(kind, n, seed=17, scale=0.02)
+    a = 1e-3 if kind == "bf16" else 2.0 ** -10
+    L0, Lp, Lm = gen.synthetic_losses(5, step, npert)
+    L0d = torch.tensor([L0], dtype=torch.float64).cuda()
+    Lpd, Lmd = torch.from_numpy(Lp).cuda(), torch.from_numpy(Lm).cuda()
+    c_eager = torch.empty(npert, dtype=torch.float32, device="cuda")
+    c_graph = torch.empty(npert, dtype=torch.float32, device="cuda")
+    eta = 1.0 if kind == "bf16" else 1e-2
+
+    def calls(t, c):
+        zo.zo_perturb(ctx, t, 0, step, 0, +a)
+        for i in range(npert):
+            zo.zo_perturb(ctx, t, 0, step, i, -2.0 * a)
+            if i + 1 < npert:
+                zo.zo_perturb2(ctx, t, 0, step, i, +a, i + 1, +a)
+        zo.zo_probe_weights(ctx, Lpd, Lmd, L0d, a, 1e-6, out=c)
+        zo.zo_restore_update(ctx, t, 0, step, npert - 1, +a, c, eta)
+
+    eager, graphed, warm = _dev(kind, h), _dev(kind, h), _dev(kind, h)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls(warm, c_graph)                      # first launches outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls(graphed, c_graph)
+    torch.cuda.synchronize()
+    assert np.array_equal(_host(kind, graphed), _host(kind, _dev(kind, h)))   # not yet run
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        calls(eager, c_eager)
+        torch.cuda.synchronize()
+        assert np.array_equal(_host(kind, graphed), _host(kind, eager))
+        assert torch.equal(c_graph, c_eager)
+
+
 # ------------------------------------------------------------------------------------
 # the other weight forms of the pages
 # ------------------------------------------------------------------------------------
