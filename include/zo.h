@@ -183,7 +183,8 @@ zo_status zo_update(zo_ctx *ctx, void *d_theta, zo_dtype dtype, uint64_t offset,
  * for bit.  This is the last restore of the two-moves-per-probe
  * schedule folded into the update that follows it (the probe weights between them read
  * only the losses), saving one full pass per step; the restore probe's signs come from the
- * update's own sign generation.  Arguments as zo_update, plus restore_probe (< n_pert, a
+ * update's own sign generation (one extra sign call per 128-param block at the probe
+ * counts where the update runs unrolled).  Arguments as zo_update, plus restore_probe (< n_pert, a
  * probe of the same step; with d_bits, its row is used) and restore_alpha (fp32).
  * Errors: as zo_update, and ZO_EINVAL if restore_probe >= n_pert. */
 zo_status zo_restore_update(zo_ctx *ctx, void *d_theta, zo_dtype dtype, uint64_t offset,
@@ -283,10 +284,10 @@ zo_status zo_stream_rmw(zo_ctx *ctx, void *d_buf, uint64_t bytes, uint32_t mask,
 /* Placement of a large parameter buffer, a property of MI355X's HBM rather than of the
  * method (the callers are those who stream a buffer in place many times, as every pass of
  * a step does): the bandwidth one launch reaches over a large buffer depends on where the
- * allocation's physical memory lies -- the eight XCDs each stream their own eighth of the
- * buffer, and on some placements those far-apart streams hold writes well below what the
- * memory allows -- while a pass issued as consecutive launches over 512 MiB slices runs
- * at the same rate on every placement.  zo_tune_placement times both forms on the
+ * allocation's physical memory lies -- on some placements a launch whose waves spread over
+ * the whole buffer holds writes well below what the memory allows -- while a pass issued
+ * as consecutive launches over 512 MiB slices (every wave in flight inside one slice) runs
+ * at nearly the same rate on every placement.  zo_tune_placement times both forms on the
  * caller's buffer (a read and write-back of every word, contents unchanged; synchronizes
  * `stream`), keeps the faster in the context, and reports both (GB/s of in-place traffic;
  * the sliced figure is 0 for buffers under 1 GiB, which always use one launch).  From then
