@@ -51,7 +51,10 @@ def relocate(ctx, buf: torch.Tensor, tries: int = 3, headroom_bytes: int = 8 << 
         free, _total = torch.cuda.mem_get_info(buf.device)
         if free < nbytes + headroom_bytes:
             break
-        cand = torch.empty_like(buf)
+        try:
+            cand = torch.empty_like(buf)
+        except torch.cuda.OutOfMemoryError:       # fragmentation: stop searching
+            break
         r = zo_tune_placement(ctx, cand)
         tried.append(dict(r))
         held.append(cand)

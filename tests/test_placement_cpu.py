@@ -104,3 +104,15 @@ def test_small_buffers_are_skipped(monkeypatch):
     b = torch.zeros(10)
     out, rep = placement.relocate(None, b)
     assert out is b and rep["skipped"] and script.calls == []
+
+
+def test_an_allocation_failure_ends_the_search(fake_device, monkeypatch):
+    script = Script([(5200, 5800), (6200, 5800)])
+    monkeypatch.setattr(zo, "zo_tune_placement", script)
+
+    def no_memory(*a, **k):
+        raise torch.cuda.OutOfMemoryError("no memory")
+    monkeypatch.setattr(torch, "empty_like", no_memory)
+    b = _buf()
+    out, rep = placement.relocate(None, b, tries=3)
+    assert out is b and len(rep["tried"]) == 1 and rep["kept"] == 0
