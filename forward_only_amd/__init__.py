@@ -90,6 +90,30 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
     return t.data_ptr()
 
 
+def _row(bits, n: int, name: str = "bits"):
+    """Device pointer of one probe's packed row over n params: a 1-D uint8 tensor of exactly
+    zo_bits_stride(n) bytes (the library reads that many from the pointer), or None."""
+    if bits is None:
+        return None
+    p = _dev(bits, name, torch.uint8)
+    if bits.dim() != 1 or bits.numel() != zo_bits_stride(n):
+        raise ValueError(f"{name} must be one packed row of {zo_bits_stride(n)} bytes, got "
+                         f"shape {tuple(bits.shape)}")
+    return p
+
+
+def _rows(bits, npert: int, n: int):
+    """Device pointer of n_pert packed rows over n params: a (n_pert, zo_bits_stride(n))
+    uint8 tensor (row i at i * stride), or None."""
+    if bits is None:
+        return None
+    p = _dev(bits, "bits", torch.uint8)
+    if tuple(bits.shape) != (npert, zo_bits_stride(n)):
+        raise ValueError(f"bits must have shape ({npert}, {zo_bits_stride(n)}), got "
+                         f"{tuple(bits.shape)}")
+    return p
+
+
 def zo_init(seed: int) -> Context:
     h = ctypes.c_void_p()
     _lib.check(_lib.lib().zo_init(int(seed) & (2 ** 64 - 1), ctypes.byref(h)), "zo_init")
@@ -121,9 +145,7 @@ def zo_gen_probes(ctx: Context, step: int, probe0: int, n_probes: int, offset: i
 def zo_perturb(ctx: Context, theta: torch.Tensor, offset: int, step: int, probe: int,
                alpha: float, bits: torch.Tensor | None = None, stream=None) -> None:
     """theta <- theta + alpha * z_probe in place (theta fp32 or bf16)."""
-    bp = None if bits is None else _dev(bits, "bits", torch.uint8)
-    if bits is not None and bits.numel() < zo_bits_stride(theta.numel()):
-        raise ValueError("bits row is too short")
+    bp = _row(bits, theta.numel())
     _lib.check(_lib.lib().zo_perturb(ctx.handle, _dev(theta, "theta"), _dtype_code(theta),
                                      offset, theta.numel(), step, probe, float(alpha), bp,
                                      _stream(stream)), "zo_perturb")
@@ -136,11 +158,8 @@ def zo_perturb2(ctx: Context, theta: torch.Tensor, offset: int, step: int, probe
     """theta <- theta + (+/-alpha_a) + (+/-alpha_b) in one pass (probes a and b)."""
     if (bits_a is None) != (bits_b is None):
         raise ValueError("give both packed rows or neither")
-    pa = None if bits_a is None else _dev(bits_a, "bits_a", torch.uint8)
-    pb = None if bits_b is None else _dev(bits_b, "bits_b", torch.uint8)
-    for b in (bits_a, bits_b):
-        if b is not None and b.numel() < zo_bits_stride(theta.numel()):
-            raise ValueError("bits row is too short")
+    pa = _row(bits_a, theta.numel(), "bits_a")
+    pb = _row(bits_b, theta.numel(), "bits_b")
     _lib.check(_lib.lib().zo_perturb2(ctx.handle, _dev(theta, "theta"), _dtype_code(theta),
                                       offset, theta.numel(), step, probe_a, float(alpha_a),
                                       probe_b, float(alpha_b), pa, pb, _stream(stream)),
@@ -173,8 +192,12 @@ def zo_probe_weights_ex(ctx: Context, Lp: torch.Tensor, Lm: torch.Tensor,
     n = Lp.numel()
     if Lm.numel() != n:
         raise ValueError("Lp and Lm must have the same length")
+    if L0 is not None and L0.numel() < 1:
+        raise ValueError("L0 must hold one element")
     if out is None:
         out = torch.empty(n, dtype=torch.float32, device="cuda")
+    if out.numel() < n:
+        raise ValueError("out is too small")
     p0 = None if L0 is None else _dev(L0, "L0", torch.float64)
     _lib.check(_lib.lib().zo_probe_weights_ex(
         ctx.handle, _dev(Lp, "Lp", torch.float64), _dev(Lm, "Lm", torch.float64), p0, n,
@@ -187,11 +210,7 @@ def zo_update(ctx: Context, theta: torch.Tensor, offset: int, step: int, c: torc
               eta: float, bits: torch.Tensor | None = None, stream=None) -> None:
     """theta <- theta - eta * sum_i c_i z_i in place; bits: (n_pert, stride) rows or None."""
     npert = c.numel()
-    bp = None
-    if bits is not None:
-        bp = _dev(bits, "bits", torch.uint8)
-        if bits.numel() < npert * zo_bits_stride(theta.numel()):
-            raise ValueError("bits must hold n_pert rows")
+    bp = _rows(bits, npert, theta.numel())
     _lib.check(_lib.lib().zo_update(ctx.handle, _dev(theta, "theta"), _dtype_code(theta),
                                     offset, theta.numel(), step, _dev(c, "c", torch.float32),
                                     npert, float(eta), bp, _stream(stream)), "zo_update")
@@ -203,11 +222,7 @@ def zo_restore_update(ctx: Context, theta: torch.Tensor, offset: int, step: int,
     """zo_perturb(restore_probe, restore_alpha) then zo_update, in one pass (bit-identical
     to the two calls)."""
     npert = c.numel()
-    bp = None
-    if bits is not None:
-        bp = _dev(bits, "bits", torch.uint8)
-        if bits.numel() < npert * zo_bits_stride(theta.numel()):
-            raise ValueError("bits must hold n_pert rows")
+    bp = _rows(bits, npert, theta.numel())
     _lib.check(_lib.lib().zo_restore_update(
         ctx.handle, _dev(theta, "theta"), _dtype_code(theta), offset, theta.numel(), step,
         int(restore_probe), float(restore_alpha), _dev(c, "c", torch.float32), npert,
@@ -297,11 +312,7 @@ def zo_mlp_loss_perturbed(ctx: Context, params: torch.Tensor, offset: int, step:
     """The MLP loss at params + alpha * z_probe, without writing params."""
     batch, d_in, pp, px, pl, ws, pw, wbytes, out = _mlp_args(params, X, labels, d_hid, d_out,
                                                              workspace, out)
-    bp = None
-    if bits is not None:
-        bp = _dev(bits, "bits", torch.uint8)
-        if bits.numel() < zo_bits_stride(params.numel()):
-            raise ValueError("bits row is too short")
+    bp = _row(bits, params.numel())
     _lib.check(_lib.lib().zo_mlp_loss_perturbed(
         ctx.handle, pp, offset, step, probe, float(alpha), bp, px, pl, batch, d_in, d_hid,
         d_out, pw, wbytes, _dev(out, "out", torch.float64), _stream(stream)),
@@ -320,11 +331,7 @@ def zo_mlp_loss_pair(ctx: Context, params: torch.Tensor, offset: int, step: int,
                                                                   d_out, workspace, out_plus)
     if out_minus is None:
         out_minus = torch.empty(1, dtype=torch.float64, device="cuda")
-    bp = None
-    if bits is not None:
-        bp = _dev(bits, "bits", torch.uint8)
-        if bits.numel() < zo_bits_stride(params.numel()):
-            raise ValueError("bits row is too short")
+    bp = _row(bits, params.numel())
     _lib.check(_lib.lib().zo_mlp_loss_pair(
         ctx.handle, pp, offset, step, probe, float(alpha), bp, px, pl, batch, d_in, d_hid,
         d_out, pw, wbytes, _dev(out_plus, "out_plus", torch.float64),

@@ -5,6 +5,8 @@
 #include "../../include/zo.h"
 #include "zo_launch.hpp"
 
+static_assert(ZO_MAX_NPERT == zo::kMaxNpert, "one probe-count limit");
+
 struct zo_ctx {
     uint64_t seed;
     int device;
@@ -95,7 +97,8 @@ zo_status zo_init(uint64_t seed, zo_ctx **out)
         (void)hipGetLastError();
         return ZO_ENOMEM;
     }
-    if (zo::launch_zero_u32(c->d_counter, 64, nullptr) != hipSuccess ||
+    if (zo::prepare_update() != hipSuccess ||
+        zo::launch_zero_u32(c->d_counter, 64, nullptr) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {
         (void)hipFree(c->d_partials);
         (void)hipFree(c->d_counter);

@@ -321,6 +321,13 @@ __global__ __launch_bounds__(kUpdThreads) __attribute__((amdgpu_waves_per_eu(6, 
     }
 }
 
+// Dynamic LDS of the general kernel: the sign tables of `ngroups` groups and the
+// per-wave exchange slices.
+static size_t general_lds_bytes(uint32_t ngroups)
+{
+    return (size_t)ngroups * 256u * 8u + (size_t)kUpdWavesPerWG * kXchWordsPerWave * 4u;
+}
+
 // Launch-shape override from the environment (read once per process): workgroups per CU,
 // accepted in [1, 64], anything else keeps the default.
 static int env_int(const char *name, int dflt)
@@ -337,15 +344,9 @@ static hipError_t update_launch(void *theta, uint64_t n, uint64_t blk0, uint32_t
                                 uint32_t rprobe, float ralpha, int num_cus, hipStream_t stream)
 {
     const uint32_t ngroups = (npert + 7u) / 8u;
-    const size_t lds = kNG > 0 ? 0
-                               : (size_t)ngroups * 256u * 8u +
-                                     (size_t)kUpdWavesPerWG * kXchWordsPerWave * 4u;
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&k_update<kBF16, kBits, kRestore, kNG>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    // above 64 KiB the general kernel relies on the limit raised once per device by
+    // prepare_update (from zo_init), so that a launch makes no runtime call but the launch
+    const size_t lds = kNG > 0 ? 0 : general_lds_bytes(ngroups);
     const uint64_t nblk = (n + kBlockParams - 1) / kBlockParams;
     const uint64_t nwc = (nblk + kUpdBlocksPerWave - 1) / kUpdBlocksPerWave;
     // Many workgroups per CU: each builds its tables once and the persistent loop's tail
@@ -407,6 +408,27 @@ static hipError_t update_dispatch(void *theta, bool bf16, uint64_t offset, uint6
                                                      bits, rprobe, ralpha, num_cus, stream)
                 : update_impl<false, false, kRestore>(theta, n, blk0, step, key, c, npert, eta,
                                                       bits, rprobe, ralpha, num_cus, stream);
+}
+
+template <bool kBF16, bool kBits, bool kRestore>
+static hipError_t raise_lds_limit(int bytes)
+{
+    return hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&k_update<kBF16, kBits, kRestore, 0>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+hipError_t prepare_update()
+{
+    const int bytes = (int)general_lds_bytes((kMaxNpert + 7u) / 8u);
+    const hipError_t e[8] = {
+        raise_lds_limit<false, false, false>(bytes), raise_lds_limit<false, false, true>(bytes),
+        raise_lds_limit<false, true, false>(bytes),  raise_lds_limit<false, true, true>(bytes),
+        raise_lds_limit<true, false, false>(bytes),  raise_lds_limit<true, false, true>(bytes),
+        raise_lds_limit<true, true, false>(bytes),   raise_lds_limit<true, true, true>(bytes)};
+    for (hipError_t x : e)
+        if (x != hipSuccess) return x;
+    return hipSuccess;
 }
 
 hipError_t launch_update(void *theta, bool bf16, uint64_t offset, uint64_t n, Key key,

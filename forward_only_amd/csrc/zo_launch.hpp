@@ -39,6 +39,13 @@ hipError_t launch_probe_weights(const double *Lp, const double *Lm, const double
                                 uint32_t npert, double eps, double delta, int mode,
                                 double power, float *c, uint32_t *counter, hipStream_t stream);
 
+// Largest probe count of one update (its sign tables live in LDS).
+constexpr uint32_t kMaxNpert = 512;
+
+// Raise the dynamic-LDS limit of the general update kernels to what kMaxNpert needs, on the
+// current device (once per context, from zo_init; launches then call no attribute setter).
+hipError_t prepare_update();
+
 // theta[0..n) -= eta * sum_i c_i z_i through per-8-probe LDS tables.
 hipError_t launch_update(void *theta, bool bf16, uint64_t offset, uint64_t n, Key key,
                          uint32_t step, const float *c, uint32_t npert, float eta,

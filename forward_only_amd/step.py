@@ -6,10 +6,14 @@ Transformers Without Backprop: What Two Zero-Order Papers Actually Measure"): th
 loss, then per probe four in-place passes +eps, -eps (restore), -eps, +eps (restore) with
 a loss after the first and third, then the probe weights, then one update pass.
 
-schedule="S2f" visits the same points with two passes per probe: +eps z_0, then per
-probe a -2 eps z_i pass (to theta - eps z_i) and one fused pass (zo_perturb2) that restores
-probe i and applies +eps z_(i+1); the last probe's restore is folded into the update pass
-(zo_restore_update), which nothing reads in between (the weights read only the losses).
+schedule="S2f" makes two passes per probe: +eps z_0, then per probe a -2 eps z_i pass (to
+theta - eps z_i) and one fused pass (zo_perturb2) that restores probe i and applies
++eps z_(i+1); the last probe's restore is folded into the update pass (zo_restore_update),
+which nothing reads in between (the weights read only the losses).  Its points are S4's
+exactly where every move is exact (e.g. dyadic fp32 values); otherwise each pass rounds
+once from where the previous one left theta -- in bf16 the -eps point is
+rnd(rnd(theta + eps z) - 2 eps z), not S4's rnd(theta - eps z) -- so the points may differ
+from S4's by rounding.
 
 Python only orders the launches; every pass over the parameters, the weights and the
 update run in libzo's kernels on torch's current stream.  Losses stay on the device.

@@ -24,9 +24,10 @@
  *  - Every compute call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream).  The caller owns every buffer; hot-path calls allocate nothing.  The step's
  *    calls (zo_perturb, zo_perturb2, zo_probe_weights, zo_update, zo_restore_update) only
- *    launch kernels -- no allocation, host synchronisation or memset node (counters are
- *    cleared by a kernel) -- so they can be recorded into a HIP graph and replayed.
- *    zo_nonfinite_count and zo_tune_placement synchronise and cannot.
+ *    launch kernels -- no allocation, host synchronisation, attribute call or memset node
+ *    (counters are cleared by a kernel) -- so they can be recorded into a HIP graph and
+ *    replayed, at every probe count up to ZO_MAX_NPERT and with regenerated or stored
+ *    signs.  zo_nonfinite_count and zo_tune_placement synchronise and cannot.
  *  - Return values report argument and launch errors only: ZO_EINVAL is returned before
  *    anything is launched, ZO_EHIP when the HIP runtime reports an error.  Numeric
  *    trouble is not an error (see zo_probe_weights).  n == 0 (or n_pert == 0) is a
@@ -69,9 +70,10 @@ typedef enum { ZO_FP32 = 0, ZO_BF16 = 1 } zo_dtype;
 #define ZO_MAX_NPERT 512u
 
 /* Create a context for probe seed `seed` on the current HIP device.  Allocates the host
- * context and a small device area (the non-finite counter and reduction partials).
- * Errors: ZO_EINVAL if out is NULL; ZO_ENOMEM / ZO_EHIP if an allocation fails (for
- * example when no GPU is present).  *out is set only on success. */
+ * context and a small device area (the non-finite counter and reduction partials), and
+ * raises the update kernel's dynamic-LDS limit on this device (so that no later call makes a runtime call besides its
+ * launches).  Errors: ZO_EINVAL if out is NULL; ZO_ENOMEM / ZO_EHIP if an allocation or
+ * runtime call fails (for example when no GPU is present).  *out is set only on success. */
 zo_status zo_init(uint64_t seed, zo_ctx **out);
 
 /* Release a context (NULL is allowed).  Synchronizes the device first. */
@@ -183,8 +185,10 @@ zo_status zo_update(zo_ctx *ctx, void *d_theta, zo_dtype dtype, uint64_t offset,
  * for bit.  This is the last restore of the two-moves-per-probe
  * schedule folded into the update that follows it (the probe weights between them read
  * only the losses), saving one full pass per step; the restore probe's signs come from the
- * update's own sign generation (one extra sign call per 128-param block at the probe
- * counts where the update runs unrolled).  Arguments as zo_update, plus restore_probe (< n_pert, a
+ * update's own sign generation at general probe counts, and at the probe counts where the
+ * update runs unrolled (16, 32, 64, 160) from one extra Philox call per lane, i.e. eight
+ * extra calls per 128-param block (the eight lanes sharing a block each make one).
+ * Arguments as zo_update, plus restore_probe (< n_pert, a
  * probe of the same step; with d_bits, its row is used) and restore_alpha (fp32).
  * Errors: as zo_update, and ZO_EINVAL if restore_probe >= n_pert. */
 zo_status zo_restore_update(zo_ctx *ctx, void *d_theta, zo_dtype dtype, uint64_t offset,

@@ -19,9 +19,11 @@ The eps handed to the weights is the fp32 value that the passes actually added.
 schedule="none" runs no passes at all (the losses must be given): the step of a forward
 that applies the probe on the fly while reading the parameters, leaving them untouched.
 
-schedule="S2f" visits the same perturbed points with two passes per probe instead of
-four: +eps z_0; then for each i a pass of -2 eps z_i (to theta - eps z_i) and a fused pass
-that restores probe i and applies +eps z_(i+1) (the last one only restores).
+schedule="S2f" makes two passes per probe instead of four: +eps z_0; then for each i a
+pass of -2 eps z_i (to theta - eps z_i) and a fused pass that restores probe i and applies
++eps z_(i+1) (the last one only restores).  Each pass rounds once from where the previous
+one left theta, so its points equal S4's only where every move is exact; in bf16 its -eps
+point is rnd(rnd(theta + eps z) - 2 eps z) rather than S4's rnd(theta - eps z).
 """
 from __future__ import annotations
 

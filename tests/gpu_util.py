@@ -3,8 +3,11 @@
 Tolerances (written here, used by every GPU parity test):
   * integer / bit work (packed planes, perturb, probe weights): bit-exact;
   * fp32 update: |theta_gpu - theta_ora| <= 1e-5 * max(|theta_ora|, eta * sum_i |c_i|);
-  * bf16 update: at most one bf16 ulp apart (the GPU rounds fp32 -> bf16 after a fused
-    multiply-add, the oracle rounds the exact fp64 value once, so ties may differ by one).
+  * bf16 update: at most one bf16 ulp apart.  Both sides form theta - eta * s in fp64 and
+    round that double once to bf16 (the GPU through a round-to-odd fp32 and the hardware
+    nearest-even convert, which together round the double correctly; the oracle directly),
+    but they sum the probes in different orders (per-8-probe tables against one running
+    sum), so s -- and with it a result next to a rounding boundary -- may differ by one.
 """
 from __future__ import annotations
 

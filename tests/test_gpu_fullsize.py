@@ -2,16 +2,19 @@
 
 The whole parameter buffer goes through the same calls the benchmark makes (zo_perturb,
 zo_perturb2, and zo_restore_update -- the update carrying a restore -- on the full buffer,
-probes regenerated); sampled windows (random ones, the first, the one holding the ragged
-tail and the last) are copied to the host before and after and recomputed by the oracle
-from their global offsets -- the probe bits are counter-based, so a window is an exact
-sub-problem.  Passes are compared bit for bit, the update within the update tolerance
-(fp32) or one bf16 ulp.
+probes regenerated); 64 random windows of 2^20 parameters, the first window, the last one
+(which ends at the buffer's ragged end) and one straddling the perturb kernel's last whole
+chunk are copied to the host before and after and recomputed by the oracle from their
+global offsets -- the probe bits are counter-based, so a window is an exact sub-problem.
+Passes are compared bit for bit, the update within the update tolerance (fp32) or one bf16
+ulp.  The oracle runs the windows on a pool of host threads.
 
 Properties that hold at any size are checked on every element of the 30B buffer: the
 drift bound of a whole two-pass step, the agreement of the three routes to a probe's signs
 (update, perturb, packed plane), and the restore-carrying update against the two calls.
 """
+import concurrent.futures as cf
+
 import numpy as np
 import pytest
 import torch
@@ -23,57 +26,75 @@ from workloads import CONFIGS, gen
 
 pytestmark = pytest.mark.gpu
 
-WIN = 8192
+WIN = 1 << 20
+N_RANDOM = 64
+THREADS = 16
 
 
-def _windows(M, k, seed):
+def _windows(M, k, seed, extra_starts=()):
+    """(start, length) of k random windows, the first, the last and the extra ones; starts
+    are multiples of 128 (whole probe blocks), the last window runs to M."""
     rng = np.random.default_rng(seed)
     nblk = M // 128
     starts = set((rng.integers(1, nblk - WIN // 128 - 1, k) * 128).tolist())
-    starts |= {0, (M // 8192) * 8192 - 4096, ((M - 1) // 128) * 128 - WIN + 128}
-    return sorted(s for s in starts if 0 <= s < M)
+    starts |= {0, (M // 8192) * 8192 - 4096}
+    starts |= set(extra_starts)
+    last = ((M - WIN) // 128) * 128
+    wins = [(s, WIN) for s in sorted(starts) if 0 <= s and s + WIN <= last]
+    wins.append((last, M - last))
+    return wins
 
 
-def _take(t, starts, kind):
+def _take(t, wins, kind):
     out = []
-    for s in starts:
-        w = t[s:s + WIN]
+    for s, n in wins:
+        w = t[s:s + n]
         out.append(w.cpu().numpy().copy() if kind == "f32" else bf16_bits(w).copy())
     return out
 
 
 def _run_and_check(t, M, kind, seed, npert, eps, eta, label, slice_bytes=0, extra_starts=()):
-    starts = sorted(set(_windows(M, 24, seed=M % 1000)) | set(extra_starts))
-    before = _take(t, starts, kind)
+    wins = _windows(M, N_RANDOM, seed=M % 1000, extra_starts=extra_starts)
+    assert len(wins) >= N_RANDOM - 2 and wins[0][0] == 0 and sum(wins[-1]) == M
+    before = _take(t, wins, kind)
     ctx = zo.zo_init(seed)
     zo.zo_set_slice_bytes(ctx, slice_bytes)
     a = float(np.float32(eps))
     c = (np.random.default_rng(7).standard_normal(npert) * 2.5e-3).astype(np.float32)
-    print(f"[fullsize] {label}: M={M} passes", flush=True)
+    print(f"[fullsize] {label}: M={M} passes, {len(wins)} windows", flush=True)
     zo.zo_perturb(ctx, t, 0, 1, 0, +a)
     zo.zo_perturb(ctx, t, 0, 1, 0, -2.0 * a)
     zo.zo_perturb2(ctx, t, 0, 1, 0, +a, 1, +a)
     torch.cuda.synchronize()
-    after_passes = _take(t, starts, kind)
+    after_passes = _take(t, wins, kind)
     print(f"[fullsize] {label}: restore + update n_pert={npert}", flush=True)
     zo.zo_restore_update(ctx, t, 0, 1, 1, -a, torch.from_numpy(c).cuda(), eta)
     torch.cuda.synchronize()
-    after_update = _take(t, starts, kind)
+    after_update = _take(t, wins, kind)
     ctx.close()
-    for s, h0, hp, hu in zip(starts, before, after_passes, after_update):
-        h = h0.copy()
+    view = np.uint32 if kind == "f32" else np.uint16
+
+    def recompute(i):
+        s = wins[i][0]
+        h = before[i].copy()
         oracle.perturb(h, s, seed, 1, 0, +a)
         oracle.perturb(h, s, seed, 1, 0, -2.0 * a)
         oracle.perturb2(h, s, seed, 1, 0, +a, 1, +a)
-        assert np.array_equal(h.view(np.uint32 if kind == "f32" else np.uint16),
-                              hp.view(np.uint32 if kind == "f32" else np.uint16)), (label, s)
+        passes = h.copy()
         oracle.perturb(h, s, seed, 1, 1, -a)
         oracle.update(h, s, seed, 1, c, eta)
+        return passes, h
+
+    print(f"[fullsize] {label}: oracle on {len(wins)} windows", flush=True)
+    with cf.ThreadPoolExecutor(THREADS) as ex:
+        refs = list(ex.map(recompute, range(len(wins))))
+    for (s, _), hp, hu, (rp, ru) in zip(wins, after_passes, after_update, refs):
+        assert np.array_equal(rp.view(view), hp.view(view)), (label, s)
         if kind == "f32":
-            assert_f32_update_close(hu, h, eta, c)
+            assert_f32_update_close(hu, ru, eta, c)
         else:
-            assert_bf16_within_ulp(hu, h)
-    return len(starts)
+            assert_bf16_within_ulp(hu, ru)
+    return len(wins)
 
 
 def test_flat125m_full_size():
@@ -82,7 +103,7 @@ def test_flat125m_full_size():
     t = torch.from_numpy(th0).cuda()
     del th0
     n = _run_and_check(t, cfg.M, "f32", cfg.seed, cfg.npert, cfg.eps, cfg.eta, "flat125m")
-    assert n >= 20
+    assert n >= N_RANDOM
 
 
 @pytest.mark.parametrize("name", ["opt13b", "opt30b"])
@@ -91,7 +112,7 @@ def test_opt_shaped_bf16_full_size(name):
     t = torch.empty(cfg.M, dtype=torch.bfloat16, device="cuda")
     gen.device_normal_(t, cfg.theta_std, cfg.seed)
     n = _run_and_check(t, cfg.M, "bf16", cfg.seed, cfg.npert, cfg.eps, 1.0, name)
-    assert n >= 20
+    assert n >= N_RANDOM
     del t
     torch.cuda.empty_cache()
 
@@ -105,7 +126,7 @@ def test_opt30b_largest_probe_count():
     gen.device_normal_(t, cfg.theta_std, cfg.seed)
     n = _run_and_check(t, cfg.M, "bf16", cfg.seed, int(zo.ZO_MAX_NPERT), cfg.eps, 1.0,
                        "opt30b n_pert=512")
-    assert n >= 20
+    assert n >= N_RANDOM
     del t
     torch.cuda.empty_cache()
 
@@ -218,9 +239,10 @@ def test_opt30b_passes_in_slices():
     gen.device_normal_(t, cfg.theta_std, cfg.seed)
     per = (512 << 20) // 2                                  # params per slice
     extra = [per - WIN // 2, 17 * per - WIN // 2, (cfg.M // per) * per - WIN // 2]
+    assert all(x % 128 == 0 for x in extra)
     n = _run_and_check(t, cfg.M, "bf16", cfg.seed, cfg.npert, cfg.eps, 1.0, "opt30b sliced",
                        slice_bytes=512 << 20, extra_starts=extra)
-    assert n >= 20
+    assert n >= N_RANDOM
     del t
     torch.cuda.empty_cache()
 

@@ -361,6 +361,38 @@ def test_argument_checks(ctx):
     assert torch.all(t == 0)
 
 
+def test_binding_requires_exact_packed_rows(ctx):
+    """Rows generated over a larger range (say the whole model) are not rows of a
+    sub-buffer: the library reads zo_bits_stride(n) bytes per row at a fixed row stride, so
+    the binding refuses rows and row sets whose shape is not exactly the buffer's, and a
+    weights output shorter than n_pert."""
+    n = 4096
+    t = torch.zeros(n, dtype=torch.float32, device="cuda")
+    c = torch.zeros(4, dtype=torch.float32, device="cuda")
+    wide = zo.zo_gen_probes(ctx, 0, 0, 4, 0, 2 * n)           # rows over 2n params
+    with pytest.raises(ValueError):
+        zo.zo_perturb(ctx, t, 0, 0, 0, 1.0, wide[0])
+    with pytest.raises(ValueError):
+        zo.zo_perturb2(ctx, t, 0, 0, 0, 1.0, 1, 1.0, wide[0], wide[1])
+    with pytest.raises(ValueError):
+        zo.zo_update(ctx, t, 0, 0, c, 1.0, wide)
+    with pytest.raises(ValueError):
+        zo.zo_restore_update(ctx, t, 0, 0, 0, 1.0, c, 1.0, wide)
+    own = zo.zo_gen_probes(ctx, 0, 0, 4, 0, n)
+    with pytest.raises(ValueError):
+        zo.zo_update(ctx, t, 0, 0, c, 1.0, own.reshape(-1))   # right bytes, not n_pert rows
+    with pytest.raises(ValueError):
+        zo.zo_update(ctx, t, 0, 0, c[:3], 1.0, own)           # 4 rows for 3 probes
+    zo.zo_update(ctx, t, 0, 0, c, 1.0, own)                   # the exact shape is accepted
+    zo.zo_perturb(ctx, t, 0, 0, 0, 0.0, own[0])
+    d = torch.zeros(4, dtype=torch.float64, device="cuda")
+    with pytest.raises(ValueError):
+        zo.zo_probe_weights_ex(ctx, d, d, d[:1], 1e-3, 1e-6, zo.ZO_WEIGHTS_PRECOND,
+                               out=torch.empty(3, dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.all(t == 0)
+
+
 # ------------------------------------------------------------------------------------
 # whole steps
 # ------------------------------------------------------------------------------------
@@ -410,13 +442,80 @@ def test_tiny_config_steps_from_seeded_theta(ctx, schedule, mode):
         scale = np.maximum(np.abs(h.astype(np.float64)),
                            float(np.float32(cfg.eta)) * float(np.sum(np.abs(res["c"]))))
         assert np.all(np.abs(got.astype(np.float64) - h) <= 1e-5 * scale + extra)
-    # GPU alone along a 10-step trajectory: the loss goes down
-    t = to_dev_f32(th0)
-    first = zo.zo_quad_loss(local, t, ad).item()
+    local.close()
+
+
+def _quad_sum_bound(theta, a, eps):
+    """Bound on the difference of two fp64 evaluations of 1/2 sum a_j x_j^2 at the same
+    point near theta (|x_j| <= |theta_j| + 2 eps), summed in different orders: Higham's
+    recursive-summation bound on each side plus the products' own roundings."""
+    x = np.abs(theta.astype(np.float64)) + 2 * eps
+    return 2 * (theta.size + 3) * 2.0 ** -53 * np.sum(0.5 * a.astype(np.float64) * x * x) * 1.1
+
+
+@pytest.mark.parametrize("schedule", ["S4", "S2f"])
+@pytest.mark.parametrize("mode", ["regen", "bits"])
+def test_tiny_config_trajectory(ctx, schedule, mode):
+    """The tiny workload's 10-step trajectory, each side on its own from the seeded theta
+    (GPU: library passes, GPU losses, weights and update; oracle: its own passes, losses,
+    weights and update, probes of its own), compared after every step.
+
+    The two states can part only through rounding: the update sums the probes in another
+    order (at most one fp32 ulp of the new value per element and step), and a weight that
+    differs in its last bit moves every element by eta * |dc|.  With D the measured state
+    difference before a step, the step must satisfy
+      * losses: |L_gpu - L_ora| <= fp64 summation bound + sum_j a_j (|x_j| E_j + E_j^2 / 2),
+        with E_j = D_j + (passes) * ulp where D_j > 0, else 0 (the passes are bit-exact
+        functions, so states that agree visit the same points);
+      * weights: |c_gpu - c_ora| within the bound those loss differences imply, and that
+        bound finite for every probe;
+      * the new state: D'_j <= E_j + eta * (sum_i |dc_i| + fp64 sum error) + one fp32 ulp.
+    After ten steps nearly every element is still bit-identical and both losses fell."""
+    cfg = CONFIGS["tiny"]
+    local = zo.zo_init(cfg.seed)
+    th0, a = gen.theta_and_a(cfg)
+    ad = to_dev_f32(a)
+    af = a.astype(np.float64)
+    eps = float(np.float32(cfg.eps))
+    eta = float(np.float32(cfg.eta))
+    npasses = 4 * cfg.npert + 1
+    lossf = lambda x, o: zo.zo_quad_loss(local, x, ad, out=o)  # noqa: E731
+    t, h = to_dev_f32(th0), th0.copy()
+    first_gpu, first_ora = zo.zo_quad_loss(local, t, ad).item(), oracle.quad_loss(h, a)
     for step in range(cfg.steps):
-        spsa_step(local, t, step=step, npert=cfg.npert, eps=cfg.eps, eta=cfg.eta,
-                  delta=cfg.delta, loss=lossf, schedule=schedule)
-    assert zo.zo_quad_loss(local, t, ad).item() < first
+        D = np.abs(t.cpu().numpy().astype(np.float64) - h.astype(np.float64))
+        ulp = np.spacing((np.abs(h) + D + 4 * eps).astype(np.float32)).astype(np.float64)
+        E = np.where(D > 0, D + npasses * ulp, 0.0)
+        dL = _quad_sum_bound(h, a, eps) + float(np.sum(af * ((np.abs(h) + 4 * eps) * E
+                                                             + 0.5 * E * E)))
+        bits_d = zo.zo_gen_probes(local, step, 0, cfg.npert, 0, cfg.M) if mode == "bits" else None
+        bits_h = oracle.gen_planes(cfg.seed, step, 0, cfg.npert, 0, cfg.M) if mode == "bits" else None
+        out = spsa_step(local, t, step=step, npert=cfg.npert, eps=cfg.eps, eta=cfg.eta,
+                        delta=cfg.delta, loss=lossf, bits=bits_d, schedule=schedule)
+        res = oracle.spsa_step(h, seed=cfg.seed, step=step, npert=cfg.npert, eps=cfg.eps,
+                               eta=cfg.eta, delta=cfg.delta,
+                               loss_fn=lambda x: oracle.quad_loss(x, a), bits=bits_h,
+                               schedule=schedule)
+        L0, Lp, Lm = out["L0"].item(), out["Lp"].cpu().numpy(), out["Lm"].cpu().numpy()
+        assert abs(L0 - res["L0"]) <= dL, (step, L0, res["L0"], dL)
+        assert np.all(np.abs(Lp - res["Lp"]) <= dL) and np.all(np.abs(Lm - res["Lm"]) <= dL), step
+        c = out["c"].cpu().numpy().astype(np.float64)
+        bound = weight_bound(res["Lp"], res["Lm"], res["L0"], dL, eps, cfg.delta, res["c"])
+        assert np.all(np.isfinite(bound)), (step, bound)
+        dc = np.abs(c - res["c"])
+        assert np.all(dc <= bound), (step, dc, bound)
+        got = t.cpu().numpy()
+        sum_err = 2 * (cfg.npert + 8) * 2.0 ** -53 * float(np.sum(np.abs(res["c"]))) * 1.01
+        new_ulp = np.spacing(np.maximum(np.abs(got), np.abs(h))).astype(np.float64)
+        allow = E + eta * (float(np.sum(dc)) + sum_err) + new_ulp
+        D_next = np.abs(got.astype(np.float64) - h.astype(np.float64))
+        assert np.all(D_next <= allow), (step, int(np.sum(D_next > allow)))
+        print(f"[trajectory] {schedule}/{mode} step {step}: {int(np.sum(D_next > 0))} of "
+              f"{cfg.M} elements differ, max |dc| {dc.max():.3e}", flush=True)
+    same = float(np.mean(t.cpu().numpy().view(np.uint32) == h.view(np.uint32)))
+    assert same >= 0.99, same
+    assert zo.zo_quad_loss(local, t, ad).item() < first_gpu
+    assert oracle.quad_loss(h, a) < first_ora
     local.close()
 
 
@@ -486,12 +585,17 @@ def test_bf16_synthetic_two_pass_step_small(ctx):
     assert np.array_equal(bf16_bits(t), h)
 
 
-@pytest.mark.parametrize("kind,npert", [("bf16", 16), ("f32", 160)])
-def test_step_calls_replay_from_a_captured_graph(ctx, kind, npert):
+@pytest.mark.parametrize("kind,npert,mode", [("bf16", 16, "regen"), ("f32", 160, "regen"),
+                                             ("bf16", 512, "regen"), ("f32", 512, "bits"),
+                                             ("bf16", 160, "bits")])
+def test_step_calls_replay_from_a_captured_graph(ctx, kind, npert, mode):
     """The library's calls of one two-pass step (passes, fused passes, weights, the update
-    carrying the last restore) captured into a HIP graph: no allocation, synchronisation or
-    memset node in them, so each replay equals the same calls made eagerly, replay after
-    replay, with eager work and synchronisations in between."""
+    carrying the last restore; with stored signs also the plane generator) captured into a
+    HIP graph: no allocation, synchronisation, attribute call or memset node in them, so
+    each replay equals the same calls made eagerly, replay after replay, with eager work and
+    synchronisations in between.  n_pert = 512 runs the general update kernel with 138 KiB
+    of dynamic LDS (the limit raised once by zo_init), stored signs the general kernel at
+    any probe count."""
     n, step = 8192 * 5 + 77, 4
     h = _theta(kind, n, seed=17, scale=0.02)
     a = 1e-3 if kind == "bf16" else 2.0 ** -10
@@ -501,35 +605,45 @@ def test_step_calls_replay_from_a_captured_graph(ctx, kind, npert):
     c_eager = torch.empty(npert, dtype=torch.float32, device="cuda")
     c_graph = torch.empty(npert, dtype=torch.float32, device="cuda")
     eta = 1.0 if kind == "bf16" else 1e-2
+    stride = zo.zo_bits_stride(n)
+    planes = {}
+    for name in ("eager", "graph", "warm"):
+        planes[name] = (torch.empty((npert, stride), dtype=torch.uint8, device="cuda")
+                        if mode == "bits" else None)
 
-    def calls(t, c):
-        zo.zo_perturb(ctx, t, 0, step, 0, +a)
+    def calls(t, c, bits):
+        row = (lambda i: None) if bits is None else (lambda i: bits[i])
+        if bits is not None:
+            zo.zo_gen_probes(ctx, step, 0, npert, 0, n, out=bits)
+        zo.zo_perturb(ctx, t, 0, step, 0, +a, row(0))
         for i in range(npert):
-            zo.zo_perturb(ctx, t, 0, step, i, -2.0 * a)
+            zo.zo_perturb(ctx, t, 0, step, i, -2.0 * a, row(i))
             if i + 1 < npert:
-                zo.zo_perturb2(ctx, t, 0, step, i, +a, i + 1, +a)
+                zo.zo_perturb2(ctx, t, 0, step, i, +a, i + 1, +a, row(i), row(i + 1))
         zo.zo_probe_weights(ctx, Lpd, Lmd, L0d, a, 1e-6, out=c)
-        zo.zo_restore_update(ctx, t, 0, step, npert - 1, +a, c, eta)
+        zo.zo_restore_update(ctx, t, 0, step, npert - 1, +a, c, eta, bits)
 
     eager, graphed, warm = _dev(kind, h), _dev(kind, h), _dev(kind, h)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        calls(warm, c_graph)                      # first launches outside the capture
+        calls(warm, c_graph, planes["warm"])      # first launches outside the capture
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        calls(graphed, c_graph)
+        calls(graphed, c_graph, planes["graph"])
     torch.cuda.synchronize()
     assert np.array_equal(_host(kind, graphed), _host(kind, _dev(kind, h)))   # not yet run
     for _ in range(3):
         g.replay()
         torch.cuda.synchronize()
-        calls(eager, c_eager)
+        calls(eager, c_eager, planes["eager"])
         torch.cuda.synchronize()
         assert np.array_equal(_host(kind, graphed), _host(kind, eager))
         assert torch.equal(c_graph, c_eager)
+        if mode == "bits":
+            assert torch.equal(planes["graph"], planes["eager"])
 
 
 # ------------------------------------------------------------------------------------
