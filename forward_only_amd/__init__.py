@@ -20,7 +20,7 @@ import torch
 
 from . import _lib
 from ._lib import (ZO_BF16, ZO_EHIP, ZO_EINVAL, ZO_ENOMEM, ZO_EUNSUPPORTED, ZO_FP32,  # noqa: F401
-                   ZO_MAX_NPERT, ZO_OK, ZO_WEIGHTS_POWER, ZO_WEIGHTS_PRECOND,
+                   ZO_MAX_NPERT, ZO_NOALLOC_SCRATCH_BYTES, ZO_OK, ZO_WEIGHTS_POWER, ZO_WEIGHTS_PRECOND,
                    ZO_WEIGHTS_SPSA_MEAN, ZOError)
 
 __all__ = [
@@ -28,7 +28,7 @@ __all__ = [
     "zo_perturb", "zo_perturb2", "zo_probe_weights", "zo_probe_weights_ex", "zo_update",
     "zo_restore_update", "zo_nonfinite_count", "zo_reset_nonfinite", "zo_quad_loss",
     "zo_lowrank_quad_loss", "zo_mlp_workspace_bytes", "zo_mlp_loss", "zo_mlp_loss_perturbed",
-    "zo_mlp_loss_pair", "zo_stream_rmw", "zo_tune_placement", "zo_set_slice_bytes",
+    "zo_mlp_loss_pair", "zo_mlp_loss_pair_noalloc", "zo_stream_rmw", "zo_tune_placement", "zo_set_slice_bytes",
     "zo_get_slice_bytes", "library_path",
 ]
 
@@ -337,6 +337,26 @@ def zo_mlp_loss_pair(ctx: Context, params: torch.Tensor, offset: int, step: int,
         d_out, pw, wbytes, _dev(out_plus, "out_plus", torch.float64),
         _dev(out_minus, "out_minus", torch.float64), _stream(stream)), "zo_mlp_loss_pair")
     return out_plus, out_minus
+
+
+def zo_mlp_loss_pair_noalloc(ctx: Context, params: torch.Tensor, offset: int, step: int,
+                             probe: int, alpha: float, X: torch.Tensor, labels: torch.Tensor,
+                             d_hid: int, d_out: int, out_plus: torch.Tensor,
+                             out_minus: torch.Tensor, bits: torch.Tensor | None = None,
+                             stream=None) -> None:
+    """zo_mlp_loss_pair with the library's static per-GPU scratch instead of a workspace:
+    the call allocates nothing (the caller passes both one-element float64 outputs)."""
+    batch, d_in = X.shape
+    if params.numel() != d_hid * d_in + d_hid + d_out * d_hid + d_out:
+        raise ValueError("params must hold the MLP's parameters")
+    if labels.numel() != batch:
+        raise ValueError("one label per row")
+    _lib.check(_lib.lib().zo_mlp_loss_pair_noalloc(
+        ctx.handle, _dev(params, "params", torch.float32), offset, step, probe, float(alpha),
+        _row(bits, params.numel()), _dev(X, "X", torch.float32),
+        _dev(labels, "labels", torch.int64), batch, d_in, d_hid, d_out,
+        _dev(out_plus, "out_plus", torch.float64), _dev(out_minus, "out_minus", torch.float64),
+        _stream(stream)), "zo_mlp_loss_pair_noalloc")
 
 
 def zo_stream_rmw(ctx: Context, buf: torch.Tensor, mask: int = 0, stream=None) -> None:

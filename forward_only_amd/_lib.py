@@ -16,6 +16,7 @@ ZO_OK, ZO_EINVAL, ZO_EHIP, ZO_ENOMEM, ZO_EUNSUPPORTED = 0, 1, 2, 3, 4
 ZO_FP32, ZO_BF16 = 0, 1
 ZO_WEIGHTS_PRECOND, ZO_WEIGHTS_POWER, ZO_WEIGHTS_SPSA_MEAN = 0, 1, 2
 ZO_MAX_NPERT = 512
+ZO_NOALLOC_SCRATCH_BYTES = 1 << 20
 
 _vp = ctypes.c_void_p
 _u8p = ctypes.POINTER(ctypes.c_uint8)
@@ -46,6 +47,8 @@ SIGNATURES = {
                                      _u32, _u32, _u32, _vp, _u64, _vp, _vp]),
     "zo_mlp_loss_pair": (_int, [_vp, _vp, _u64, _u32, _u32, _f32, _vp, _vp, _vp, _u32,
                                 _u32, _u32, _u32, _vp, _u64, _vp, _vp, _vp]),
+    "zo_mlp_loss_pair_noalloc": (_int, [_vp, _vp, _u64, _u32, _u32, _f32, _vp, _vp, _vp, _u32,
+                                        _u32, _u32, _u32, _vp, _vp, _vp]),
     "zo_stream_rmw": (_int, [_vp, _vp, _u64, _u32, _vp]),
     "zo_tune_placement": (_int, [_vp, _vp, _u64, _vp, _vp, _vp, _vp]),
     "zo_set_slice_bytes": (_int, [_vp, _u64]),

@@ -1,11 +1,18 @@
 // api.hip -- the extern "C" boundary of libzo: context, argument validation, launches.
 // Every check happens before any launch; a rejected call touches no device memory.
+#include <mutex>
 #include <new>
 
 #include "../../include/zo.h"
 #include "zo_launch.hpp"
 
 static_assert(ZO_MAX_NPERT == zo::kMaxNpert, "one probe-count limit");
+
+// Scratch of zo_mlp_loss_pair_noalloc: the partial logits and row losses of both signs,
+// ZO_NOALLOC_SCRATCH_BYTES per device, held until the process ends.  Host code never
+// passes this name to a kernel (on the host it is only a stand-in symbol): kernels get the
+// device address that hipGetSymbolAddress returns for the current device (scratch_on).
+static __device__ __align__(256) unsigned char scratch[ZO_NOALLOC_SCRATCH_BYTES];
 
 struct zo_ctx {
     uint64_t seed;
@@ -14,9 +21,30 @@ struct zo_ctx {
     uint32_t *d_counter;   // non-finite probe counter
     double *d_partials;    // loss partial sums (zo::kLossPartials * (kLowRankMax + 1) doubles)
     uint64_t slice_bytes;  // perturb passes issued per slice of this many bytes (0: whole)
+    void *d_scratch;       // this device's copy of `scratch`
 };
 
 namespace {
+
+// Device address of `scratch` on device `dev` (which must be current), looked up once per
+// device and kept; nullptr if the lookup fails.
+void *scratch_on(int dev)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -97,7 +125,8 @@ zo_status zo_init(uint64_t seed, zo_ctx **out)
         (void)hipGetLastError();
         return ZO_ENOMEM;
     }
-    if (zo::prepare_update() != hipSuccess ||
+    c->d_scratch = scratch_on(c->device);
+    if (!c->d_scratch || zo::prepare_update() != hipSuccess ||
         zo::launch_zero_u32(c->d_counter, 64, nullptr) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {
         (void)hipFree(c->d_partials);
@@ -338,6 +367,31 @@ zo_status zo_mlp_loss_pair(zo_ctx *c, const float *d_params, uint64_t offset, ui
     const zo::MlpPerturb pert{offset, step, probe, alpha, d_bits};
     return from_hip(zo::launch_mlp_loss(d_params, d_X, d_labels, batch, d_in, d_hid, d_out,
                                         static_cast<double *>(d_workspace), d_loss_plus, &pert,
+                                        key_of(c), as_stream(stream), d_loss_minus));
+}
+
+zo_status zo_mlp_loss_pair_noalloc(zo_ctx *c, const float *d_params, uint64_t offset,
+                                   uint32_t step, uint32_t probe, float alpha,
+                                   const uint8_t *d_bits, const float *d_X,
+                                   const int64_t *d_labels, uint32_t batch, uint32_t d_in,
+                                   uint32_t d_hid, uint32_t d_out, double *d_loss_plus,
+                                   double *d_loss_minus, void *stream)
+{
+    if (!ctx_ok(c)) return ZO_EINVAL;
+    // the workspace check below compares the library's own size with the scratch size;
+    // shapes whose pair workspace exceeds it are refused before anything is launched
+    if (batch != 0 && d_hid != 0 &&
+        zo_mlp_workspace_bytes(batch, d_in, d_hid, d_out) > ZO_NOALLOC_SCRATCH_BYTES)
+        return ZO_EUNSUPPORTED;
+    const zo_status st = mlp_checks(c, d_params, d_X, d_labels, batch, d_in, d_hid, d_out,
+                                    c->d_scratch, ZO_NOALLOC_SCRATCH_BYTES, d_loss_plus);
+    if (st != ZO_OK) return st;
+    if (!d_loss_minus) return ZO_EINVAL;
+    const uint64_t nparams = (uint64_t)d_hid * d_in + d_hid + (uint64_t)d_out * d_hid + d_out;
+    if (!range_ok(offset, nparams)) return ZO_EINVAL;
+    const zo::MlpPerturb pert{offset, step, probe, alpha, d_bits};
+    return from_hip(zo::launch_mlp_loss(d_params, d_X, d_labels, batch, d_in, d_hid, d_out,
+                                        static_cast<double *>(c->d_scratch), d_loss_plus, &pert,
                                         key_of(c), as_stream(stream), d_loss_minus));
 }
 

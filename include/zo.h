@@ -69,9 +69,13 @@ typedef enum { ZO_FP32 = 0, ZO_BF16 = 1 } zo_dtype;
 /* Largest n_pert one zo_update call accepts (its sign tables live in LDS). */
 #define ZO_MAX_NPERT 512u
 
+/* Device scratch of zo_mlp_loss_pair_noalloc, one static array per GPU (1 MiB). */
+#define ZO_NOALLOC_SCRATCH_BYTES (1u << 20)
+
 /* Create a context for probe seed `seed` on the current HIP device.  Allocates the host
- * context and a small device area (the non-finite counter and reduction partials), and
- * raises the update kernel's dynamic-LDS limit on this device (so that no later call makes a runtime call besides its
+ * context and a small device area (the non-finite counter and reduction partials), looks
+ * up this device's copy of the library's static scratch, and raises the update kernel's
+ * dynamic-LDS limit on this device (so that no later call makes a runtime call besides its
  * launches).  Errors: ZO_EINVAL if out is NULL; ZO_ENOMEM / ZO_EHIP if an allocation or
  * runtime call fails (for example when no GPU is present).  *out is set only on success. */
 zo_status zo_init(uint64_t seed, zo_ctx **out);
@@ -273,6 +277,24 @@ zo_status zo_mlp_loss_pair(zo_ctx *ctx, const float *d_params, uint64_t offset, 
                            uint32_t d_hid, uint32_t d_out, void *d_workspace,
                            uint64_t workspace_bytes, double *d_loss_plus, double *d_loss_minus,
                            void *stream);
+
+/* zo_mlp_loss_pair for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same kernels and the
+ * same results, bit for bit, but the partial logits and row losses live in a static device
+ * array of ZO_NOALLOC_SCRATCH_BYTES (1 MiB) per GPU, held until the process ends, instead
+ * of a caller workspace; the call allocates nothing.  Every call on one GPU shares that
+ * GPU's array (nothing in it must start at zero; the kernels write every slot they read),
+ * so calls that overlap on one GPU -- on different streams or from different host threads
+ * -- race and must not be made.  Arguments, results and errors as zo_mlp_loss_pair without
+ * d_workspace / workspace_bytes; ZO_EUNSUPPORTED if zo_mlp_workspace_bytes(batch, d_in,
+ * d_hid, d_out) exceeds ZO_NOALLOC_SCRATCH_BYTES (the 128 x 768 -> 3072 -> 2 classifier
+ * needs 788,480 bytes). */
+zo_status zo_mlp_loss_pair_noalloc(zo_ctx *ctx, const float *d_params, uint64_t offset,
+                                   uint32_t step, uint32_t probe, float alpha,
+                                   const uint8_t *d_bits, const float *d_X,
+                                   const int64_t *d_labels, uint32_t batch, uint32_t d_in,
+                                   uint32_t d_hid, uint32_t d_out, double *d_loss_plus,
+                                   double *d_loss_minus, void *stream);
 
 /* Diagnostic, not a step of the method: every 32-bit word of d_buf becomes word ^ mask,
  * in place, streaming in the same order as zo_perturb (mask = 0 leaves the buffer
