@@ -60,6 +60,8 @@ def parse_args(argv=None):
                    help="skip the CPU oracle leg (profiling runs)")
     p.add_argument("--no-relocate", action="store_true",
                    help="keep theta on its first allocation (no placement search)")
+    p.add_argument("--no-other-sizes", action="store_true",
+                   help="with the opt30b headline, skip the opt13b and flat125m measurements")
     p.add_argument("--cpu-params-per-thread", type=int, default=1 << 20)
     p.add_argument("--cpu-threads", type=int, default=None)
     p.add_argument("--copy-calibration", action="store_true",
@@ -205,21 +207,11 @@ def main(argv=None):
         copy_calibration()
         return
 
-    import numpy as np
-    import torch
-
-    import forward_only_amd as zo
-    from forward_only_amd import placement
-    from forward_only_amd.step import applied_eps
-    from workloads import CONFIGS, gen
+    from workloads import CONFIGS
 
     cfg = CONFIGS[args.config]
     K = args.steps if args.steps is not None else cfg.steps
     W = args.warmup
-    n, M = cfg.npert, cfg.M
-    esize = 2 if cfg.dtype == "bf16" else 4
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda", 0)
 
     # CPU oracle leg first (host only; keeps the GPU phase uninterrupted).
     cpu = None
@@ -229,6 +221,43 @@ def main(argv=None):
         cpu = cpu_baseline(cfg, args.cpu_params_per_thread, threads, args.schedule)
         log(f"[bench] cpu baseline: {cpu['value']:.3e} probe*params/s")
 
+    result = run_workload(args, args.config, K, W, cpu=cpu, gen_plane=True)
+    if args.config == "opt30b" and not args.no_other_sizes:
+        # the other parameter-set sizes of the same path, measured after the headline (its
+        # buffer freed first), each with its own step count and one warmup step
+        other = {}
+        for name in OTHER_SIZES:
+            r = run_workload(args, name, CONFIGS[name].steps, 1, cpu=None, gen_plane=False)
+            other[name] = {k: r[k] for k in OTHER_KEYS}
+        result["other_sizes"] = other
+    print(json.dumps(result), flush=True)
+
+
+# Parameter-set sizes measured beside the 30B headline, and what each reports.
+OTHER_SIZES = ("opt13b", "flat125m")
+OTHER_KEYS = ("value", "unit", "steps", "warmup", "ms_per_step", "ms_per_step_median", "dtype",
+              "config", "hbm_gbps", "hbm_frac_of_peak", "kernels_ms", "roofline",
+              "pass_roofline", "update_roofline", "nonfinite_probes")
+
+
+def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = True) -> dict:
+    """Time K steps (after W warmup steps) of workload `name` on cuda:0; returns the bench
+    record (the device memory it used is released before it returns)."""
+    import numpy as np
+    import torch
+
+    import forward_only_amd as zo
+    from forward_only_amd import placement
+    from forward_only_amd.step import applied_eps
+    from workloads import CONFIGS, gen
+
+    cfg = CONFIGS[name]
+    n, M = cfg.npert, cfg.M
+    esize = 2 if cfg.dtype == "bf16" else 4
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+
+    schedule = args.schedule
     ctx = zo.zo_init(cfg.seed)
     log(f"[bench] {cfg.name}: M={M} {cfg.dtype} ({M * esize / 1e9:.2f} GB), n_pert={n}, "
         f"steps={K}, warmup={W}")
@@ -334,7 +363,7 @@ def main(argv=None):
             timed("update", lambda: zo.zo_update(ctx, theta, 0, s, c_buf, cfg.eta), record)
             return
         loss_into(L0, record)
-        if args.schedule == "S4":
+        if schedule == "S4":
             for i in range(n):
                 timed("perturb", lambda: zo.zo_perturb(ctx, theta, 0, s, i, +a), record)
                 loss_into(Lp[i:i + 1], record)
@@ -353,7 +382,7 @@ def main(argv=None):
                           lambda: zo.zo_perturb2(ctx, theta, 0, s, i, +a, i + 1, +a), record)
         timed("weights", lambda: zo.zo_probe_weights(ctx, Lp, Lm, L0, a, cfg.delta, out=c_buf),
               record)
-        if args.schedule == "S2f":
+        if schedule == "S2f":
             # the last probe's restore rides on the update pass
             timed("update", lambda: zo.zo_restore_update(ctx, theta, 0, s, n - 1, +a, c_buf,
                                                          cfg.eta), record)
@@ -401,7 +430,7 @@ def main(argv=None):
     # The packed-plane generator (the step regenerates bits inline; planes serve callers
     # that store them): one probe's plane over the whole buffer, timed after the step.
     gen_probes = None
-    if mlp is None:
+    if mlp is None and gen_plane:
         stride = zo.zo_bits_stride(M)
         plane = torch.empty((1, stride), dtype=torch.uint8, device=dev)
         zo.zo_gen_probes(ctx, 0, 0, 1, 0, M, out=plane)
@@ -433,9 +462,15 @@ def main(argv=None):
     kernel_ms_per_step = sum(times(list(per))) / K     # sum of every timed kernel call
     # every pass of either perturb entry point runs k_perturb_chunks (one or two probes)
     pert_ms, upd_ms, w_ms = avg_ms("perturb", "perturb2"), avg_ms("update"), avg_ms("weights")
-    passes = 0 if mlp is not None else (4 * n if args.schedule == "S4" else 2 * n)
+    passes = 0 if mlp is not None else (4 * n if schedule == "S4" else 2 * n)
     pass_bytes = 2.0 * esize * M                      # one read + one write of theta
     step_bytes = (passes + 1) * pass_bytes            # the passes + the update
+    pass_roofline = None
+    if pert_ms:
+        pa = pass_bytes / (pert_ms * 1e-3) / 1e9
+        pass_roofline = {"kernel": "k_perturb_chunks", "bound": "hbm", "achieved": pa,
+                         "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": pa / PEAK_HBM_GBPS,
+                         "bytes_per_pass": pass_bytes}
     if mlp is not None:
         mlp_ms = avg_ms("mlp_pair")
         achieved = 2.0 * mlp["flop"] / (mlp_ms * 1e-3) / 1e12
@@ -459,7 +494,7 @@ def main(argv=None):
                         "frac": la / PEAK_HBM_GBPS, "traffic": None,
                         "note": f"{loss_bytes / 1e6:.0f} MB per evaluation; partly resident in "
                                 f"the 256 MB last-level cache"}
-    traffic = stored_traffic(f"{cfg.name}/{args.schedule}", pass_bytes)
+    traffic = stored_traffic(f"{cfg.name}/{schedule}", pass_bytes)
     result = {
         "metric": "probe*params/s and HBM GB/s (% peak) per 1.5-SPSA step, n_pert=160, 1 GPU",
         "value": value,
@@ -479,13 +514,13 @@ def main(argv=None):
                                 f"n_pert={n}, eps={cfg.eps}, eta={cfg.eta}, " +
                                 ("probes applied inside the MFMA forward, both signs per "
                                  "launch (no passes over theta) + update" if mlp is not None else
-                                 f"schedule {args.schedule} ({passes} passes + update" +
-                                 (" carrying the last restore)" if args.schedule == "S2f"
+                                 f"schedule {schedule} ({passes} passes + update" +
+                                 (" carrying the last restore)" if schedule == "S2f"
                                   else ")")) +
                                 ", probes regenerated, losses " +
                                 ("synthetic" if cfg.loss == "synthetic" else cfg.loss)),
                    "params": M, "n_pert": n,
-                   "schedule": "fused forward" if mlp is not None else args.schedule,
+                   "schedule": "fused forward" if mlp is not None else schedule,
                    "passes_per_step": passes + 1},
         "hbm_gbps": step_bytes / T / 1e9,
         "hbm_frac_of_peak": step_bytes / T / 1e9 / PEAK_HBM_GBPS,
@@ -504,13 +539,17 @@ def main(argv=None):
                                  "placement_relocation": relocation,
                                  "frac_of_placement_ceiling": (achieved / placement_gbps
                                                                if placement_gbps else None)},
+        "pass_roofline": pass_roofline,
         "update_roofline": update_roofline(M, n, pass_bytes, upd_ms),
         "gen_probes": gen_probes,
         "nonfinite_probes": nonfinite,
         "cpu_baseline": cpu,
     }
     ctx.close()
-    print(json.dumps(result), flush=True)
+    del theta, L0s, Lps, Lms, c_buf, a_dev, mlp, per, step_marks
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return result
 
 
 if __name__ == "__main__":

@@ -1,6 +1,7 @@
 // k_diag.hip -- diagnostic streaming kernel: every 16-byte word of a buffer is read, xored
 // with a mask and written back, in the perturb kernel's order (eight contiguous chunk
-// ranges, one per XCD, 16 KiB per wave per chunk, non-temporal loads and stores).  With
+// ranges, one per XCD, one 16 KiB chunk per wave, non-persistent, non-temporal loads and
+// stores).  With
 // mask 0 the buffer is unchanged, and timing the call on a parameter buffer gives the
 // in-place read-modify-write ceiling of the physical memory that buffer occupies.  The mask
 // is a run-time argument on purpose: a store of the value just loaded from the same address
@@ -18,12 +19,9 @@ constexpr uint64_t kDiagChunk16 = kDiagLoads * kWave;  // 16-byte words per chun
 __global__ __launch_bounds__(256) void k_stream_rmw(u32x4_t *__restrict__ p, uint64_t nchunks,
                                                     uint32_t mask)
 {
-    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-    const uint32_t xcd = blockIdx.x & 7u;
-    const uint64_t stride = (uint64_t)(gridDim.x >> 3) * 4;
-    const uint64_t end = nchunks * (xcd + 1) / 8;
-    for (uint64_t ch = nchunks * xcd / 8 + (uint64_t)(blockIdx.x >> 3) * 4 + wv; ch < end;
-         ch += stride) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint64_t ch = xcd_range_chunk<4>(nchunks);
+    if (ch < nchunks) {
         u32x4_t *b = p + ch * kDiagChunk16 + lane;
         u32x4_t v[kDiagLoads];
 #pragma unroll
@@ -47,12 +45,10 @@ static hipError_t stream_rmw_range(void *buf, uint64_t bytes, uint32_t mask, int
     const uint64_t nwords = bytes / 16;
     const uint64_t nchunks = nwords / kDiagChunk16;
     u32x4_t *p = static_cast<u32x4_t *>(buf);
-    if (nchunks) {
-        const uint64_t want = (nchunks + 3) / 4;
-        const uint64_t cap = (uint64_t)num_cus * 8;
-        const uint32_t grid = (uint32_t)(((want < cap ? want : cap) + 7) / 8 * 8);
-        hipLaunchKernelGGL(k_stream_rmw, dim3(grid), dim3(256), 0, stream, p, nchunks, mask);
-    }
+    (void)num_cus;
+    if (nchunks)
+        hipLaunchKernelGGL(k_stream_rmw, dim3(xcd_range_grid(nchunks, 4)), dim3(256), 0, stream,
+                           p, nchunks, mask);
     const uint64_t start = nchunks * kDiagChunk16;
     if (start < nwords) {
         const uint32_t grid = (uint32_t)((nwords - start + 255) / 256);
@@ -65,7 +61,9 @@ static hipError_t stream_rmw_range(void *buf, uint64_t bytes, uint32_t mask, int
 hipError_t launch_stream_rmw(void *buf, uint64_t bytes, uint32_t mask, int num_cus,
                              hipStream_t stream, uint64_t slice_bytes)
 {
-    if (slice_bytes == 0 || slice_bytes >= bytes)
+    constexpr uint64_t kMaxLaunchBytes = kMaxChunksPerLaunch * kDiagChunk16 * 16;
+    if (slice_bytes == 0 || slice_bytes > kMaxLaunchBytes) slice_bytes = kMaxLaunchBytes;
+    if (slice_bytes >= bytes)
         return stream_rmw_range(buf, bytes, mask, num_cus, stream);
     for (uint64_t b0 = 0; b0 < bytes; b0 += slice_bytes) {
         const uint64_t m = (bytes - b0) < slice_bytes ? (bytes - b0) : slice_bytes;

@@ -76,6 +76,21 @@ __device__ __forceinline__ float signed_alpha(uint32_t nm, int b, uint32_t abits
     return __uint_as_float(abits ^ s);
 }
 
+// Chunk of this wave in a non-persistent XCD-range launch over chunks [0, n): the chunks
+// are split into eight contiguous ranges, one per XCD (workgroups are dispatched to the XCDs
+// round-robin, so workgroup b runs on XCD b % 8), and workgroup b gives each of its
+// kWavesPerWG waves the next chunk of range b % 8 in dispatch order.  Every wave handles one
+// chunk and exits, so the waves in flight on an XCD always cover one compact window of its
+// range: a persistent loop lets waves drift apart over a wide window, which some physical
+// placements of a large buffer serve much more slowly.  Returns n for a wave past its range.
+template <int kWavesPerWG>
+__device__ __forceinline__ uint64_t xcd_range_chunk(uint64_t n)
+{
+    const uint64_t x = blockIdx.x & 7u;
+    const uint64_t ch = n * x / 8 + (uint64_t)(blockIdx.x >> 3) * kWavesPerWG + threadIdx.x / kWave;
+    return ch < n * (x + 1) / 8 ? ch : n;
+}
+
 // Order LDS traffic among the lanes of one wavefront: no compiler reordering across it,
 // and the wave's LDS operations complete in issue order in hardware.
 __device__ __forceinline__ void wave_lds_sync()

@@ -19,6 +19,16 @@ hipError_t launch_gen_probes(Key key, uint32_t step, uint32_t probe0, uint32_t n
 // Params per streaming chunk of the perturb kernel; slice lengths are multiples of it.
 constexpr uint64_t kPerturbChunkParams = 8192;
 
+// Workgroups of a non-persistent XCD-range launch (xcd_range_chunk) over n chunks with
+// `waves` waves per workgroup: eight times those of the longest range (ranges differ by at
+// most one chunk, so the longest holds ceil(n / 8)).  Launches cover at most
+// kMaxChunksPerLaunch chunks, which keeps the grid below 2^31 workgroups.
+constexpr uint64_t kMaxChunksPerLaunch = (uint64_t)1 << 31;
+inline uint32_t xcd_range_grid(uint64_t n, uint32_t waves)
+{
+    return (uint32_t)(8 * (((n + 7) / 8 + waves - 1) / waves));
+}
+
 // theta[0..n) += alpha * z (fp32 or bf16), bits == nullptr regenerates.  slice > 0 (a
 // multiple of kPerturbChunkParams) issues the pass as one launch per slice of that many
 // params; 0 is one launch.

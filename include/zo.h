@@ -39,10 +39,11 @@
  *    different streams (the non-finite counter is updated atomically and may be shared).
  *  - Devices: a context belongs to the device that was current at zo_init; every call
  *    on it must be made with that device current, or it returns ZO_EINVAL.
- *  - Launch shapes: ZO_PERTURB_WG_PER_CU (default 8) and ZO_UPDATE_WG_PER_CU (default 16)
- *    override the workgroups per CU of the perturb and update kernels, read once per
- *    process, accepted in [1, 64].  Results do not depend on them.  ZO_UPDATE_GENERIC=1
- *    makes the update use its general kernel at every probe count (same results).
+ *  - Launch shapes: ZO_UPDATE_WG_PER_CU (default 16) overrides the workgroups per CU of the
+ *    update kernel, read once per process, accepted in [1, 64]; ZO_UPDATE_GENERIC=1 makes
+ *    the update use its general kernel at every probe count.  Results do not depend on
+ *    either.  The passes over the parameters (zo_perturb, zo_perturb2, zo_stream_rmw) run
+ *    one chunk per wave in a non-persistent grid.
  */
 #ifndef ZO_H
 #define ZO_H
