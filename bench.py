@@ -271,8 +271,9 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
         th0, _ = gen.theta_and_a(cfg)
         theta.copy_(torch.from_numpy(th0))
         mlp = {"X": torch.from_numpy(X).to(dev), "y": torch.from_numpy(y).to(dev),
-               "ws": torch.empty(zo.zo_mlp_workspace_bytes(e["batch"], e["d_in"], e["d_hid"],
-                                                           e["d_out"]), dtype=torch.uint8,
+               "ws": torch.empty(zo.zo_mlp_probes_workspace_bytes(e["batch"], e["d_in"], e["d_hid"],
+                                                                  e["d_out"], n),
+                                 dtype=torch.uint8,
                                  device=dev), "d_hid": e["d_hid"], "d_out": e["d_out"],
                "flop": 2.0 * e["batch"] * e["d_in"] * e["d_hid"]}
         del th0
@@ -299,7 +300,7 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
         if not relocation["skipped"]:
             log("[bench] placement search: " + ", ".join(
                 f"{r['gbps_whole']:.0f}/{r['gbps_sliced']:.0f}" for r in relocation["tried"]) +
-                f" GB/s (one launch / 512 MiB slices); kept allocation {relocation['kept']}")
+                f" GB/s (one launch / 1 GiB slices); kept allocation {relocation['kept']}")
 
     total = W + K
     L0s = torch.empty((total, 1), dtype=torch.float64, device=dev)
@@ -316,7 +317,7 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     per = {"perturb": [], "perturb2": [], "weights": [], "update": [], "loss": [], "mlp": [],
-           "mlp_pair": []}
+           "mlp_probes": []}
 
     def timed(kind, fn, record):
         if record:
@@ -345,9 +346,9 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
                 ctx, theta, 0, s, probe, alpha, mlp["X"], mlp["y"], mlp["d_hid"],
                 mlp["d_out"], workspace=mlp["ws"], out=out), record)
 
-    def mlp_pair(op, om, probe, s, record):
-        timed("mlp_pair", lambda: zo.zo_mlp_loss_pair(
-            ctx, theta, 0, s, probe, a, mlp["X"], mlp["y"], mlp["d_hid"], mlp["d_out"],
+    def mlp_probes(op, om, s, record):
+        timed("mlp_probes", lambda: zo.zo_mlp_loss_probes(
+            ctx, theta, 0, s, 0, n, a, mlp["X"], mlp["y"], mlp["d_hid"], mlp["d_out"],
             workspace=mlp["ws"], out_plus=op, out_minus=om), record)
 
     def one_step(s, record):
@@ -356,8 +357,7 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
             # the forward applies each probe while reading the weights: no passes over
             # theta; one paired launch sequence gives both losses of a probe
             mlp_loss(L0, None, 0.0, s, record)
-            for i in range(n):
-                mlp_pair(Lp[i:i + 1], Lm[i:i + 1], i, s, record)
+            mlp_probes(Lp, Lm, s, record)
             timed("weights", lambda: zo.zo_probe_weights(ctx, Lp, Lm, L0, a, cfg.delta,
                                                          out=c_buf), record)
             timed("update", lambda: zo.zo_update(ctx, theta, 0, s, c_buf, cfg.eta), record)
@@ -396,9 +396,9 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
     tune = None
     if mlp is None:
         # one-time choice, on this very buffer, between one launch per pass and launches per
-        # 512 MiB slice (contents unchanged); the passes below use the faster form
+        # 1 GiB slice (contents unchanged); the passes below use the faster form
         tune = zo.zo_tune_placement(ctx, theta)
-        log(f"[bench] placement: one launch {tune['gbps_whole']:.0f} GB/s, 512 MiB slices "
+        log(f"[bench] placement: one launch {tune['gbps_whole']:.0f} GB/s, 1 GiB slices "
             f"{tune['gbps_sliced']:.0f} GB/s -> slice_bytes {tune['slice_bytes']}")
         zo.zo_stream_rmw(ctx, theta)
         e0, e1 = ev(), ev()
@@ -472,10 +472,11 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
                          "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": pa / PEAK_HBM_GBPS,
                          "bytes_per_pass": pass_bytes}
     if mlp is not None:
-        mlp_ms = avg_ms("mlp_pair")
-        achieved = 2.0 * mlp["flop"] / (mlp_ms * 1e-3) / 1e12
+        mlp_ms = avg_ms("mlp_probes")
+        achieved = 2.0 * n * mlp["flop"] / (mlp_ms * 1e-3) / 1e12
         roofline = {"kernel": "k_mlp_tiles (MFMA fp32 GEMM of the MLP forward, both signs of "
-                              "a probe per launch; time of the whole loss chain)",
+                              "eight probes per launch; time of the whole zo_mlp_loss_probes "
+                              "call: tiles, row and mean kernels of all n_pert probes)",
                     "bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS,
                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
                     "traffic": None}
@@ -512,8 +513,9 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
         "data": "synthetic",
         "config": {"workload": (f"{cfg.name}: {M} {cfg.dtype} params in one flat buffer, "
                                 f"n_pert={n}, eps={cfg.eps}, eta={cfg.eta}, " +
-                                ("probes applied inside the MFMA forward, both signs per "
-                                 "launch (no passes over theta) + update" if mlp is not None else
+                                ("probes applied inside the MFMA forward, both signs of eight "
+                                 "probes per launch (no passes over theta) + update"
+                                 if mlp is not None else
                                  f"schedule {schedule} ({passes} passes + update" +
                                  (" carrying the last restore)" if schedule == "S2f"
                                   else ")")) +
@@ -528,7 +530,7 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
                        "perturb2_avg": avg_ms("perturb2"), "update_avg": upd_ms,
                        "weights_avg": w_ms, "loss_avg": avg_ms("loss"),
                        "mlp_forward_avg": avg_ms("mlp"),
-                       "mlp_pair_avg": avg_ms("mlp_pair")},
+                       "mlp_probes_avg": avg_ms("mlp_probes")},
         "roofline": roofline or {"kernel": f"k_perturb_chunks ({cfg.dtype}, probes regenerated; "
                                            f"every zo_perturb / zo_perturb2 pass)",
                                  "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,

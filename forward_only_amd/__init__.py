@@ -28,7 +28,8 @@ __all__ = [
     "zo_perturb", "zo_perturb2", "zo_probe_weights", "zo_probe_weights_ex", "zo_update",
     "zo_restore_update", "zo_nonfinite_count", "zo_reset_nonfinite", "zo_quad_loss",
     "zo_lowrank_quad_loss", "zo_mlp_workspace_bytes", "zo_mlp_loss", "zo_mlp_loss_perturbed",
-    "zo_mlp_loss_pair", "zo_mlp_loss_pair_noalloc", "zo_stream_rmw", "zo_tune_placement", "zo_set_slice_bytes",
+    "zo_mlp_loss_pair", "zo_mlp_probes_workspace_bytes", "zo_mlp_loss_probes",
+    "zo_mlp_loss_pair_noalloc", "zo_stream_rmw", "zo_tune_placement", "zo_set_slice_bytes",
     "zo_get_slice_bytes", "library_path",
 ]
 
@@ -339,6 +340,45 @@ def zo_mlp_loss_pair(ctx: Context, params: torch.Tensor, offset: int, step: int,
     return out_plus, out_minus
 
 
+def zo_mlp_probes_workspace_bytes(batch: int, d_in: int, d_hid: int, d_out: int,
+                                  n_probes: int) -> int:
+    return int(_lib.lib().zo_mlp_probes_workspace_bytes(batch, d_in, d_hid, d_out, n_probes))
+
+
+def zo_mlp_loss_probes(ctx: Context, params: torch.Tensor, offset: int, step: int, probe0: int,
+                       n_probes: int, alpha: float, X: torch.Tensor, labels: torch.Tensor,
+                       d_hid: int, d_out: int, bits: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None,
+                       out_plus: torch.Tensor | None = None,
+                       out_minus: torch.Tensor | None = None, stream=None):
+    """The MLP losses at params +/- alpha * z_i for probes probe0 .. probe0 + n_probes - 1
+    (up to eight per launch sequence), without writing params; returns (out_plus, out_minus),
+    float64 tensors of n_probes.  bits: None or (n_probes, zo_bits_stride(params)) rows."""
+    batch, d_in = X.shape
+    if params.numel() != d_hid * d_in + d_hid + d_out * d_hid + d_out:
+        raise ValueError("params must hold the MLP's parameters")
+    if labels.numel() != batch:
+        raise ValueError("one label per row")
+    need = zo_mlp_probes_workspace_bytes(batch, d_in, d_hid, d_out, n_probes)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device="cuda")
+    for name, o in (("out_plus", out_plus), ("out_minus", out_minus)):
+        if o is not None and o.numel() < n_probes:
+            raise ValueError(f"{name} is too small")
+    if out_plus is None:
+        out_plus = torch.empty(n_probes, dtype=torch.float64, device="cuda")
+    if out_minus is None:
+        out_minus = torch.empty(n_probes, dtype=torch.float64, device="cuda")
+    _lib.check(_lib.lib().zo_mlp_loss_probes(
+        ctx.handle, _dev(params, "params", torch.float32), offset, step, probe0, n_probes,
+        float(alpha), _rows(bits, n_probes, params.numel()), _dev(X, "X", torch.float32),
+        _dev(labels, "labels", torch.int64), batch, d_in, d_hid, d_out,
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _dev(out_plus, "out_plus", torch.float64), _dev(out_minus, "out_minus", torch.float64),
+        _stream(stream)), "zo_mlp_loss_probes")
+    return out_plus, out_minus
+
+
 def zo_mlp_loss_pair_noalloc(ctx: Context, params: torch.Tensor, offset: int, step: int,
                              probe: int, alpha: float, X: torch.Tensor, labels: torch.Tensor,
                              d_hid: int, d_out: int, out_plus: torch.Tensor,
@@ -369,7 +409,7 @@ def zo_stream_rmw(ctx: Context, buf: torch.Tensor, mask: int = 0, stream=None) -
 
 
 def zo_tune_placement(ctx: Context, buf: torch.Tensor, stream=None) -> dict:
-    """Time a pass over `buf` as one launch and as 512 MiB slices (contents unchanged), keep
+    """Time a pass over `buf` as one launch and as 1 GiB slices (contents unchanged), keep
     the faster form in the context; returns {"slice_bytes", "gbps_whole", "gbps_sliced"}."""
     sl, gw, gs = ctypes.c_uint64(), ctypes.c_double(), ctypes.c_double()
     nbytes = buf.numel() * buf.element_size()

@@ -47,6 +47,9 @@ SIGNATURES = {
                                      _u32, _u32, _u32, _vp, _u64, _vp, _vp]),
     "zo_mlp_loss_pair": (_int, [_vp, _vp, _u64, _u32, _u32, _f32, _vp, _vp, _vp, _u32,
                                 _u32, _u32, _u32, _vp, _u64, _vp, _vp, _vp]),
+    "zo_mlp_probes_workspace_bytes": (_u64, [_u32, _u32, _u32, _u32, _u32]),
+    "zo_mlp_loss_probes": (_int, [_vp, _vp, _u64, _u32, _u32, _u32, _f32, _vp, _vp, _vp, _u32,
+                                  _u32, _u32, _u32, _vp, _u64, _vp, _vp, _vp]),
     "zo_mlp_loss_pair_noalloc": (_int, [_vp, _vp, _u64, _u32, _u32, _f32, _vp, _vp, _vp, _u32,
                                         _u32, _u32, _u32, _vp, _vp, _vp]),
     "zo_stream_rmw": (_int, [_vp, _vp, _u64, _u32, _vp]),

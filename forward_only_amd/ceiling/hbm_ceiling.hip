@@ -10,9 +10,11 @@
 //                                allocations held at once (default 59.92 GB, 6)
 //
 // Each kernel walks 16 KiB chunks per wave (16 dwordx4 per lane, one contiguous KiB per
-// instruction) in the same order as the perturb kernel: the buffer is split into eight
-// contiguous ranges, one per XCD (workgroup b runs on XCD b % 8), each walked grid-stride
-// by its XCD's workgroups.  Loads and stores carry the non-temporal hint (the fastest
+// instruction); the buffer is split into eight contiguous ranges, one per XCD (workgroup b
+// runs on XCD b % 8).  Two forms: persistent (each XCD's range walked grid-stride by a few
+// resident workgroups per CU, launch shapes 2-16 workgroups per CU) and non-persistent
+// (one chunk per wave, each XCD's chunks taken in dispatch order -- the order of the
+// library's passes).  Loads and stores carry the non-temporal hint (the fastest
 // setting measured for streaming here).  Every figure is bytes moved / kernel time (HIP
 // events), best over the launch shapes tried.  A large buffer's bandwidth depends on the
 // physical memory the allocation lands on (the same physical memory mapped at other
@@ -109,6 +111,66 @@ __global__ __launch_bounds__(256) void k_rmw(u32x4_t *__restrict__ p, uint64_t n
     }
 }
 
+// Non-persistent walk: the wave's chunk (one per wave, XCD ranges in dispatch order), or n.
+__device__ __forceinline__ uint64_t np_chunk(uint64_t n)
+{
+    const uint64_t x = blockIdx.x & 7u;
+    const uint64_t ch = n * x / 8 + (uint64_t)(blockIdx.x >> 3) * 4 + (threadIdx.x >> 6);
+    return ch < n * (x + 1) / 8 ? ch : n;
+}
+static uint32_t np_grid(uint64_t n) { return (uint32_t)(8 * (((n + 7) / 8 + 3) / 4)); }
+
+__global__ __launch_bounds__(256) void k_read_np(const u32x4_t *__restrict__ p, uint64_t n,
+                                                 uint32_t *__restrict__ sink)
+{
+    const uint64_t ch = np_chunk(n);
+    if (ch >= n) return;
+    const u32x4_t *b = p + ch * kChunk16 + (threadIdx.x & 63);
+    u32x4_t acc = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) acc ^= __builtin_nontemporal_load(b + k * 64);
+    if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) sink[0] = acc.x;   // keeps the loads
+}
+
+__global__ __launch_bounds__(256) void k_write_np(u32x4_t *__restrict__ p, uint64_t n)
+{
+    const uint64_t ch = np_chunk(n);
+    if (ch >= n) return;
+    u32x4_t *b = p + ch * kChunk16 + (threadIdx.x & 63);
+    const u32x4_t v = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) __builtin_nontemporal_store(v, b + k * 64);
+}
+
+__global__ __launch_bounds__(256) void k_copy_np(const u32x4_t *__restrict__ src,
+                                                 u32x4_t *__restrict__ dst, uint64_t n)
+{
+    const uint64_t ch = np_chunk(n);
+    if (ch >= n) return;
+    const u32x4_t *s = src + ch * kChunk16 + (threadIdx.x & 63);
+    u32x4_t *d = dst + ch * kChunk16 + (threadIdx.x & 63);
+    u32x4_t v[kLoads];
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) v[k] = __builtin_nontemporal_load(s + k * 64);
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) __builtin_nontemporal_store(v[k], d + k * 64);
+}
+
+__global__ __launch_bounds__(256) void k_rmw_np(u32x4_t *__restrict__ p, uint64_t n)
+{
+    const uint64_t ch = np_chunk(n);
+    if (ch >= n) return;
+    u32x4_t *b = p + ch * kChunk16 + (threadIdx.x & 63);
+    u32x4_t v[kLoads];
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) v[k] = __builtin_nontemporal_load(b + k * 64);
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+        v[k] += 0x00010001u;
+        __builtin_nontemporal_store(v[k], b + k * 64);
+    }
+}
+
 template <typename F>
 static float time_ms(F launch, int iters)
 {
@@ -130,14 +192,26 @@ static float time_ms(F launch, int iters)
     return ms / iters;
 }
 
-// In-place RMW bandwidth of one buffer, one launch of 8 workgroups per CU (the perturb
-// kernel's default shape).
-static double rmw_gbps(char *buf, uint64_t nchunks, int cus)
+// In-place RMW bandwidth of one buffer: persistent (one launch of 8 workgroups per CU),
+// non-persistent as one launch, and non-persistent per 1 GiB slice.
+struct RmwRates {
+    double persistent, np, np_sliced;
+};
+static RmwRates rmw_gbps(char *buf, uint64_t nchunks, int cus)
 {
     u32x4_t *p = reinterpret_cast<u32x4_t *>(buf);
     const int grid = cus * 8;
-    return 2.0 * nchunks * kChunk16 * 16 /
-           (time_ms([&] { hipLaunchKernelGGL(k_rmw, dim3(grid), dim3(256), 0, 0, p, nchunks); }, 3) * 1e6);
+    const double bytes = 2.0 * nchunks * kChunk16 * 16;
+    const uint64_t sl = (1ull << 30) / (kChunk16 * 16);   // chunks per 1 GiB slice
+    RmwRates r;
+    r.persistent = bytes / (time_ms([&] { hipLaunchKernelGGL(k_rmw, dim3(grid), dim3(256), 0, 0, p, nchunks); }, 3) * 1e6);
+    r.np = bytes / (time_ms([&] { hipLaunchKernelGGL(k_rmw_np, dim3(np_grid(nchunks)), dim3(256), 0, 0, p, nchunks); }, 3) * 1e6);
+    r.np_sliced = bytes / (time_ms([&] {
+        for (uint64_t s0 = 0; s0 < nchunks; s0 += sl) {
+            const uint64_t m = nchunks - s0 < sl ? nchunks - s0 : sl;
+            hipLaunchKernelGGL(k_rmw_np, dim3(np_grid(m)), dim3(256), 0, 0, p + s0 * kChunk16, m);
+        } }, 3) * 1e6);
+    return r;
 }
 
 // --allocations mode: the placement of successive allocations of one size.  First `count`
@@ -152,13 +226,15 @@ static int allocations(double gb, int count)
     const uint64_t bytes = nchunks * chunk_bytes;
     size_t fr, tot;
     CHECK(hipMemGetInfo(&fr, &tot));
-    printf("allocations of %.3f GB; device memory free %.1f of %.1f GB; in-place RMW, 8 "
-           "workgroups per CU\n", bytes / 1e9, fr / 1e9, tot / 1e9);
+    printf("allocations of %.3f GB; device memory free %.1f of %.1f GB; in-place RMW GB/s: "
+           "persistent (8 workgroups per CU) / non-persistent / non-persistent per 1 GiB slice\n",
+           bytes / 1e9, fr / 1e9, tot / 1e9);
     for (int r = 0; r < count; ++r) {
         char *buf;
         CHECK(hipMalloc(&buf, bytes));
         CHECK(hipMemset(buf, 0, bytes));
-        printf("allocate-measure-free %d: %.0f GB/s\n", r, rmw_gbps(buf, nchunks, cus));
+        const RmwRates g = rmw_gbps(buf, nchunks, cus);
+        printf("allocate-measure-free %d: %.0f / %.0f / %.0f\n", r, g.persistent, g.np, g.np_sliced);
         fflush(stdout);
         CHECK(hipFree(buf));
     }
@@ -169,7 +245,8 @@ static int allocations(double gb, int count)
         if (fr < bytes + (4ull << 30)) break;
         CHECK(hipMalloc(&held[nh], bytes));
         CHECK(hipMemset(held[nh], 0, bytes));
-        printf("held %d: %.0f GB/s\n", nh, rmw_gbps(held[nh], nchunks, cus));
+        const RmwRates g = rmw_gbps(held[nh], nchunks, cus);
+        printf("held %d: %.0f / %.0f / %.0f\n", nh, g.persistent, g.np, g.np_sliced);
         fflush(stdout);
         ++nh;
     }
@@ -214,6 +291,21 @@ int main(int argc, char **argv)
             gbs[3] = 2.0 * bytes / (time_ms([&] { hipLaunchKernelGGL(k_rmw, dim3(grid), dim3(256), 0, 0, p, nchunks); }, 5) * 1e6);
             printf("round %d workgroups/CU %2d: read %.1f  write %.1f  copy %.1f  rmw %.1f GB/s\n", r,
                    wpc, gbs[0], gbs[1], gbs[2], gbs[3]);
+            fflush(stdout);
+            for (int i = 0; i < 4; ++i)
+                if (gbs[i] > best[i]) best[i] = gbs[i];
+        }
+        {   // non-persistent form: one chunk per wave
+            u32x4_t *p = reinterpret_cast<u32x4_t *>(buf);
+            const uint64_t half = nchunks / 2;
+            double gbs[4];
+            gbs[0] = bytes / (time_ms([&] { hipLaunchKernelGGL(k_read_np, dim3(np_grid(nchunks)), dim3(256), 0, 0, p, nchunks, sink); }, 5) * 1e6);
+            gbs[1] = bytes / (time_ms([&] { hipLaunchKernelGGL(k_write_np, dim3(np_grid(nchunks)), dim3(256), 0, 0, p, nchunks); }, 5) * 1e6);
+            gbs[2] = 2.0 * half * chunk_bytes /
+                     (time_ms([&] { hipLaunchKernelGGL(k_copy_np, dim3(np_grid(half)), dim3(256), 0, 0, p, p + half * kChunk16, half); }, 5) * 1e6);
+            gbs[3] = 2.0 * bytes / (time_ms([&] { hipLaunchKernelGGL(k_rmw_np, dim3(np_grid(nchunks)), dim3(256), 0, 0, p, nchunks); }, 5) * 1e6);
+            printf("round %d non-persistent  : read %.1f  write %.1f  copy %.1f  rmw %.1f GB/s\n", r,
+                   gbs[0], gbs[1], gbs[2], gbs[3]);
             fflush(stdout);
             for (int i = 0; i < 4; ++i)
                 if (gbs[i] > best[i]) best[i] = gbs[i];

@@ -70,8 +70,9 @@ inline uint64_t slice_params(const zo_ctx *c, uint64_t elem)
     return p / zo::kPerturbChunkParams * zo::kPerturbChunkParams;
 }
 
-// Slice size zo_tune_placement tries against one whole launch.
-constexpr uint64_t kTuneSliceBytes = (uint64_t)512 << 20;
+// Slice size zo_tune_placement tries against one whole launch: on 60 GB and 25.7 GB
+// buffers, 1 GiB slices gave the perturb pass its best sliced rate (256 MiB - 8 GiB tried).
+constexpr uint64_t kTuneSliceBytes = (uint64_t)1 << 30;
 
 // Common checks for a parameter range [offset, offset + n).
 inline bool range_ok(uint64_t offset, uint64_t n)
@@ -304,6 +305,15 @@ uint64_t zo_mlp_workspace_bytes(uint32_t batch, uint32_t d_in, uint32_t d_hid, u
     return 2u * ((uint64_t)(d_hid / 16u) * batch * d_out + batch) * sizeof(double);
 }
 
+uint64_t zo_mlp_probes_workspace_bytes(uint32_t batch, uint32_t d_in, uint32_t d_hid,
+                                       uint32_t d_out, uint32_t n_probes)
+{
+    (void)d_in;
+    // partial logits and row losses of both signs of up to kMlpProbesPerLaunch probes
+    const uint64_t k = n_probes < zo::kMlpProbesPerLaunch ? n_probes : zo::kMlpProbesPerLaunch;
+    return 2u * k * ((uint64_t)(d_hid / 16u) * batch * d_out + batch) * sizeof(double);
+}
+
 static zo_status mlp_checks(zo_ctx *c, const float *d_params, const float *d_X,
                             const int64_t *d_labels, uint32_t batch, uint32_t d_in,
                             uint32_t d_hid, uint32_t d_out, void *d_workspace,
@@ -368,6 +378,32 @@ zo_status zo_mlp_loss_pair(zo_ctx *c, const float *d_params, uint64_t offset, ui
     return from_hip(zo::launch_mlp_loss(d_params, d_X, d_labels, batch, d_in, d_hid, d_out,
                                         static_cast<double *>(d_workspace), d_loss_plus, &pert,
                                         key_of(c), as_stream(stream), d_loss_minus));
+}
+
+zo_status zo_mlp_loss_probes(zo_ctx *c, const float *d_params, uint64_t offset, uint32_t step,
+                             uint32_t probe0, uint32_t n_probes, float alpha,
+                             const uint8_t *d_bits, const float *d_X, const int64_t *d_labels,
+                             uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out,
+                             void *d_workspace, uint64_t workspace_bytes, double *d_loss_plus,
+                             double *d_loss_minus, void *stream)
+{
+    if (!ctx_ok(c)) return ZO_EINVAL;
+    if (n_probes == 0) return ZO_OK;
+    const zo_status st = mlp_checks(c, d_params, d_X, d_labels, batch, d_in, d_hid, d_out,
+                                    d_workspace, UINT64_MAX, d_loss_plus);
+    if (st != ZO_OK) return st;
+    if (!d_loss_minus) return ZO_EINVAL;
+    if (workspace_bytes < zo_mlp_probes_workspace_bytes(batch, d_in, d_hid, d_out, n_probes))
+        return ZO_EINVAL;
+    if (n_probes - 1 > UINT32_MAX - probe0) return ZO_EINVAL;   // probe indices wrap
+    if (d_bits && !aligned16(d_bits)) return ZO_EINVAL;
+    const uint64_t nparams = (uint64_t)d_hid * d_in + d_hid + (uint64_t)d_out * d_hid + d_out;
+    if (!range_ok(offset, nparams)) return ZO_EINVAL;
+    const zo::MlpPerturb pert{offset, step, probe0, alpha, d_bits};
+    return from_hip(zo::launch_mlp_loss_probes(d_params, d_X, d_labels, batch, d_in, d_hid, d_out,
+                                               static_cast<double *>(d_workspace), pert, n_probes,
+                                               key_of(c), d_loss_plus, d_loss_minus,
+                                               as_stream(stream)));
 }
 
 zo_status zo_mlp_loss_pair_noalloc(zo_ctx *c, const float *d_params, uint64_t offset,

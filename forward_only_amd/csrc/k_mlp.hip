@@ -24,8 +24,12 @@
 // Paired variant (kPair): the losses at +alpha and -alpha in one launch sequence; each W1
 // operand is loaded once and feeds two accumulators (the second sees theta_j + (bit ?
 // -alpha : alpha)), each with exactly the MFMA sequence of a single fused launch, so both
-// losses equal the single fused results bit for bit.  Sign s (0: +alpha, 1: -alpha) writes
-// its partial logits, row losses and loss to its own slots.
+// losses equal the single fused results bit for bit.
+// Several probes (kNP > 1): probes probe .. probe+kNP-1 in one launch sequence, both signs
+// each, so every X and W1 operand loaded feeds 2*kNP accumulators -- the forward's loads are
+// shared by all the step's probes of the launch, while each accumulator still runs exactly
+// the single fused launch's MFMA sequence.  Slot s = 2i + sign (i < kNP; sign 0: +alpha,
+// 1: -alpha) writes its partial logits, row losses and loss to its own places.
 #include <stdlib.h>
 
 #include "zo_device.hpp"
@@ -35,22 +39,24 @@ namespace zo {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// Sign source for the fused variant: Philox of (global block, probe, step) or a plane.
+// Sign source for the fused variant: Philox of (global block, probe, step) or stored rows.
 struct PertArgs {
     uint64_t offset;      // global index of params[0] (multiple of 128)
-    uint32_t step, probe, k0, k1;
+    uint32_t step, probe, k0, k1;   // probe: the launch's first probe
     float alpha;
-    const uint8_t *bits;  // packed row over the params, or nullptr
+    const uint8_t *bits;  // packed rows over the params (row i: probe + i), or nullptr
+    uint64_t bits_stride; // bytes per row
 };
 
-// Sign bits of the 4 consecutive params j .. j+3 (j % 4 == 0) in the low 4 bits.
-__device__ __forceinline__ uint32_t quad_bits(const PertArgs &p, uint64_t j)
+// Sign bits of the 4 consecutive params j .. j+3 (j % 4 == 0) of probe p.probe + i in the
+// low 4 bits.
+__device__ __forceinline__ uint32_t quad_bits(const PertArgs &p, uint32_t i, uint64_t j)
 {
     if (p.bits) {
-        return (uint32_t)(p.bits[j >> 3] >> (j & 4)) & 0xFu;
+        return (uint32_t)(p.bits[(uint64_t)i * p.bits_stride + (j >> 3)] >> (j & 4)) & 0xFu;
     }
     const uint64_t g = p.offset + j;
-    const U32x4 r = probe_block_bits(g >> 7, p.probe, p.step, p.k0, p.k1);
+    const U32x4 r = probe_block_bits(g >> 7, p.probe + i, p.step, p.k0, p.k1);
     const uint32_t sel = (uint32_t)(g >> 5) & 3u;
     const uint32_t word = sel == 0 ? r.x : sel == 1 ? r.y : sel == 2 ? r.z : r.w;
     return (word >> (g & 31)) & 0xFu;
@@ -61,13 +67,14 @@ __device__ __forceinline__ float with_sign(float v, uint32_t bit, float alpha)
     return v + (bit ? alpha : -alpha);
 }
 
+// Parameter j as the forward of probe p.probe + i with step `alpha` reads it.
 __device__ __forceinline__ float param(const float *params, uint64_t j, const PertArgs &p,
-                                       bool pert)
+                                       uint32_t i, float alpha, bool pert)
 {
     const float v = params[j];
     if (!pert) return v;
-    const uint32_t b = quad_bits(p, j & ~(uint64_t)3) >> (j & 3);
-    return with_sign(v, b & 1u, p.alpha);
+    const uint32_t b = quad_bits(p, i, j & ~(uint64_t)3) >> (j & 3);
+    return with_sign(v, b & 1u, alpha);
 }
 
 __device__ __forceinline__ float gelu_exact(float x)
@@ -75,7 +82,9 @@ __device__ __forceinline__ float gelu_exact(float x)
     return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
 }
 
-template <bool kPert, bool kPair>
+// kNP: probes of the launch (0: the clean loss, no perturbation); kPair: both signs per
+// probe.  kNS accumulator slots, slot s = probe s / kPer, sign s % kPer.
+template <int kNP, bool kPair>
 __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
                                                   const float *__restrict__ params,
                                                   uint32_t batch, uint32_t d_in, uint32_t d_hid,
@@ -94,27 +103,50 @@ __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
     const uint64_t wrow = (uint64_t)(n0 + li) * d_in + 4u * kq;   // flat index in params
     const float *wptr = params + wrow;
 
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    f32x4_t acc2 = {0.0f, 0.0f, 0.0f, 0.0f};   // kPair: the -alpha accumulator
+    constexpr bool kPert = kNP > 0;
+    constexpr int kPer = kPair ? 2 : 1;
+    constexpr int kNS = kPert ? kNP * kPer : 1;
+    constexpr int kNB = kPert ? kNP : 1;
+    f32x4_t acc[kNS];
+#pragma unroll
+    for (int s = 0; s < kNS; ++s) acc[s] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     uint64_t cached_blk = ~(uint64_t)0;
-    U32x4 cw = {0u, 0u, 0u, 0u};
+    // the four Philox words of the cached block, one array per word (an array of 4-word
+    // structs picked by a run-time word index ends up in scratch memory)
+    uint32_t cwx[kNB], cwy[kNB], cwz[kNB], cww[kNB];
+#pragma unroll
+    for (int i = 0; i < kNB; ++i) cwx[i] = cwy[i] = cwz[i] = cww[i] = 0u;
 
-    // Sign bits of the 4 params j .. j+3 of W1 (j a multiple of 4) in the low 4 bits.
-    auto bits4 = [&](uint64_t j) -> uint32_t {
-        uint32_t q;
+    // Sign bits of the 4 params j .. j+3 of W1 (j a multiple of 4) of each probe of the
+    // launch, in the low 4 bits of q[i].  The probes share the parameters, so one block
+    // change refreshes all their Philox words.
+    auto bits4 = [&](uint64_t j, uint32_t (&q)[kNB]) {
         if (pa.bits) {
-            q = (uint32_t)(pa.bits[j >> 3] >> (j & 4)) & 0xFu;
-        } else {
-            const uint64_t g = pa.offset + j;
-            if ((g >> 7) != cached_blk) {
-                cached_blk = g >> 7;
-                cw = probe_block_bits(cached_blk, pa.probe, pa.step, pa.k0, pa.k1);
-            }
-            const uint32_t sel = (uint32_t)(g >> 5) & 3u;
-            const uint32_t word = sel == 0 ? cw.x : sel == 1 ? cw.y : sel == 2 ? cw.z : cw.w;
-            q = (word >> (g & 31)) & 0xFu;
+#pragma unroll
+            for (int i = 0; i < kNB; ++i)
+                q[i] = (uint32_t)(pa.bits[(uint64_t)i * pa.bits_stride + (j >> 3)] >> (j & 4)) & 0xFu;
+            return;
         }
-        return q;
+        const uint64_t g = pa.offset + j;
+        if ((g >> 7) != cached_blk) {
+            cached_blk = g >> 7;
+#pragma unroll
+            for (int i = 0; i < kNB; ++i) {
+                const U32x4 w = probe_block_bits(cached_blk, pa.probe + (uint32_t)i, pa.step,
+                                                 pa.k0, pa.k1);
+                cwx[i] = w.x;
+                cwy[i] = w.y;
+                cwz[i] = w.z;
+                cww[i] = w.w;
+            }
+        }
+        const bool odd = (g >> 5) & 1u, high = (g >> 6) & 1u;   // word (g >> 5) & 3
+#pragma unroll
+        for (int i = 0; i < kNB; ++i) {
+            const uint32_t lo = odd ? cwy[i] : cwx[i];
+            const uint32_t hi = odd ? cww[i] : cwz[i];
+            q[i] = ((high ? hi : lo) >> (g & 31)) & 0xFu;
+        }
     };
     auto mfma4 = [](f32x4_t &c, const f32x4_t &a, const f32x4_t &b) {
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
@@ -125,26 +157,33 @@ __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
     // One 16-k group: operand a of X, operand b of W1 at flat index j.
     auto group = [&](const f32x4_t &a, const f32x4_t &b, uint64_t j) {
         if constexpr (!kPert) {
-            mfma4(acc, a, b);
+            mfma4(acc[0], a, b);
         } else {
-            const uint32_t q = bits4(j);
-            f32x4_t bp;
+            uint32_t q[kNB];
+            bits4(j, q);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) bp[t] = with_sign(b[t], (q >> t) & 1u, pa.alpha);
-            mfma4(acc, a, bp);
-            if constexpr (kPair) {
-                f32x4_t bm;
+            for (int i = 0; i < kNP; ++i) {
+                f32x4_t bp;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) bm[t] = with_sign(b[t], (q >> t) & 1u, -pa.alpha);
-                mfma4(acc2, a, bm);
+                for (int t = 0; t < 4; ++t) bp[t] = with_sign(b[t], (q[i] >> t) & 1u, pa.alpha);
+                mfma4(acc[kPer * i], a, bp);
+                if constexpr (kPair) {
+                    f32x4_t bm;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        bm[t] = with_sign(b[t], (q[i] >> t) & 1u, -pa.alpha);
+                    mfma4(acc[kPer * i + 1], a, bm);
+                }
             }
         }
     };
 
     // Stages of kStage K-groups (16 k each): the loads of stage s+1 are in flight while
     // stage s runs through the MFMAs, so memory latency is paid once per kernel rather
-    // than once per 16 k.
-    constexpr uint32_t kStage = 8;
+    // than once per 16 k.  With several probes each stage carries 2*kNP times the MFMA work,
+    // so shorter stages suffice (and keep the registers from spilling).  The k order, and
+    // with it every accumulator's sequence, does not depend on the staging.
+    constexpr uint32_t kStage = kNP >= 8 ? 2 : kNP >= 2 ? 4 : 8;
     const uint32_t kfull = (d_in / (16u * kStage)) * (16u * kStage);
     f32x4_t a0[kStage], b0[kStage], a1[kStage], b1[kStage];
     auto load_stage = [&](f32x4_t (&a)[kStage], f32x4_t (&b)[kStage], uint32_t kb) {
@@ -186,17 +225,17 @@ __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
     const uint64_t pset = (uint64_t)n_tiles * batch * d_out;   // one sign's partial logits
     const uint32_t n = n0 + li;
 #pragma unroll
-    for (int sgn = 0; sgn < (kPair ? 2 : 1); ++sgn) {
-        PertArgs ps = pa;
-        if (sgn) ps.alpha = -pa.alpha;
-        const f32x4_t &c = sgn ? acc2 : acc;
-        double *out = partial + (uint64_t)sgn * pset;
-        const float bias = param(params, b1_at + n, ps, kPert);
+    for (int slot = 0; slot < kNS; ++slot) {
+        const uint32_t pi = (uint32_t)(slot / kPer);
+        const float alpha = (slot % kPer) ? -pa.alpha : pa.alpha;
+        const f32x4_t &c = acc[slot];
+        double *out = partial + (uint64_t)slot * pset;
+        const float bias = param(params, b1_at + n, pa, pi, alpha, kPert);
         float g[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) g[r] = gelu_exact(c[r] + bias);
         for (uint32_t o = 0; o < d_out; ++o) {
-            const float w2 = param(params, w2_at + (uint64_t)o * d_hid + n, ps, kPert);
+            const float w2 = param(params, w2_at + (uint64_t)o * d_hid + n, pa, pi, alpha, kPert);
             float p[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) p[r] = g[r] * w2;
@@ -221,14 +260,15 @@ __global__ __launch_bounds__(256) void k_mlp_rows(const double *__restrict__ par
                                                   const int64_t *__restrict__ labels,
                                                   uint32_t batch, uint32_t d_in, uint32_t d_hid,
                                                   uint32_t d_out, double *__restrict__ rowloss,
-                                                  PertArgs pa)
+                                                  PertArgs pa, uint32_t per)
 {
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t m = blockIdx.x * 4u + (threadIdx.x >> 6);
     if (m >= batch) return;
     const uint32_t n_tiles = d_hid / 16;
-    // sign slot blockIdx.y (paired launch: 1 is the -alpha loss)
-    if (blockIdx.y) pa.alpha = -pa.alpha;
+    // slot blockIdx.y: probe pa.probe + blockIdx.y / per, -alpha for the odd slots of pairs
+    const uint32_t pi = blockIdx.y / per;
+    const float alpha = (blockIdx.y % per) ? -pa.alpha : pa.alpha;
     partial += (uint64_t)blockIdx.y * n_tiles * batch * d_out;
     rowloss += (uint64_t)blockIdx.y * batch;
     const uint64_t b2_at = (uint64_t)d_hid * d_in + d_hid + (uint64_t)d_out * d_hid;
@@ -240,7 +280,7 @@ __global__ __launch_bounds__(256) void k_mlp_rows(const double *__restrict__ par
         for (uint32_t t = lane; t < n_tiles; t += 64) s += row[t];
 #pragma unroll
         for (int w = 32; w >= 1; w >>= 1) s += __shfl_xor(s, w, 64);
-        s += (double)param(params, b2_at + o, pa, kPert);
+        s += (double)param(params, b2_at + o, pa, pi, alpha, kPert);
         z[o] = s;
         zmax = s > zmax ? s : zmax;
     }
@@ -255,12 +295,12 @@ __global__ __launch_bounds__(256) void k_mlp_rows(const double *__restrict__ par
 
 __global__ __launch_bounds__(256) void k_mlp_mean(const double *__restrict__ rowloss,
                                                   uint32_t batch, double *__restrict__ out,
-                                                  double *__restrict__ out2)
+                                                  double *__restrict__ out2, uint32_t per)
 {
     __shared__ double red[256];
-    // sign slot blockIdx.x (paired launch: 1 is the -alpha loss, written to out2)
+    // slot blockIdx.x: probe blockIdx.x / per; the -alpha slot of a pair writes to out2
     rowloss += (uint64_t)blockIdx.x * batch;
-    if (blockIdx.x) out = out2;
+    out = ((blockIdx.x % per) ? out2 : out) + blockIdx.x / per;
     double acc = 0.0;
     for (uint32_t m = threadIdx.x; m < batch; m += blockDim.x) acc += rowloss[m];
     red[threadIdx.x] = acc;
@@ -272,20 +312,41 @@ __global__ __launch_bounds__(256) void k_mlp_mean(const double *__restrict__ row
     if (threadIdx.x == 0) *out = red[0] / (double)batch;
 }
 
-template <bool kPert, bool kPair>
+template <int kNP, bool kPair>
 static void launch_chain(const float *params, const float *X, const int64_t *labels,
                          uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out,
                          double *partial, double *out, double *out2, const PertArgs &pa,
                          hipStream_t stream)
 {
     const uint32_t tiles = (batch / 16) * (d_hid / 16);
-    const uint32_t nsign = kPair ? 2u : 1u;
-    double *rowloss = partial + (uint64_t)nsign * (d_hid / 16) * batch * d_out;
-    hipLaunchKernelGGL((k_mlp_tiles<kPert, kPair>), dim3(tiles), dim3(64), 0, stream, X, params,
+    const uint32_t per = kPair ? 2u : 1u;
+    const uint32_t nslot = kNP > 0 ? (uint32_t)kNP * per : 1u;
+    double *rowloss = partial + (uint64_t)nslot * (d_hid / 16) * batch * d_out;
+    hipLaunchKernelGGL((k_mlp_tiles<kNP, kPair>), dim3(tiles), dim3(64), 0, stream, X, params,
                        batch, d_in, d_hid, d_out, partial, pa);
-    hipLaunchKernelGGL(k_mlp_rows<kPert>, dim3((batch + 3) / 4, nsign), dim3(256), 0, stream,
-                       partial, params, labels, batch, d_in, d_hid, d_out, rowloss, pa);
-    hipLaunchKernelGGL(k_mlp_mean, dim3(nsign), dim3(256), 0, stream, rowloss, batch, out, out2);
+    hipLaunchKernelGGL(k_mlp_rows<(kNP > 0)>, dim3((batch + 3) / 4, nslot), dim3(256), 0, stream,
+                       partial, params, labels, batch, d_in, d_hid, d_out, rowloss, pa, per);
+    hipLaunchKernelGGL(k_mlp_mean, dim3(nslot), dim3(256), 0, stream, rowloss, batch, out, out2,
+                       per);
+}
+
+static PertArgs pert_args(const MlpPerturb *pert, Key key, uint64_t nparams)
+{
+    PertArgs pa{0, 0, 0, key.k0, key.k1, 0.0f, nullptr, 0};
+    if (pert) {
+        pa.offset = pert->offset;
+        pa.step = pert->step;
+        pa.probe = pert->probe;
+        pa.alpha = pert->alpha;
+        pa.bits = pert->bits;
+        pa.bits_stride = (nparams + 127) / 128 * 16;
+    }
+    return pa;
+}
+
+static uint64_t mlp_params(uint32_t d_in, uint32_t d_hid, uint32_t d_out)
+{
+    return (uint64_t)d_hid * d_in + d_hid + (uint64_t)d_out * d_hid + d_out;
 }
 
 hipError_t launch_mlp_loss(const float *params, const float *X, const int64_t *labels,
@@ -293,24 +354,52 @@ hipError_t launch_mlp_loss(const float *params, const float *X, const int64_t *l
                            double *partial, double *out, const MlpPerturb *pert, Key key,
                            hipStream_t stream, double *out_minus)
 {
-    PertArgs pa{0, 0, 0, key.k0, key.k1, 0.0f, nullptr};
+    const PertArgs pa = pert_args(pert, key, mlp_params(d_in, d_hid, d_out));
     if (pert) {
-        pa.offset = pert->offset;
-        pa.step = pert->step;
-        pa.probe = pert->probe;
-        pa.alpha = pert->alpha;
-        pa.bits = pert->bits;
         if (out_minus)
-            launch_chain<true, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, out,
-                                     out_minus, pa, stream);
+            launch_chain<1, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, out,
+                                  out_minus, pa, stream);
         else
-            launch_chain<true, false>(params, X, labels, batch, d_in, d_hid, d_out, partial, out,
-                                      nullptr, pa, stream);
-    } else {
-        launch_chain<false, false>(params, X, labels, batch, d_in, d_hid, d_out, partial, out,
+            launch_chain<1, false>(params, X, labels, batch, d_in, d_hid, d_out, partial, out,
                                    nullptr, pa, stream);
+    } else {
+        launch_chain<0, false>(params, X, labels, batch, d_in, d_hid, d_out, partial, out,
+                               nullptr, pa, stream);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_mlp_loss_probes(const float *params, const float *X, const int64_t *labels,
+                                  uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out,
+                                  double *partial, const MlpPerturb &pert, uint32_t nprobes,
+                                  Key key, double *out_plus, double *out_minus,
+                                  hipStream_t stream)
+{
+    const uint64_t nparams = mlp_params(d_in, d_hid, d_out);
+    // launches of 8 probes, then 4, 2, 1 for the rest; each reuses the workspace from its
+    // start (the launches run in order on the stream)
+    for (uint32_t done = 0; done < nprobes;) {
+        const uint32_t left = nprobes - done;
+        const uint32_t k = left >= kMlpProbesPerLaunch ? kMlpProbesPerLaunch
+                           : left >= 4             ? 4u
+                           : left >= 2             ? 2u
+                                                   : 1u;
+        MlpPerturb p = pert;
+        p.probe = pert.probe + done;
+        if (pert.bits) p.bits = pert.bits + (uint64_t)done * ((nparams + 127) / 128 * 16);
+        const PertArgs pa = pert_args(&p, key, nparams);
+        double *op = out_plus + done, *om = out_minus + done;
+        switch (k) {
+        case 8: launch_chain<8, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream); break;
+        case 4: launch_chain<4, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream); break;
+        case 2: launch_chain<2, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream); break;
+        default: launch_chain<1, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream); break;
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        done += k;
+    }
+    return hipSuccess;
 }
 
 }  // namespace zo

@@ -97,6 +97,17 @@ hipError_t launch_mlp_loss(const float *params, const float *X, const int64_t *l
                            double *partial, double *out, const MlpPerturb *pert, Key key,
                            hipStream_t stream, double *out_minus = nullptr);
 
+// Both losses of probes pert.probe .. pert.probe + nprobes - 1 (out_plus[i], out_minus[i]),
+// up to kMlpProbesPerLaunch probes per launch sequence sharing every operand load; pert.bits
+// (if given) holds nprobes packed rows.  The workspace holds 2 * min(nprobes,
+// kMlpProbesPerLaunch) slots of partial logits and row losses.
+constexpr uint32_t kMlpProbesPerLaunch = 8;
+hipError_t launch_mlp_loss_probes(const float *params, const float *X, const int64_t *labels,
+                                  uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out,
+                                  double *partial, const MlpPerturb &pert, uint32_t nprobes,
+                                  Key key, double *out_plus, double *out_minus,
+                                  hipStream_t stream);
+
 // Diagnostic: every 16-byte word of buf (bytes % 16 == 0) <- word ^ mask, in place;
 // slice_bytes > 0 (a multiple of 16 KiB) issues it as one launch per slice of that size.
 hipError_t launch_stream_rmw(void *buf, uint64_t bytes, uint32_t mask, int num_cus,

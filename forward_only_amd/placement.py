@@ -2,9 +2,9 @@
 
 The streaming bandwidth of a large allocation depends on the physical memory the driver
 gives it, which neither the kernels nor the caller choose: on MI355X a 60 GB buffer read
-and written back in place runs at about 5.2 TB/s on some allocations and 6.1-6.3 TB/s on
-others (512 MiB launches, which `zo_tune_placement` picks on slow memory, reach about
-5.8 TB/s on either).  Allocations made while earlier ones are still held land on other
+and written back in place as one launch runs at about 5.8 TB/s on some allocations and
+6.3-6.4 TB/s on others (1 GiB launches, which `zo_tune_placement` picks on slow memory, reach
+about 6.0 TB/s on either).  Allocations made while earlier ones are still held land on other
 memory, so trying a few is enough to find a fast one.
 
 `relocate` keeps the caller's buffer, allocates up to `tries` more buffers of its size while
@@ -16,8 +16,8 @@ from __future__ import annotations
 
 import torch
 
-# Below this size the placement spread is not seen (and 512 MiB slices do not apply).
-MIN_BYTES = 1 << 30
+# Below this size the placement spread is not seen (and 1 GiB slices do not apply).
+MIN_BYTES = 2 << 30
 
 
 def _rate(r: dict) -> float:
@@ -29,7 +29,7 @@ def relocate(ctx, buf: torch.Tensor, tries: int = 3, headroom_bytes: int = 8 << 
     """Return (buffer, report): `buf` itself, or a same-shaped tensor on faster memory holding
     a copy of its contents.
 
-    A placement counts as fast once one launch per pass beats 512 MiB slices by
+    A placement counts as fast once one launch per pass beats 1 GiB slices by
     `fast_ratio`; the search stops there, after `tries` extra allocations, or when the
     device has less than the buffer's size plus `headroom_bytes` free.  A candidate replaces
     the original only if it is `min_gain` times faster.  The context's pass form is left set

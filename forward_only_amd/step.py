@@ -91,14 +91,16 @@ def spsa_step(ctx, theta: torch.Tensor, *, step: int, npert: int, eps: float, et
 
 def spsa_step_fused(ctx, theta: torch.Tensor, *, step: int, npert: int, eps: float, eta: float,
                     delta: float, loss_at, offset: int = 0, bits=None,
-                    buffers: dict | None = None, loss_pair_at=None) -> dict:
+                    buffers: dict | None = None, loss_pair_at=None,
+                    loss_probes_at=None) -> dict:
     """One step whose forward applies each probe while reading the parameters.
 
     loss_at(probe, alpha, row, out) writes the loss at theta + alpha * z_probe (probe None:
     the clean loss) into `out`; theta itself is only written by the update.  Used with
     zo_mlp_loss_perturbed: no perturb or restore pass over the parameters at all.  With
     loss_pair_at(probe, alpha, row, out_plus, out_minus) (zo_mlp_loss_pair) each probe's two
-    losses come from one call.
+    losses come from one call; with loss_probes_at(probe0, n, alpha, rows, out_plus,
+    out_minus) (zo_mlp_loss_probes) all probes' losses come from one call.
     """
     a = applied_eps(eps)
     b = buffers if buffers is not None else {}
@@ -107,7 +109,9 @@ def spsa_step_fused(ctx, theta: torch.Tensor, *, step: int, npert: int, eps: flo
     Lp = b.get("Lp") if b.get("Lp") is not None else torch.empty(npert, dtype=torch.float64, device=dev)
     Lm = b.get("Lm") if b.get("Lm") is not None else torch.empty(npert, dtype=torch.float64, device=dev)
     loss_at(None, 0.0, None, L0)
-    for i in range(npert):
+    if loss_probes_at is not None and npert > 0:
+        loss_probes_at(0, npert, +a, bits, Lp, Lm)
+    for i in range(npert if loss_probes_at is None else 0):
         row = None if bits is None else bits[i]
         if loss_pair_at is not None:
             loss_pair_at(i, +a, row, Lp[i:i + 1], Lm[i:i + 1])

@@ -279,6 +279,27 @@ zo_status zo_mlp_loss_pair(zo_ctx *ctx, const float *d_params, uint64_t offset, 
                            uint64_t workspace_bytes, double *d_loss_plus, double *d_loss_minus,
                            void *stream);
 
+/* Both losses of n_probes consecutive probes probe0 .. probe0 + n_probes - 1:
+ * d_loss_plus[i] at theta + alpha * z_{probe0+i} and d_loss_minus[i] at
+ * theta - alpha * z_{probe0+i} (device, n_probes doubles each), each equal bit for bit to
+ * zo_mlp_loss_perturbed of that probe and sign: the step's forwards of "How 1.5-SPSA Works"
+ * (n_pert probes, two losses each) with up to eight probes per launch sequence, so that every
+ * operand of X and W1 loaded feeds up to sixteen accumulators of the MFMA GEMM.  d_bits: NULL
+ * (regenerate) or n_probes packed rows over the parameters, row i = probe probe0 + i
+ * (zo_bits_stride(params) bytes apart, 16-byte aligned).  d_workspace: device, 8-byte aligned,
+ * at least zo_mlp_probes_workspace_bytes(batch, d_in, d_hid, d_out, n_probes) bytes.  Other
+ * arguments and limits as zo_mlp_loss_perturbed.  n_probes == 0 is an empty call.
+ * Errors (ZO_EINVAL): as zo_mlp_loss_pair, a workspace below that size, probe indices past
+ * 2^32 - 1, misaligned d_bits. */
+uint64_t zo_mlp_probes_workspace_bytes(uint32_t batch, uint32_t d_in, uint32_t d_hid,
+                                       uint32_t d_out, uint32_t n_probes);
+zo_status zo_mlp_loss_probes(zo_ctx *ctx, const float *d_params, uint64_t offset, uint32_t step,
+                             uint32_t probe0, uint32_t n_probes, float alpha,
+                             const uint8_t *d_bits, const float *d_X, const int64_t *d_labels,
+                             uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out,
+                             void *d_workspace, uint64_t workspace_bytes, double *d_loss_plus,
+                             double *d_loss_minus, void *stream);
+
 /* zo_mlp_loss_pair for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the same kernels and the
  * same results, bit for bit, but the partial logits and row losses live in a static device
@@ -311,13 +332,13 @@ zo_status zo_stream_rmw(zo_ctx *ctx, void *d_buf, uint64_t bytes, uint32_t mask,
 /* Placement of a large parameter buffer, a property of MI355X's HBM rather than of the
  * method (the callers are those who stream a buffer in place many times, as every pass of
  * a step does): the bandwidth one launch reaches over a large buffer depends on where the
- * allocation's physical memory lies -- on some placements a launch whose waves spread over
- * the whole buffer holds writes well below what the memory allows -- while a pass issued
- * as consecutive launches over 512 MiB slices (every wave in flight inside one slice) runs
+ * allocation's physical memory lies -- on some placements a launch whose eight XCD streams
+ * lie far apart in the buffer runs well below what the memory allows -- while a pass issued
+ * as consecutive launches over 1 GiB slices (every wave in flight inside one slice) runs
  * at nearly the same rate on every placement.  zo_tune_placement times both forms on the
  * caller's buffer (a read and write-back of every word, contents unchanged; synchronizes
  * `stream`), keeps the faster in the context, and reports both (GB/s of in-place traffic;
- * the sliced figure is 0 for buffers under 1 GiB, which always use one launch).  From then
+ * the sliced figure is 0 for buffers under 2 GiB, which always use one launch).  From then
  * on zo_perturb, zo_perturb2 and zo_stream_rmw on this context issue their passes in that
  * form; results do not depend on it.  zo_set_slice_bytes sets the form directly (0: one
  * launch per pass; otherwise a multiple of 1 MiB), zo_get_slice_bytes reads it.

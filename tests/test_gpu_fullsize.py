@@ -232,16 +232,17 @@ def test_opt30b_restore_update_equals_two_calls_everywhere():
 
 
 def test_opt30b_passes_in_slices():
-    """The bench's calls with the passes issued per 512 MiB slice (the form zo_tune_placement
+    """The bench's calls with the passes issued per 1 GiB slice (the form zo_tune_placement
     picks on slow placements), with windows straddling slice boundaries."""
     cfg = CONFIGS["opt30b"]
     t = torch.empty(cfg.M, dtype=torch.bfloat16, device="cuda")
     gen.device_normal_(t, cfg.theta_std, cfg.seed)
-    per = (512 << 20) // 2                                  # params per slice
+    per = (1 << 30) // 2                                    # params per slice
     extra = [per - WIN // 2, 17 * per - WIN // 2, (cfg.M // per) * per - WIN // 2]
+    assert 17 * per < cfg.M
     assert all(x % 128 == 0 for x in extra)
     n = _run_and_check(t, cfg.M, "bf16", cfg.seed, cfg.npert, cfg.eps, 1.0, "opt30b sliced",
-                       slice_bytes=512 << 20, extra_starts=extra)
+                       slice_bytes=1 << 30, extra_starts=extra)
     assert n >= N_RANDOM
     del t
     torch.cuda.empty_cache()

@@ -110,6 +110,55 @@ def test_pair_equals_two_fused_calls(ctx, shape, mode):
     assert np.array_equal(t.cpu().numpy(), theta)
 
 
+@pytest.mark.parametrize("shape", [(16, 16, 16, 2), (32, 48, 64, 3), (48, 144, 128, 16),
+                                   (128, 768, 3072, 2)])
+@pytest.mark.parametrize("mode", ["regen", "bits"])
+@pytest.mark.parametrize("nprobes", [1, 3, 8, 13])
+def test_probes_equal_pairs(ctx, shape, mode, nprobes):
+    """zo_mlp_loss_probes gives, for every probe of the batch, exactly the losses of
+    zo_mlp_loss_pair (13 probes run as launches of 8, 4 and 1); parameters untouched."""
+    batch, d_in, d_hid, d_out = shape
+    theta, X, y = _problem(*shape, seed=57 + sum(shape) + nprobes)
+    t, x, yl = _dev(theta, X, y)
+    M = theta.size
+    probe0, step, alpha = 5, 6, 1e-3
+    rows = zo.zo_gen_probes(ctx, step, probe0, nprobes, 0, M) if mode == "bits" else None
+    lp, lm = zo.zo_mlp_loss_probes(ctx, t, 0, step, probe0, nprobes, alpha, x, yl, d_hid, d_out,
+                                   bits=rows)
+    gp, gm = lp.cpu().numpy(), lm.cpu().numpy()
+    for i in range(nprobes):
+        sp, sm = zo.zo_mlp_loss_pair(ctx, t, 0, step, probe0 + i, alpha, x, yl, d_hid, d_out,
+                                     bits=None if rows is None else rows[i])
+        assert (gp[i], gm[i]) == (sp.item(), sm.item()), (i, gp[i], gm[i], sp.item(), sm.item())
+    assert len(set(gp.tolist())) == nprobes                 # every probe its own loss
+    assert np.array_equal(t.cpu().numpy(), theta)
+
+
+def test_probes_argument_checks(ctx):
+    theta, X, y = _problem(16, 16, 16, 2, seed=1)
+    t, x, yl = _dev(theta, X, y)
+    L = zo._lib.lib()
+    need = zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 5)
+    eight = zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 8)
+    assert zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 100) == eight   # 8 per launch
+    assert need * 8 == eight * 5
+    assert zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 1) == zo.zo_mlp_workspace_bytes(16, 16, 16, 2)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = torch.empty(10, dtype=torch.float64, device="cuda")
+    args = lambda n, minus, wbytes=need, probe0=0: L.zo_mlp_loss_probes(  # noqa: E731
+        ctx.handle, t.data_ptr(), 0, 0, probe0, n, 1e-3, None, x.data_ptr(), yl.data_ptr(), 16,
+        16, 16, 2, ws.data_ptr(), wbytes, out.data_ptr(), minus, None)
+    assert args(5, None) == zo.ZO_EINVAL                                  # no -alpha outputs
+    assert args(5, out.data_ptr() + 40, wbytes=need - 8) == zo.ZO_EINVAL  # workspace
+    assert args(5, out.data_ptr() + 40, probe0=2 ** 32 - 3) == zo.ZO_EINVAL  # probe wraps
+    assert args(0, None) == zo.ZO_OK                                      # empty
+    assert args(5, out.data_ptr() + 40) == zo.ZO_OK
+    torch.cuda.synchronize()
+    with pytest.raises(ValueError):
+        zo.zo_mlp_loss_probes(ctx, t, 0, 0, 0, 5, 1e-3, x, yl, 16, 2,
+                              bits=zo.zo_gen_probes(ctx, 0, 0, 4, 0, theta.size))  # 4 rows for 5
+
+
 def test_pair_argument_checks(ctx):
     theta, X, y = _problem(16, 16, 16, 2, seed=1)
     t, x, yl = _dev(theta, X, y)
@@ -144,8 +193,9 @@ def test_mlp_argument_checks(ctx):
 
 
 def test_pair_step_equals_single_call_step():
-    """A whole MLP-workload step with paired forwards equals the step with single fused
-    forwards bit for bit: losses, weights and the updated parameters."""
+    """A whole MLP-workload step with paired forwards, and one with all probes in one batched
+    call, equal the step with single fused forwards bit for bit: losses, weights and the
+    updated parameters."""
     cfg = CONFIGS["mlp"]
     e = cfg.extra
     npert, step = 32, 3
@@ -153,11 +203,12 @@ def test_pair_step_equals_single_call_step():
     X, y = gen.mlp_data(cfg)
     x, yl = to_dev_f32(X), torch.from_numpy(y).cuda()
     results = []
-    for paired in (False, True):
+    for form in ("single", "paired", "batched"):
         local = zo.zo_init(cfg.seed)
         t = to_dev_f32(theta)
-        ws = torch.empty(zo.zo_mlp_workspace_bytes(e["batch"], e["d_in"], e["d_hid"],
-                                                   e["d_out"]), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(zo.zo_mlp_probes_workspace_bytes(e["batch"], e["d_in"], e["d_hid"],
+                                                          e["d_out"], npert), dtype=torch.uint8,
+                         device="cuda")
 
         def loss_at(probe, alpha, row, out):
             if probe is None:
@@ -170,14 +221,20 @@ def test_pair_step_equals_single_call_step():
             zo.zo_mlp_loss_pair(local, t, 0, step, probe, alpha, x, yl, e["d_hid"], e["d_out"],
                                 bits=row, workspace=ws, out_plus=op, out_minus=om)
 
+        def probes_at(probe0, n, alpha, rows, op, om):
+            zo.zo_mlp_loss_probes(local, t, 0, step, probe0, n, alpha, x, yl, e["d_hid"],
+                                  e["d_out"], bits=rows, workspace=ws, out_plus=op, out_minus=om)
+
         out = spsa_step_fused(local, t, step=step, npert=npert, eps=cfg.eps, eta=cfg.eta,
                               delta=cfg.delta, loss_at=loss_at,
-                              loss_pair_at=pair_at if paired else None)
+                              loss_pair_at=pair_at if form == "paired" else None,
+                              loss_probes_at=probes_at if form == "batched" else None)
         results.append((out["Lp"].cpu().numpy(), out["Lm"].cpu().numpy(),
                         out["c"].cpu().numpy(), t.cpu().numpy()))
         local.close()
-    for a, b in zip(*results):
-        assert np.array_equal(a, b)
+    for other in results[1:]:
+        for a, b in zip(results[0], other):
+            assert np.array_equal(a, b)
 
 
 @pytest.mark.parametrize("mode", ["bits", "regen"])
@@ -190,7 +247,8 @@ def test_mlp_config_fused_step(ctx, mode):
     smallest curvature |h_i| of this workload's 64 probes is ~10 against a loss-difference
     term of ~0.3); theta within the update tolerance plus eta * sum of those bounds; the
     GPU's parameters are untouched by the 64 x 2 perturbed forwards (only the update moves
-    them)."""
+    them).  The GPU side runs the benchmark's calls: the clean loss and one batched call for
+    all 64 probes' losses."""
     cfg = CONFIGS["mlp"]
     e = cfg.extra
     npert, step = cfg.npert, 0
@@ -198,7 +256,8 @@ def test_mlp_config_fused_step(ctx, mode):
     theta, _ = gen.theta_and_a(cfg)
     X, y = gen.mlp_data(cfg)
     t, x, yl = to_dev_f32(theta), to_dev_f32(X), torch.from_numpy(y).cuda()
-    ws = torch.empty(zo.zo_mlp_workspace_bytes(e["batch"], e["d_in"], e["d_hid"], e["d_out"]),
+    ws = torch.empty(zo.zo_mlp_probes_workspace_bytes(e["batch"], e["d_in"], e["d_hid"],
+                                                      e["d_out"], npert),
                      dtype=torch.uint8, device="cuda")
 
     def loss_at(probe, alpha, row, out):
@@ -208,9 +267,13 @@ def test_mlp_config_fused_step(ctx, mode):
             zo.zo_mlp_loss_perturbed(local, t, 0, step, probe, alpha, x, yl, e["d_hid"],
                                      e["d_out"], bits=row, workspace=ws, out=out)
 
+    def probes_at(probe0, n, alpha, rows, op, om):
+        zo.zo_mlp_loss_probes(local, t, 0, step, probe0, n, alpha, x, yl, e["d_hid"],
+                              e["d_out"], bits=rows, workspace=ws, out_plus=op, out_minus=om)
+
     bits = zo.zo_gen_probes(local, step, 0, npert, 0, cfg.M) if mode == "bits" else None
     out = spsa_step_fused(local, t, step=step, npert=npert, eps=cfg.eps, eta=cfg.eta,
-                          delta=cfg.delta, loss_at=loss_at, bits=bits)
+                          delta=cfg.delta, loss_at=loss_at, bits=bits, loss_probes_at=probes_at)
     a = float(np.float32(cfg.eps))
     lossf = lambda p: oracle.mlp_loss(p, X, y, e["d_hid"], e["d_out"])  # noqa: E731
     L0 = lossf(theta)

@@ -11,7 +11,7 @@ from forward_only_amd import placement
 
 class Script:
     """zo_tune_placement stand-in: the n-th buffer it sees gets the n-th scripted rate pair
-    (one launch, 512 MiB slices); a buffer seen again gets its earlier answer."""
+    (one launch, 1 GiB slices); a buffer seen again gets its earlier answer."""
 
     def __init__(self, rates):
         self.rates = list(rates)
@@ -22,7 +22,7 @@ class Script:
         key = id(buf)
         if key not in self.seen:
             w, s = self.rates[len(self.seen)]
-            self.seen[key] = {"slice_bytes": 0 if w >= s else 512 << 20, "gbps_whole": float(w),
+            self.seen[key] = {"slice_bytes": 0 if w >= s else 1 << 30, "gbps_whole": float(w),
                               "gbps_sliced": float(s)}
         self.calls.append(key)
         return dict(self.seen[key])
