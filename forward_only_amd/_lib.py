@@ -1,4 +1,5 @@
-"""ctypes loader of libzo.so: symbol signatures and status codes of include/zo.h.
+"""ctypes loader of libzo.so: symbol signatures and status codes of include/zo.h and
+include/zo_placement.h.
 
 Loading builds the library in-tree with hipcc only when no built library is present, and
 fails loudly otherwise: there is no fallback implementation of any call.
@@ -23,13 +24,13 @@ _u8p = ctypes.POINTER(ctypes.c_uint8)
 _u32, _u64, _f32, _f64, _int = (ctypes.c_uint32, ctypes.c_uint64, ctypes.c_float,
                                 ctypes.c_double, ctypes.c_int)
 
-# name -> (restype, argtypes), in the order of include/zo.h
+# name -> (restype, argtypes), in the order of include/zo.h, then include/zo_placement.h
 SIGNATURES = {
     "zo_init": (_int, [_u64, ctypes.POINTER(_vp)]),
     "zo_destroy": (_int, [_vp]),
     "zo_get_seed": (_u64, [_vp]),
     "zo_strerror": (ctypes.c_char_p, [_int]),
-    "zo_bits_stride": (_u64, [_u64]),
+    "zo_bits_stride": (ctypes.c_size_t, [_u64]),
     "zo_gen_probes": (_int, [_vp, _u32, _u32, _u32, _u64, _u64, _vp, _vp]),
     "zo_perturb": (_int, [_vp, _vp, _int, _u64, _u64, _u32, _u32, _f32, _vp, _vp]),
     "zo_perturb2": (_int, [_vp, _vp, _int, _u64, _u64, _u32, _u32, _f32, _u32, _f32, _vp, _vp,

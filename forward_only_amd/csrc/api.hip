@@ -4,6 +4,7 @@
 #include <new>
 
 #include "../../include/zo.h"
+#include "../../include/zo_placement.h"
 #include "zo_launch.hpp"
 
 static_assert(ZO_MAX_NPERT == zo::kMaxNpert, "one probe-count limit");
@@ -98,7 +99,7 @@ const char *zo_strerror(zo_status s)
     return "unknown status";
 }
 
-uint64_t zo_bits_stride(uint64_t n) { return ((n + 127u) / 128u) * 16u; }
+size_t zo_bits_stride(uint64_t n) { return (size_t)(((n + 127u) / 128u) * 16u); }
 
 zo_status zo_init(uint64_t seed, zo_ctx **out)
 {

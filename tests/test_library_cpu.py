@@ -1,6 +1,7 @@
 """Host-only checks of libzo.so: it loads without a GPU, exports every entry point that
-include/zo.h declares, and rejects bad arguments before touching the device."""
+include/*.h declares, and rejects bad arguments before touching the device."""
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -14,14 +15,17 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def declared_functions():
-    src = open(os.path.join(ROOT, "include", "zo.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(zo_[a-z_]+)\s*\(", src)))
+    names = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(zo_[a-z_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for must in ("zo_init", "zo_gen_probes", "zo_perturb", "zo_probe_weights", "zo_update"):
+    for must in ("zo_init", "zo_gen_probes", "zo_perturb", "zo_probe_weights", "zo_update",
+                 "zo_tune_placement"):
         assert must in names
 
 
