@@ -43,10 +43,12 @@
  *    streaming diagnostic, the per-buffer choice between one launch and slices per pass)
  *    are declared in zo_placement.h.
  *  - Launch shapes: ZO_UPDATE_WG_PER_CU (default 16) overrides the workgroups per CU of the
- *    update kernel, read once per process, accepted in [1, 64]; ZO_UPDATE_GENERIC=1 makes
- *    the update use its general kernel at every probe count.  Results do not depend on
- *    either.  The passes over the parameters (zo_perturb, zo_perturb2, zo_stream_rmw) run
- *    one chunk per wave in a non-persistent grid.
+ *    update kernel, accepted in [1, 64]; ZO_UPDATE_GENERIC=1 makes the update use its
+ *    general kernel at every probe count; ZO_MLP_PROBES_PER_WAVE (default 2; 1, 2, 4 or 8)
+ *    sets the probes per wave of zo_mlp_loss_probes.  Each is read once per process, and
+ *    results do not depend on them.  The passes over the parameters (zo_perturb,
+ *    zo_perturb2, zo_stream_rmw) and the plane generator run one chunk per wave in a
+ *    non-persistent grid.
  */
 #ifndef ZO_H
 #define ZO_H
@@ -286,8 +288,9 @@ zo_status zo_mlp_loss_pair(zo_ctx *ctx, const float *d_params, uint64_t offset, 
  * d_loss_plus[i] at theta + alpha * z_{probe0+i} and d_loss_minus[i] at
  * theta - alpha * z_{probe0+i} (device, n_probes doubles each), each equal bit for bit to
  * zo_mlp_loss_perturbed of that probe and sign: the step's forwards of "How 1.5-SPSA Works"
- * (n_pert probes, two losses each) with up to eight probes per launch sequence, so that every
- * operand of X and W1 loaded feeds up to sixteen accumulators of the MFMA GEMM.  d_bits: NULL
+ * (n_pert probes, two losses each) as launch sequences of up to sixteen probes, each wave of
+ * the MFMA GEMM running two probes (ZO_MLP_PROBES_PER_WAVE: 1, 2, 4 or 8) so that every X
+ * and W1 operand it loads feeds both signs of each.  d_bits: NULL
  * (regenerate) or n_probes packed rows over the parameters, row i = probe probe0 + i
  * (zo_bits_stride(params) bytes apart, 16-byte aligned).  d_workspace: device, 8-byte aligned,
  * at least zo_mlp_probes_workspace_bytes(batch, d_in, d_hid, d_out, n_probes) bytes.  Other
