@@ -1,7 +1,7 @@
 // k_diag.hip -- diagnostic streaming kernel: every 16-byte word of a buffer is read, xored
-// with a mask and written back, in the perturb kernel's order (eight contiguous chunk
-// ranges, one per XCD, one 16 KiB chunk per wave, non-persistent, non-temporal loads and
-// stores).  With
+// with a mask and written back, in the perturb kernel's order and form (eight contiguous
+// chunk ranges, one per XCD, one 8 KiB chunk per single-wave workgroup, non-persistent,
+// non-temporal loads and stores).  With
 // mask 0 the buffer is unchanged, and timing the call on a parameter buffer gives the
 // in-place read-modify-write ceiling of the physical memory that buffer occupies.  The mask
 // is a run-time argument on purpose: a store of the value just loaded from the same address
@@ -13,14 +13,14 @@ namespace zo {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kDiagLoads = 16;                         // dwordx4 per lane per chunk
-constexpr uint64_t kDiagChunk16 = kDiagLoads * kWave;  // 16-byte words per chunk (16 KiB)
+constexpr int kDiagLoads = 8;                          // dwordx4 per lane per chunk
+constexpr uint64_t kDiagChunk16 = kDiagLoads * kWave;  // 16-byte words per chunk (8 KiB)
 
-__global__ __launch_bounds__(256) void k_stream_rmw(u32x4_t *__restrict__ p, uint64_t nchunks,
-                                                    uint32_t mask)
+__global__ __launch_bounds__(kWave) void k_stream_rmw(u32x4_t *__restrict__ p, uint64_t nchunks,
+                                                      uint32_t mask)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const uint64_t ch = xcd_range_chunk<4>(nchunks);
+    const uint64_t ch = xcd_range_chunk<1>(nchunks);
     if (ch < nchunks) {
         u32x4_t *b = p + ch * kDiagChunk16 + lane;
         u32x4_t v[kDiagLoads];
@@ -47,8 +47,8 @@ static hipError_t stream_rmw_range(void *buf, uint64_t bytes, uint32_t mask, int
     u32x4_t *p = static_cast<u32x4_t *>(buf);
     (void)num_cus;
     if (nchunks)
-        hipLaunchKernelGGL(k_stream_rmw, dim3(xcd_range_grid(nchunks, 4)), dim3(256), 0, stream,
-                           p, nchunks, mask);
+        hipLaunchKernelGGL(k_stream_rmw, dim3(xcd_range_grid(nchunks, 1)), dim3(kWave), 0,
+                           stream, p, nchunks, mask);
     const uint64_t start = nchunks * kDiagChunk16;
     if (start < nwords) {
         const uint32_t grid = (uint32_t)((nwords - start + 255) / 256);

@@ -25,11 +25,14 @@
 // operand is loaded once and feeds two accumulators (the second sees theta_j + (bit ?
 // -alpha : alpha)), each with exactly the MFMA sequence of a single fused launch, so both
 // losses equal the single fused results bit for bit.
-// Several probes (kNP > 1): probes probe .. probe+kNP-1 in one launch sequence, both signs
-// each, so every X and W1 operand loaded feeds 2*kNP accumulators -- the forward's loads are
-// shared by all the step's probes of the launch, while each accumulator still runs exactly
-// the single fused launch's MFMA sequence.  Slot s = 2i + sign (i < kNP; sign 0: +alpha,
-// 1: -alpha) writes its partial logits, row losses and loss to its own places.
+// Several probes (kNP > 1): each wave runs kNP probes, both signs each, so every X and W1
+// operand it loads feeds 2*kNP accumulators, while each accumulator still runs exactly the
+// single fused launch's MFMA sequence.  A launch covers kNP * gridDim.y probes: blockIdx.y
+// picks the wave's group of kNP probes, so the tiles' waves come gridDim.y times over and
+// each SIMD gets several to interleave (one 8-probe wave per tile left 1.5 waves per SIMD,
+// which serialised every wave's sign arithmetic with its own MFMAs).  Slot s = 2i + sign
+// (probe i of the launch; sign 0: +alpha, 1: -alpha) writes its partial logits, row losses
+// and loss to its own places.
 #include <stdlib.h>
 
 #include "zo_device.hpp"
@@ -98,6 +101,11 @@ __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
     if ((total & 7u) == 0) t = (t & 7u) * (total >> 3) + (t >> 3);  // XCD-contiguous tiles
     const uint32_t m0 = (t % m_tiles) * 16, nt = t / m_tiles, n0 = nt * 16;
     const uint32_t li = lane & 15u, kq = lane >> 4;
+    // this wave's probes: kNP of them from pa.probe + blockIdx.y * kNP (slots likewise)
+    if constexpr (kNP > 0) {
+        pa.probe += blockIdx.y * (uint32_t)kNP;
+        if (pa.bits) pa.bits += (uint64_t)blockIdx.y * kNP * pa.bits_stride;
+    }
 
     const float *xrow = X + (uint64_t)(m0 + li) * d_in + 4u * kq;
     const uint64_t wrow = (uint64_t)(n0 + li) * d_in + 4u * kq;   // flat index in params
@@ -222,7 +230,8 @@ __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
     // epilogue: column n = n0 + li, rows m0 + 4*kq + r
     const uint64_t b1_at = (uint64_t)d_hid * d_in;
     const uint64_t w2_at = b1_at + d_hid;
-    const uint64_t pset = (uint64_t)n_tiles * batch * d_out;   // one sign's partial logits
+    const uint64_t pset = (uint64_t)n_tiles * batch * d_out;   // one slot's partial logits
+    partial += (uint64_t)blockIdx.y * (kNP > 0 ? kNP * (kPair ? 2 : 1) : 1) * pset;
     const uint32_t n = n0 + li;
 #pragma unroll
     for (int slot = 0; slot < kNS; ++slot) {
@@ -312,18 +321,19 @@ __global__ __launch_bounds__(256) void k_mlp_mean(const double *__restrict__ row
     if (threadIdx.x == 0) *out = red[0] / (double)batch;
 }
 
+// One launch sequence: tiles (kNP probes per wave, `groups` probe groups), row losses, means.
 template <int kNP, bool kPair>
 static void launch_chain(const float *params, const float *X, const int64_t *labels,
                          uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out,
                          double *partial, double *out, double *out2, const PertArgs &pa,
-                         hipStream_t stream)
+                         hipStream_t stream, uint32_t groups = 1)
 {
     const uint32_t tiles = (batch / 16) * (d_hid / 16);
     const uint32_t per = kPair ? 2u : 1u;
-    const uint32_t nslot = kNP > 0 ? (uint32_t)kNP * per : 1u;
+    const uint32_t nslot = kNP > 0 ? (uint32_t)kNP * per * groups : 1u;
     double *rowloss = partial + (uint64_t)nslot * (d_hid / 16) * batch * d_out;
-    hipLaunchKernelGGL((k_mlp_tiles<kNP, kPair>), dim3(tiles), dim3(64), 0, stream, X, params,
-                       batch, d_in, d_hid, d_out, partial, pa);
+    hipLaunchKernelGGL((k_mlp_tiles<kNP, kPair>), dim3(tiles, groups), dim3(64), 0, stream, X,
+                       params, batch, d_in, d_hid, d_out, partial, pa);
     hipLaunchKernelGGL(k_mlp_rows<(kNP > 0)>, dim3((batch + 3) / 4, nslot), dim3(256), 0, stream,
                        partial, params, labels, batch, d_in, d_hid, d_out, rowloss, pa, per);
     hipLaunchKernelGGL(k_mlp_mean, dim3(nslot), dim3(256), 0, stream, rowloss, batch, out, out2,
@@ -369,6 +379,18 @@ hipError_t launch_mlp_loss(const float *params, const float *X, const int64_t *l
     return hipGetLastError();
 }
 
+// Probes per wave of the batched MLP forward, from the environment (read once per process):
+// 1, 2, 4 or 8; anything else keeps the default.  Results do not depend on it.
+static uint32_t mlp_probes_per_wave()
+{
+    static const uint32_t v = [] {
+        const char *s = getenv("ZO_MLP_PROBES_PER_WAVE");
+        const int x = (s && *s) ? atoi(s) : 0;
+        return (x == 1 || x == 2 || x == 4 || x == 8) ? (uint32_t)x : kMlpProbesPerWave;
+    }();
+    return v;
+}
+
 hipError_t launch_mlp_loss_probes(const float *params, const float *X, const int64_t *labels,
                                   uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out,
                                   double *partial, const MlpPerturb &pert, uint32_t nprobes,
@@ -376,24 +398,24 @@ hipError_t launch_mlp_loss_probes(const float *params, const float *X, const int
                                   hipStream_t stream)
 {
     const uint64_t nparams = mlp_params(d_in, d_hid, d_out);
-    // launches of 8 probes, then 4, 2, 1 for the rest; each reuses the workspace from its
-    // start (the launches run in order on the stream)
+    const uint32_t pw = mlp_probes_per_wave();
+    // launch sequences of 16 probes, then 8, 4, 2, 1 for the rest, each with min(pw, size)
+    // probes per wave; each reuses the workspace from its start (they run in stream order)
     for (uint32_t done = 0; done < nprobes;) {
         const uint32_t left = nprobes - done;
-        const uint32_t k = left >= kMlpProbesPerLaunch ? kMlpProbesPerLaunch
-                           : left >= 4             ? 4u
-                           : left >= 2             ? 2u
-                                                   : 1u;
+        uint32_t k = kMlpProbesPerLaunch;
+        while (k > left) k >>= 1;
+        const uint32_t w = pw < k ? pw : k;
         MlpPerturb p = pert;
         p.probe = pert.probe + done;
         if (pert.bits) p.bits = pert.bits + (uint64_t)done * ((nparams + 127) / 128 * 16);
         const PertArgs pa = pert_args(&p, key, nparams);
         double *op = out_plus + done, *om = out_minus + done;
-        switch (k) {
-        case 8: launch_chain<8, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream); break;
-        case 4: launch_chain<4, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream); break;
-        case 2: launch_chain<2, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream); break;
-        default: launch_chain<1, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream); break;
+        switch (w) {
+        case 8: launch_chain<8, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 8); break;
+        case 4: launch_chain<4, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 4); break;
+        case 2: launch_chain<2, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 2); break;
+        default: launch_chain<1, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k); break;
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -4,26 +4,26 @@
 // Works" on "Stanford's 1.5-SPSA Trains OPT-30B Without Backpropagation").
 //
 // Layout and mapping (gfx950, wave64):
-//  * A wave owns one chunk of 64 Philox blocks = 8192 consecutive params (16 KiB of bf16,
-//    32 KiB of fp32) and exits.  The chunks are split into eight contiguous ranges, one per
-//    XCD: workgroups are dispatched to the XCDs round-robin, so workgroup b (on XCD b % 8)
-//    takes the next chunks of range b % 8 in dispatch order.  Each XCD then streams
-//    through its own eighth of the buffer (its L2 and address translation see one compact
-//    window instead of every XCD touching every window), and since no wave loops, the
-//    waves in flight never drift apart: on a 60 GB buffer this non-persistent form ran at
-//    6.33-6.38 TB/s in place where a persistent grid-stride walk of the same ranges ran at
-//    6.16-6.24 (fast physical placements) and 5.79-5.92 against 5.2 (slow ones).  The
-//    split is a plain partition of the chunks, so results do not depend on where
-//    workgroups actually run.
-//  * Each lane issues its 16 (bf16) or 32 (fp32) global_load_dwordx4 first; load k of
-//    lane L covers 16 bytes at chunk + 1 KiB*k + 16*L, so every load instruction moves
-//    one contiguous KiB per wave.
-//  * While those loads are in flight, lane L computes Philox for block L of the chunk
-//    (or reads its 16 bytes of a stored plane) and writes the 16 bytes to a 1 KiB LDS
-//    slice private to the wave.  The chunk's sign bits are then a linear 1 KiB array:
-//    bf16 load k of lane L needs byte 64k + L, fp32 load k needs the nibble
-//    (L & 1) of byte 32k + L/2 -- one ds_read_u8 each, with the load index folded
-//    into the instruction's offset.
+//  * A workgroup is one wave; it owns one 8 KiB chunk (4096 bf16 or 2048 fp32 consecutive
+//    params: 32 or 16 Philox blocks) and exits.  The chunks are split into eight contiguous
+//    ranges, one per XCD: workgroups are dispatched to the XCDs round-robin, so workgroup b
+//    (on XCD b % 8) takes the next chunk of range b % 8 in dispatch order.  Each XCD then
+//    streams through its own eighth of the buffer (its L2 and address translation see one
+//    compact window instead of every XCD touching every window), and since no wave loops,
+//    the waves in flight never drift apart.  Measured on 60 GB buffers (in-place streaming
+//    of the same shape): a persistent grid-stride walk of the same ranges ran at 6.16-6.24
+//    TB/s on fast physical placements and 5.2 on slow ones; non-persistent 16 KiB chunks in
+//    four-wave workgroups 6.34-6.39 and 5.86-5.92; 8 KiB single-wave workgroups, this form,
+//    6.42-6.47 and 6.00-6.07.  The split is a plain partition of the chunks, so results do
+//    not depend on where workgroups actually run.
+//  * Each lane issues its 8 global_load_dwordx4 first; load k of lane L covers 16 bytes at
+//    chunk + 1 KiB*k + 16*L, so every load instruction moves one contiguous KiB per wave.
+//  * While those loads are in flight, lane L < 32 (bf16; < 16 for fp32) computes Philox for
+//    block L of the chunk (or reads its 16 bytes of a stored plane) and writes the 16 bytes
+//    to an LDS slice private to the wave.  The chunk's sign bits are then a linear array:
+//    bf16 load k of lane L needs byte 64k + L, fp32 load k needs the nibble (L & 1) of byte
+//    32k + L/2 -- one ds_read_u8 each, with the load index folded into the instruction's
+//    offset.
 //  * Apply: flip alpha's sign bit when the param's bit is clear, one fp32 add, and for
 //    bf16 one v_cvt_pk_bf16_f32 (round to nearest even) per pair; store dwordx4.
 //  * The ragged end (fewer than 8192 params) goes to a small per-element kernel.
@@ -39,13 +39,18 @@
 
 namespace zo {
 
-constexpr int kChunkParams = kWave * kBlockParams;  // 8192
-constexpr int kWavesPerWG = 4;
+// Params per chunk (one wave's 8 KiB): 4096 bf16 or 2048 fp32.
+template <bool kBF16>
+constexpr int chunk_params() { return kBF16 ? 4096 : 2048; }
+constexpr int kWavesPerWG = 1;
+static_assert(kPerturbChunkParams % chunk_params<true>() == 0 &&
+                  kPerturbChunkParams % chunk_params<false>() == 0,
+              "slices are whole chunks of either type");
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 template <bool kBF16, bool kBits, bool kTwo>
-__global__ __launch_bounds__(256) void k_perturb_chunks(u32x4_t *__restrict__ theta,
+__global__ __launch_bounds__(kWave * kWavesPerWG) void k_perturb_chunks(u32x4_t *__restrict__ theta,
                                                         uint64_t nchunks, uint64_t blk0,
                                                         uint32_t step, uint32_t probe_a,
                                                         uint32_t probe_b, uint32_t k0,
@@ -54,10 +59,12 @@ __global__ __launch_bounds__(256) void k_perturb_chunks(u32x4_t *__restrict__ th
                                                         const u32x4_t *__restrict__ bits_a,
                                                         const u32x4_t *__restrict__ bits_b)
 {
+    constexpr int kChunkParams = chunk_params<kBF16>();
     constexpr int kPerLoad = kBF16 ? 8 : 4;                      // params per 16 bytes
-    constexpr int kLoads = kChunkParams / (kPerLoad * kWave);   // 16 or 32
+    constexpr int kLoads = kChunkParams / (kPerLoad * kWave);   // 8
+    constexpr int kBlocks = kChunkParams / kBlockParams;         // 32 or 16
     constexpr int kProbes = kTwo ? 2 : 1;
-    __shared__ u32x4_t xch_all[kWavesPerWG][kProbes][kWave];
+    __shared__ u32x4_t xch_all[kWavesPerWG][kProbes][kBlocks];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
@@ -72,21 +79,23 @@ __global__ __launch_bounds__(256) void k_perturb_chunks(u32x4_t *__restrict__ th
 #pragma unroll
         for (int k = 0; k < kLoads; ++k) v[k] = __builtin_nontemporal_load(base + k * kWave);
 
-        const uint64_t lb = ch * kWave + lane;  // block index local to the buffer
-        u32x4_t wa, wb;
-        if constexpr (kBits) {
-            wa = bits_a[lb];
-            if constexpr (kTwo) wb = bits_b[lb];
-        } else {
-            const U32x4 r = probe_block_bits(blk0 + lb, probe_a, step, k0, k1);
-            wa = u32x4_t{r.x, r.y, r.z, r.w};
-            if constexpr (kTwo) {
-                const U32x4 q = probe_block_bits(blk0 + lb, probe_b, step, k0, k1);
-                wb = u32x4_t{q.x, q.y, q.z, q.w};
+        if (lane < kBlocks) {
+            const uint64_t lb = ch * kBlocks + lane;  // block index local to the buffer
+            u32x4_t wa, wb;
+            if constexpr (kBits) {
+                wa = bits_a[lb];
+                if constexpr (kTwo) wb = bits_b[lb];
+            } else {
+                const U32x4 r = probe_block_bits(blk0 + lb, probe_a, step, k0, k1);
+                wa = u32x4_t{r.x, r.y, r.z, r.w};
+                if constexpr (kTwo) {
+                    const U32x4 q = probe_block_bits(blk0 + lb, probe_b, step, k0, k1);
+                    wb = u32x4_t{q.x, q.y, q.z, q.w};
+                }
             }
+            xa[lane] = wa;
+            if constexpr (kTwo) xb[lane] = wb;
         }
-        xa[lane] = wa;
-        if constexpr (kTwo) xb[lane] = wb;
         wave_lds_sync();
 
 #pragma unroll
@@ -170,13 +179,15 @@ static hipError_t perturb_range(void *theta, uint64_t n, uint64_t blk0, uint32_t
                                 uint32_t bbits, const uint8_t *bits_a, const uint8_t *bits_b,
                                 int num_cus, hipStream_t stream)
 {
+    constexpr uint64_t kChunkParams = chunk_params<kBF16>();
     const uint64_t nchunks = n / kChunkParams;
     (void)num_cus;
     if (nchunks) {
-        // Non-persistent: one chunk per wave, eight XCD ranges (a caller splits passes
-        // longer than kMaxChunksPerLaunch chunks into several launches).
+        // Non-persistent: one chunk per single-wave workgroup, eight XCD ranges (a caller
+        // splits passes longer than kMaxChunksPerLaunch chunks into several launches).
         const uint32_t grid = xcd_range_grid(nchunks, kWavesPerWG);
-        hipLaunchKernelGGL((k_perturb_chunks<kBF16, kBits, kTwo>), dim3(grid), dim3(256), 0,
+        hipLaunchKernelGGL((k_perturb_chunks<kBF16, kBits, kTwo>), dim3(grid),
+                           dim3(kWave * kWavesPerWG), 0,
                            stream, static_cast<u32x4_t *>(theta), nchunks, blk0, step, probe_a,
                            probe_b, key.k0, key.k1, abits, bbits,
                            reinterpret_cast<const u32x4_t *>(bits_a),
@@ -192,7 +203,7 @@ static hipError_t perturb_range(void *theta, uint64_t n, uint64_t blk0, uint32_t
     return hipGetLastError();
 }
 
-// The pass over [0, n) as one launch, or (slice > 0, a multiple of kChunkParams) as one
+// The pass over [0, n) as one launch, or (slice > 0, a multiple of kPerturbChunkParams) as one
 // launch per slice of `slice` params in order: each slice is the same pass over its own
 // range (its block index and plane bytes advanced with it), so the result is identical.
 // Separate launches keep all waves within one slice at a time; on a large buffer whose
@@ -204,7 +215,7 @@ static hipError_t perturb_impl(void *theta, uint64_t n, uint64_t blk0, uint32_t 
                                uint32_t bbits, const uint8_t *bits_a, const uint8_t *bits_b,
                                uint64_t slice, int num_cus, hipStream_t stream)
 {
-    constexpr uint64_t kMaxLaunchParams = kMaxChunksPerLaunch * kChunkParams;
+    constexpr uint64_t kMaxLaunchParams = kMaxChunksPerLaunch * chunk_params<kBF16>();
     if (slice == 0 || slice > kMaxLaunchParams) slice = kMaxLaunchParams;
     if (slice >= n)
         return perturb_range<kBF16, kBits, kTwo>(theta, n, blk0, step, probe_a, probe_b, key,

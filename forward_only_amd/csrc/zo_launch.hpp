@@ -16,14 +16,16 @@ hipError_t launch_gen_probes(Key key, uint32_t step, uint32_t probe0, uint32_t n
                              uint64_t offset, uint64_t n, uint8_t *bits, int num_cus,
                              hipStream_t stream);
 
-// Params per streaming chunk of the perturb kernel; slice lengths are multiples of it.
-constexpr uint64_t kPerturbChunkParams = 8192;
+// Slice lengths of the perturb passes are multiples of this many params (a whole number of
+// the kernel's chunks: 4096 bf16 or 2048 fp32 params, 8 KiB each).
+constexpr uint64_t kPerturbChunkParams = 4096;
 
 // Workgroups of a non-persistent XCD-range launch (xcd_range_chunk) over n chunks with
 // `waves` waves per workgroup: eight times those of the longest range (ranges differ by at
 // most one chunk, so the longest holds ceil(n / 8)).  Launches cover at most
-// kMaxChunksPerLaunch chunks, which keeps the grid below 2^31 workgroups.
-constexpr uint64_t kMaxChunksPerLaunch = (uint64_t)1 << 31;
+// kMaxChunksPerLaunch chunks, which keeps the grid below 2^31 workgroups even with one wave
+// per workgroup.
+constexpr uint64_t kMaxChunksPerLaunch = (uint64_t)1 << 30;
 inline uint32_t xcd_range_grid(uint64_t n, uint32_t waves)
 {
     return (uint32_t)(8 * (((n + 7) / 8 + waves - 1) / waves));
@@ -111,7 +113,7 @@ hipError_t launch_mlp_loss_probes(const float *params, const float *X, const int
                                   hipStream_t stream);
 
 // Diagnostic: every 16-byte word of buf (bytes % 16 == 0) <- word ^ mask, in place;
-// slice_bytes > 0 (a multiple of 16 KiB) issues it as one launch per slice of that size.
+// slice_bytes > 0 (a multiple of 8 KiB) issues it as one launch per slice of that size.
 hipError_t launch_stream_rmw(void *buf, uint64_t bytes, uint32_t mask, int num_cus,
                              hipStream_t stream, uint64_t slice_bytes = 0);
 
