@@ -9,12 +9,13 @@
 //                                count rounds of allocate / measure / free, then up to count
 //                                allocations held at once (default 59.92 GB, 6)
 //
-// Each kernel walks 16 KiB chunks per wave (16 dwordx4 per lane, one contiguous KiB per
-// instruction); the buffer is split into eight contiguous ranges, one per XCD (workgroup b
-// runs on XCD b % 8).  Two forms: persistent (each XCD's range walked grid-stride by a few
-// resident workgroups per CU, launch shapes 2-16 workgroups per CU) and non-persistent
-// (one chunk per wave, each XCD's chunks taken in dispatch order -- the order of the
-// library's passes).  Loads and stores carry the non-temporal hint (the fastest
+// The buffer is split into eight contiguous ranges, one per XCD (workgroup b runs on XCD
+// b % 8), every load and store instruction moving one contiguous KiB per wave.  Two forms:
+// persistent (16 KiB chunks, each XCD's range walked grid-stride by a few resident
+// four-wave workgroups per CU, launch shapes 2-16 workgroups per CU) and non-persistent
+// (single-wave workgroups, one chunk each, each XCD's chunks taken in dispatch order -- the
+// form of the library's passes: 8 KiB chunks, and 4 KiB for the write-only kernel as in the
+// plane generator).  Loads and stores carry the non-temporal hint (the fastest
 // setting measured for streaming here).  Every figure is bytes moved / kernel time (HIP
 // events), best over the launch shapes tried.  A large buffer's bandwidth depends on the
 // physical memory the allocation lands on (the same physical memory mapped at other
@@ -111,61 +112,68 @@ __global__ __launch_bounds__(256) void k_rmw(u32x4_t *__restrict__ p, uint64_t n
     }
 }
 
-// Non-persistent walk: the wave's chunk (one per wave, XCD ranges in dispatch order), or n.
+// Non-persistent walk (the library's passes): single-wave workgroups, one chunk of kL KiB
+// (kL dwordx4 per lane) each, XCD ranges in dispatch order.  Returns the chunk, or n.
 __device__ __forceinline__ uint64_t np_chunk(uint64_t n)
 {
     const uint64_t x = blockIdx.x & 7u;
-    const uint64_t ch = n * x / 8 + (uint64_t)(blockIdx.x >> 3) * 4 + (threadIdx.x >> 6);
+    const uint64_t ch = n * x / 8 + (blockIdx.x >> 3);
     return ch < n * (x + 1) / 8 ? ch : n;
 }
-static uint32_t np_grid(uint64_t n) { return (uint32_t)(8 * (((n + 7) / 8 + 3) / 4)); }
+static uint32_t np_grid(uint64_t n) { return (uint32_t)(8 * ((n + 7) / 8)); }
+constexpr int kNpLoads = 8;        // read, copy, in-place RMW: 8 KiB per wave (the passes)
+constexpr int kNpWriteLoads = 4;   // write: 4 KiB per wave (the plane generator)
 
-__global__ __launch_bounds__(256) void k_read_np(const u32x4_t *__restrict__ p, uint64_t n,
-                                                 uint32_t *__restrict__ sink)
+template <int kL>
+__global__ __launch_bounds__(64) void k_read_np(const u32x4_t *__restrict__ p, uint64_t n,
+                                                uint32_t *__restrict__ sink)
 {
     const uint64_t ch = np_chunk(n);
     if (ch >= n) return;
-    const u32x4_t *b = p + ch * kChunk16 + (threadIdx.x & 63);
+    const u32x4_t *b = p + ch * (kL * 64) + threadIdx.x;
     u32x4_t acc = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) acc ^= __builtin_nontemporal_load(b + k * 64);
+    for (int k = 0; k < kL; ++k) acc ^= __builtin_nontemporal_load(b + k * 64);
     if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) sink[0] = acc.x;   // keeps the loads
 }
 
-__global__ __launch_bounds__(256) void k_write_np(u32x4_t *__restrict__ p, uint64_t n)
+template <int kL>
+__global__ __launch_bounds__(64) void k_write_np(u32x4_t *__restrict__ p, uint64_t n)
 {
     const uint64_t ch = np_chunk(n);
     if (ch >= n) return;
-    u32x4_t *b = p + ch * kChunk16 + (threadIdx.x & 63);
+    u32x4_t *b = p + ch * (kL * 64) + threadIdx.x;
     const u32x4_t v = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) __builtin_nontemporal_store(v, b + k * 64);
+    for (int k = 0; k < kL; ++k) __builtin_nontemporal_store(v, b + k * 64);
 }
 
-__global__ __launch_bounds__(256) void k_copy_np(const u32x4_t *__restrict__ src,
-                                                 u32x4_t *__restrict__ dst, uint64_t n)
+template <int kL>
+__global__ __launch_bounds__(64) void k_copy_np(const u32x4_t *__restrict__ src,
+                                                u32x4_t *__restrict__ dst, uint64_t n)
 {
     const uint64_t ch = np_chunk(n);
     if (ch >= n) return;
-    const u32x4_t *s = src + ch * kChunk16 + (threadIdx.x & 63);
-    u32x4_t *d = dst + ch * kChunk16 + (threadIdx.x & 63);
-    u32x4_t v[kLoads];
+    const u32x4_t *s = src + ch * (kL * 64) + threadIdx.x;
+    u32x4_t *d = dst + ch * (kL * 64) + threadIdx.x;
+    u32x4_t v[kL];
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) v[k] = __builtin_nontemporal_load(s + k * 64);
+    for (int k = 0; k < kL; ++k) v[k] = __builtin_nontemporal_load(s + k * 64);
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) __builtin_nontemporal_store(v[k], d + k * 64);
+    for (int k = 0; k < kL; ++k) __builtin_nontemporal_store(v[k], d + k * 64);
 }
 
-__global__ __launch_bounds__(256) void k_rmw_np(u32x4_t *__restrict__ p, uint64_t n)
+template <int kL>
+__global__ __launch_bounds__(64) void k_rmw_np(u32x4_t *__restrict__ p, uint64_t n)
 {
     const uint64_t ch = np_chunk(n);
     if (ch >= n) return;
-    u32x4_t *b = p + ch * kChunk16 + (threadIdx.x & 63);
-    u32x4_t v[kLoads];
+    u32x4_t *b = p + ch * (kL * 64) + threadIdx.x;
+    u32x4_t v[kL];
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) v[k] = __builtin_nontemporal_load(b + k * 64);
+    for (int k = 0; k < kL; ++k) v[k] = __builtin_nontemporal_load(b + k * 64);
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
+    for (int k = 0; k < kL; ++k) {
         v[k] += 0x00010001u;
         __builtin_nontemporal_store(v[k], b + k * 64);
     }
@@ -193,7 +201,7 @@ static float time_ms(F launch, int iters)
 }
 
 // In-place RMW bandwidth of one buffer: persistent (one launch of 8 workgroups per CU),
-// non-persistent as one launch, and non-persistent per 1 GiB slice.
+// non-persistent (8 KiB single-wave chunks) as one launch, and the same per 1 GiB slice.
 struct RmwRates {
     double persistent, np, np_sliced;
 };
@@ -202,14 +210,15 @@ static RmwRates rmw_gbps(char *buf, uint64_t nchunks, int cus)
     u32x4_t *p = reinterpret_cast<u32x4_t *>(buf);
     const int grid = cus * 8;
     const double bytes = 2.0 * nchunks * kChunk16 * 16;
-    const uint64_t sl = (1ull << 30) / (kChunk16 * 16);   // chunks per 1 GiB slice
+    const uint64_t nnp = nchunks * kChunk16 / (kNpLoads * 64);   // 8 KiB chunks
+    const uint64_t sl = (1ull << 30) / (kNpLoads * 1024);         // 8 KiB chunks per 1 GiB
     RmwRates r;
     r.persistent = bytes / (time_ms([&] { hipLaunchKernelGGL(k_rmw, dim3(grid), dim3(256), 0, 0, p, nchunks); }, 3) * 1e6);
-    r.np = bytes / (time_ms([&] { hipLaunchKernelGGL(k_rmw_np, dim3(np_grid(nchunks)), dim3(256), 0, 0, p, nchunks); }, 3) * 1e6);
+    r.np = bytes / (time_ms([&] { hipLaunchKernelGGL(k_rmw_np<kNpLoads>, dim3(np_grid(nnp)), dim3(64), 0, 0, p, nnp); }, 3) * 1e6);
     r.np_sliced = bytes / (time_ms([&] {
-        for (uint64_t s0 = 0; s0 < nchunks; s0 += sl) {
-            const uint64_t m = nchunks - s0 < sl ? nchunks - s0 : sl;
-            hipLaunchKernelGGL(k_rmw_np, dim3(np_grid(m)), dim3(256), 0, 0, p + s0 * kChunk16, m);
+        for (uint64_t s0 = 0; s0 < nnp; s0 += sl) {
+            const uint64_t m = nnp - s0 < sl ? nnp - s0 : sl;
+            hipLaunchKernelGGL(k_rmw_np<kNpLoads>, dim3(np_grid(m)), dim3(64), 0, 0, p + s0 * (kNpLoads * 64), m);
         } }, 3) * 1e6);
     return r;
 }
@@ -295,15 +304,16 @@ int main(int argc, char **argv)
             for (int i = 0; i < 4; ++i)
                 if (gbs[i] > best[i]) best[i] = gbs[i];
         }
-        {   // non-persistent form: one chunk per wave
+        {   // non-persistent form: single-wave workgroups, one chunk each
             u32x4_t *p = reinterpret_cast<u32x4_t *>(buf);
-            const uint64_t half = nchunks / 2;
+            const uint64_t n8 = bytes / (kNpLoads * 1024), n4 = bytes / (kNpWriteLoads * 1024);
+            const uint64_t half = n8 / 2;
             double gbs[4];
-            gbs[0] = bytes / (time_ms([&] { hipLaunchKernelGGL(k_read_np, dim3(np_grid(nchunks)), dim3(256), 0, 0, p, nchunks, sink); }, 5) * 1e6);
-            gbs[1] = bytes / (time_ms([&] { hipLaunchKernelGGL(k_write_np, dim3(np_grid(nchunks)), dim3(256), 0, 0, p, nchunks); }, 5) * 1e6);
-            gbs[2] = 2.0 * half * chunk_bytes /
-                     (time_ms([&] { hipLaunchKernelGGL(k_copy_np, dim3(np_grid(half)), dim3(256), 0, 0, p, p + half * kChunk16, half); }, 5) * 1e6);
-            gbs[3] = 2.0 * bytes / (time_ms([&] { hipLaunchKernelGGL(k_rmw_np, dim3(np_grid(nchunks)), dim3(256), 0, 0, p, nchunks); }, 5) * 1e6);
+            gbs[0] = 1024.0 * kNpLoads * n8 / (time_ms([&] { hipLaunchKernelGGL(k_read_np<kNpLoads>, dim3(np_grid(n8)), dim3(64), 0, 0, p, n8, sink); }, 5) * 1e6);
+            gbs[1] = 1024.0 * kNpWriteLoads * n4 / (time_ms([&] { hipLaunchKernelGGL(k_write_np<kNpWriteLoads>, dim3(np_grid(n4)), dim3(64), 0, 0, p, n4); }, 5) * 1e6);
+            gbs[2] = 2.0 * 1024.0 * kNpLoads * half /
+                     (time_ms([&] { hipLaunchKernelGGL(k_copy_np<kNpLoads>, dim3(np_grid(half)), dim3(64), 0, 0, p, p + half * (kNpLoads * 64), half); }, 5) * 1e6);
+            gbs[3] = 2.0 * 1024.0 * kNpLoads * n8 / (time_ms([&] { hipLaunchKernelGGL(k_rmw_np<kNpLoads>, dim3(np_grid(n8)), dim3(64), 0, 0, p, n8); }, 5) * 1e6);
             printf("round %d non-persistent  : read %.1f  write %.1f  copy %.1f  rmw %.1f GB/s\n", r,
                    gbs[0], gbs[1], gbs[2], gbs[3]);
             fflush(stdout);

@@ -2,9 +2,9 @@
 
 The streaming bandwidth of a large allocation depends on the physical memory the driver
 gives it, which neither the kernels nor the caller choose: on MI355X a 60 GB buffer read
-and written back in place as one launch runs at about 5.8 TB/s on some allocations and
-6.3-6.4 TB/s on others (1 GiB launches, which `zo_tune_placement` picks on slow memory, reach
-about 6.0 TB/s on either).  Allocations made while earlier ones are still held land on other
+and written back in place as one launch runs at about 6.0-6.1 TB/s on some allocations and
+6.45 TB/s on others, while 1 GiB launches reach about 5.9-6.0 TB/s on either; so one launch
+beats the slices by 2-5% on slow memory and by 8-9% on fast memory.  Allocations made while earlier ones are still held land on other
 memory, so trying a few is enough to find a fast one.
 
 `relocate` keeps the caller's buffer, allocates up to `tries` more buffers of its size while
@@ -25,7 +25,7 @@ def _rate(r: dict) -> float:
 
 
 def relocate(ctx, buf: torch.Tensor, tries: int = 3, headroom_bytes: int = 8 << 30,
-             fast_ratio: float = 1.03, min_gain: float = 1.02, copy: bool = True):
+             fast_ratio: float = 1.06, min_gain: float = 1.02, copy: bool = True):
     """Return (buffer, report): `buf` itself, or a same-shaped tensor on faster memory holding
     a copy of its contents.
 
