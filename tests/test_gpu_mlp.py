@@ -113,10 +113,11 @@ def test_pair_equals_two_fused_calls(ctx, shape, mode):
 @pytest.mark.parametrize("shape", [(16, 16, 16, 2), (32, 48, 64, 3), (48, 144, 128, 16),
                                    (128, 768, 3072, 2)])
 @pytest.mark.parametrize("mode", ["regen", "bits"])
-@pytest.mark.parametrize("nprobes", [1, 3, 8, 13])
+@pytest.mark.parametrize("nprobes", [1, 3, 8, 13, 21])
 def test_probes_equal_pairs(ctx, shape, mode, nprobes):
     """zo_mlp_loss_probes gives, for every probe of the batch, exactly the losses of
-    zo_mlp_loss_pair (13 probes run as launches of 8, 4 and 1); parameters untouched."""
+    zo_mlp_loss_pair (21 probes run as launch sequences of 16, 4 and 1 probes, 13 as 8, 4
+    and 1, each with several probes per wave); parameters untouched."""
     batch, d_in, d_hid, d_out = shape
     theta, X, y = _problem(*shape, seed=57 + sum(shape) + nprobes)
     t, x, yl = _dev(theta, X, y)
@@ -139,9 +140,9 @@ def test_probes_argument_checks(ctx):
     t, x, yl = _dev(theta, X, y)
     L = zo._lib.lib()
     need = zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 5)
-    eight = zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 8)
-    assert zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 100) == eight   # 8 per launch
-    assert need * 8 == eight * 5
+    sixteen = zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 16)
+    assert zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 100) == sixteen   # 16 per launch
+    assert need * 16 == sixteen * 5
     assert zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 1) == zo.zo_mlp_workspace_bytes(16, 16, 16, 2)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     out = torch.empty(10, dtype=torch.float64, device="cuda")
