@@ -18,9 +18,15 @@
 //  * Work split.  A wave takes 8 consecutive 128-param blocks; the 8 lanes of an "octet"
 //    share one block.  Per group, lane r of an octet produces probe 8g+r's 128 bits for
 //    that block (Philox, or 16 bytes of a stored row), so no Philox call is repeated.
-//    The octet swaps 32-bit words through a 1 KiB per-wave LDS slice so that lane r
-//    holds the 16 bits of all eight probes for its own 16 params 16r .. 16r+15; four
-//    v_perm_b32 select bytes and two 8x8 bit transposes turn them into 16 table indices.
+//    Lane r of the octet owns two runs of 8 params, 8r .. 8r+7 and 64+8r .. 64+8r+7 (sign
+//    bytes r and r+8 of the block), so that the octet's 16-byte accesses to a run of theta
+//    cover whole 128-byte lines in one instruction (a lane owning 16 consecutive params
+//    instead would leave each instruction 16-byte pieces 32 or 64 bytes apart: measured
+//    on a 500 MB buffer, 2.7 against 5.4 TB/s in fp32, 4.9 against 5.9 in bf16).  The
+//    octet swaps the 16-bit byte pairs (byte j, byte j+8) of its eight probes through a
+//    1 KiB per-wave LDS slice (four v_perm_b32 and eight 16-bit stores per lane, one
+//    16-byte read); four v_perm_b32 and two 8x8 bit transposes then turn the eight
+//    probes' bytes r and r+8 into the lane's 16 table indices.
 //  * Each lane keeps 16 fp64 sums (tables in ascending group order), then reads its 16
 //    params once, forms and rounds the new values, and writes them once.
 //  * Deterministic: every sum is taken in a fixed order independent of the grid.
@@ -29,8 +35,8 @@
 //    as zo_perturb rounds it -- the last restore of the two-pass schedule, which nothing
 //    reads before the update, folded into the update's single pass over theta.  That
 //    probe's bits are produced by the update anyway: after the octet exchange of its group,
-//    lane r holds word r/2 of every probe of the group, whose half r%2 is the 16 sign bits
-//    of the lane's own params, so the fold costs no extra Philox call.  (The unrolled
+//    lane r holds bytes r and r+8 of every probe of the group, the 16 sign bits of its own
+//    params, so the fold costs no extra Philox call.  (The unrolled
 //    form below takes them from one Philox call of their own per lane and block instead.)
 //  * Unrolled form.  At the group counts of the usual probe counts (2, 4, 8, 20 groups) the
 //    group loop is unrolled and the tables sit at fixed LDS addresses, so each lookup's
@@ -45,11 +51,13 @@ namespace zo {
 constexpr int kUpdWavesPerWG = 8;
 constexpr int kUpdThreads = kUpdWavesPerWG * kWave;
 constexpr int kUpdBlocksPerWave = 8;
-// 8 octets x (8 lanes x 4 words), octet slices 40 words apart so that the eight octets'
-// stores of one word fall in distinct LDS banks (a 32-word stride would put the even and
-// the odd octets on the same banks).
+// 8 octets x (8 readers x 8 probes x 16 bits), octet slices 40 words apart so that the
+// eight octets' stores of one slot fall in distinct LDS banks (a 32-word stride would put
+// the even and the odd octets on the same banks).
 constexpr uint32_t kOctetStride = 40;
 constexpr uint32_t kXchWordsPerWave = 8 * kOctetStride;
+static_assert(kUpdWavesPerWG * kXchWordsPerWave >= 8 * ((kMaxNpert + 7) / 8),
+              "the exchange slices stage the weights of every group");
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -106,16 +114,20 @@ __device__ __forceinline__ uint32_t restore_bf16_pair(uint32_t w, float dlo, flo
     return pack_bf16x2(bf16lo_to_f32(w) + dlo, bf16hi_to_f32(w) + dhi);
 }
 
+// The lane's 16 params are the runs e0 .. e0+7 and e0+64 .. e0+71: s[q] and bit q of rmask
+// belong to param e0 + q for q < 8 and to param e0 + 56 + q for q >= 8.
 template <bool kBF16, bool kRestore>
 __device__ __forceinline__ void apply_update(void *theta, uint64_t e0, uint64_t n,
                                              const double (&s)[16], double eta, uint32_t rmask,
                                              uint32_t rabits)
 {
-    if (e0 + 16 <= n) {
+    if (e0 + 72 <= n) {
         if constexpr (kBF16) {
-            u32x4_t *p = reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(theta) + e0);
-            u32x4_t t0 = __builtin_nontemporal_load(p);
-            u32x4_t t1 = __builtin_nontemporal_load(p + 1);
+            uint16_t *base = static_cast<uint16_t *>(theta) + e0;
+            u32x4_t *p0 = reinterpret_cast<u32x4_t *>(base);
+            u32x4_t *p1 = reinterpret_cast<u32x4_t *>(base + 64);
+            u32x4_t t0 = __builtin_nontemporal_load(p0);
+            u32x4_t t1 = __builtin_nontemporal_load(p1);
             if constexpr (kRestore) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -132,30 +144,36 @@ __device__ __forceinline__ void apply_update(void *theta, uint64_t e0, uint64_t 
                 t1[j] = bf16pair_from_f64((double)bf16lo_to_f32(t1[j]) - eta * s[8 + 2 * j],
                                           (double)bf16hi_to_f32(t1[j]) - eta * s[9 + 2 * j]);
             }
-            __builtin_nontemporal_store(t0, p);
-            __builtin_nontemporal_store(t1, p + 1);
+            __builtin_nontemporal_store(t0, p0);
+            __builtin_nontemporal_store(t1, p1);
         } else {
-            u32x4_t *p = reinterpret_cast<u32x4_t *>(static_cast<float *>(theta) + e0);
+            float *base = static_cast<float *>(theta) + e0;
+            u32x4_t *p[4] = {reinterpret_cast<u32x4_t *>(base), reinterpret_cast<u32x4_t *>(base + 4),
+                             reinterpret_cast<u32x4_t *>(base + 64),
+                             reinterpret_cast<u32x4_t *>(base + 68)};
+            u32x4_t t[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) t[v] = __builtin_nontemporal_load(p[v]);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                u32x4_t t = __builtin_nontemporal_load(p + v);
                 if constexpr (kRestore) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        t[j] = __float_as_uint(__uint_as_float(t[j]) +
-                                               restore_step(rmask, 4 * v + j, rabits));
+                        t[v][j] = __float_as_uint(__uint_as_float(t[v][j]) +
+                                                  restore_step(rmask, 4 * v + j, rabits));
                 }
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    t[j] = __float_as_uint(
-                        (float)((double)__uint_as_float(t[j]) - eta * s[4 * v + j]));
-                __builtin_nontemporal_store(t, p + v);
+                    t[v][j] = __float_as_uint(
+                        (float)((double)__uint_as_float(t[v][j]) - eta * s[4 * v + j]));
             }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) __builtin_nontemporal_store(t[v], p[v]);
         }
     } else if (e0 < n) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-            const uint64_t e = e0 + q;
+            const uint64_t e = e0 + (q < 8 ? (uint64_t)q : (uint64_t)(56 + q));
             if (e < n) {
                 if constexpr (kBF16) {
                     uint16_t *t = static_cast<uint16_t *>(theta);
@@ -184,8 +202,13 @@ __device__ __forceinline__ void apply_update(void *theta, uint64_t e0, uint64_t 
 // are static LDS at known addresses and the group loop is unrolled, so every table read
 // carries its group's table offset as the instruction's immediate offset and the lookup
 // index costs a single byte-select shift.  kNG == 0: any group count, tables in dynamic LDS.
+// Two unrolled groups leave the compiler more to interleave: at six waves (80 registers)
+// the restore form would spill two loop-invariant registers; five waves (96) do not.
+template <int kNG>
+constexpr int kUpdWaves = kNG == 2 ? 5 : 6;
+
 template <bool kBF16, bool kBits, bool kRestore, int kNG>
-__global__ __launch_bounds__(kUpdThreads) __attribute__((amdgpu_waves_per_eu(6, 6))) void k_update(void *__restrict__ theta, uint64_t n,
+__global__ __launch_bounds__(kUpdThreads) __attribute__((amdgpu_waves_per_eu(kUpdWaves<kNG>, kUpdWaves<kNG>))) void k_update(void *__restrict__ theta, uint64_t n,
                                                         uint64_t blk0, uint32_t step,
                                                         uint32_t k0, uint32_t k1,
                                                         const float *__restrict__ c,
@@ -201,17 +224,21 @@ __global__ __launch_bounds__(kUpdThreads) __attribute__((amdgpu_waves_per_eu(6, 
     const uint32_t ng = kNG > 0 ? (uint32_t)kNG : ngroups;
     double *tbl = kNG > 0 ? stbl : lds_d;
     const int wv = threadIdx.x / kWave;
-    uint32_t *xch = (kNG > 0 ? sxch : reinterpret_cast<uint32_t *>(lds_d + ngroups * 256u)) +
-                    wv * kXchWordsPerWave;
+    uint32_t *xbase = kNG > 0 ? sxch : reinterpret_cast<uint32_t *>(lds_d + ngroups * 256u);
+    uint32_t *xch = xbase + wv * kXchWordsPerWave;
 
+    // The weights, padded with zeros to whole groups, staged once in the (not yet used)
+    // exchange slices: one global read per probe instead of eight per table entry.
+    float *cw = reinterpret_cast<float *>(xbase);
+    for (uint32_t i = threadIdx.x; i < ng * 8u; i += blockDim.x) cw[i] = i < npert ? c[i] : 0.0f;
+    __syncthreads();
     // Signed partial-sum tables, probes ascending within each group.
     for (uint32_t e = threadIdx.x; e < ng * 256u; e += blockDim.x) {
         const uint32_t g = e >> 8, b = e & 255u;
         double acc = 0.0;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const uint32_t i = g * 8u + (uint32_t)k;
-            const double ci = i < npert ? (double)c[i] : 0.0;
+            const double ci = (double)cw[g * 8u + (uint32_t)k];
             acc = acc + (((b >> k) & 1u) ? ci : -ci);
         }
         tbl[e] = acc;
@@ -222,9 +249,9 @@ __global__ __launch_bounds__(kUpdThreads) __attribute__((amdgpu_waves_per_eu(6, 
     const int oct = lane >> 3;
     const int r = lane & 7;
     uint32_t *oxch = xch + oct * kOctetStride;
-    const uint32_t beta = 2u * (uint32_t)(r & 1);
-    // byte beta of x, byte beta of y, byte beta+1 of x, byte beta+1 of y
-    const uint32_t sel = beta | ((4u + beta) << 8) | ((beta + 1u) << 16) | ((5u + beta) << 24);
+    // 16-bit slot (reader j, probe k) of the octet's slice: reader j's eight slots are one
+    // aligned 16-byte read.
+    uint16_t *oslot = reinterpret_cast<uint16_t *>(oxch);
 
     const uint64_t nblk = (n + kBlockParams - 1) / kBlockParams;
     const uint64_t nwc = (nblk + kUpdBlocksPerWave - 1) / kUpdBlocksPerWave;
@@ -232,28 +259,17 @@ __global__ __launch_bounds__(kUpdThreads) __attribute__((amdgpu_waves_per_eu(6, 
 
     for (uint64_t wc = (uint64_t)blockIdx.x * kUpdWavesPerWG + wv; wc < nwc; wc += nwaves) {
         const uint64_t lb = wc * kUpdBlocksPerWave + oct;  // local block of this octet
-        const uint64_t e0 = lb * kBlockParams + 16u * (uint32_t)r;
+        const uint64_t e0 = lb * kBlockParams + 8u * (uint32_t)r;   // the lane's first run
         double s[16];
 #pragma unroll
         for (int q = 0; q < 16; ++q) s[q] = 0.0;
-        uint32_t rmask = 0;   // kRestore: bit q = sign bit of probe rprobe at param e0 + q
+        uint32_t rmask = 0;   // kRestore: bit q = sign bit of probe rprobe at the lane's param q
         // The lane's probe slot, opaque to the optimiser inside this loop: with the group
         // loop unrolled, everything derived from it per group (the probe's first Philox
         // product, its bit-row address) would otherwise be hoisted out of the block loop and
         // held in registers for all groups at once.
         uint32_t rr = (uint32_t)r;
-        if constexpr (kNG > 0) {
-            asm volatile("" : "+v"(rr));
-            if constexpr (kRestore) {
-                // The restore probe's bits for the lane's 16 params from their own Philox
-                // call (word r/2, half r%2), instead of picking them out of whichever
-                // unrolled group holds that probe.
-                const U32x4 q = probe_block_bits(blk0 + lb, rprobe, step, k0, k1);
-                const uint32_t h = rr >> 1;
-                const uint32_t word = h == 0 ? q.x : h == 1 ? q.y : h == 2 ? q.z : q.w;
-                rmask = (word >> (16u * (rr & 1u))) & 0xFFFFu;
-            }
-        }
+        if constexpr (kNG > 0) asm volatile("" : "+v"(rr));
 
         auto group = [&](uint32_t g) {
             const uint32_t i = g * 8u + rr;
@@ -270,31 +286,34 @@ __global__ __launch_bounds__(kUpdThreads) __attribute__((amdgpu_waves_per_eu(6, 
                 const U32x4 q = probe_block_bits(blk0 + lb, i, step, k0, k1);
                 w = u32x4_t{q.x, q.y, q.z, q.w};
             }
+            // pair j = byte j | byte j+8 << 8 of this lane's probe, for j = 0 .. 7
+            const uint32_t p01 = __builtin_amdgcn_perm(w.z, w.x, 0x05010400u);
+            const uint32_t p23 = __builtin_amdgcn_perm(w.z, w.x, 0x07030602u);
+            const uint32_t p45 = __builtin_amdgcn_perm(w.w, w.y, 0x05010400u);
+            const uint32_t p67 = __builtin_amdgcn_perm(w.w, w.y, 0x07030602u);
             wave_lds_sync();  // previous group's reads precede these writes
-            oxch[0 * 8 + r] = w.x;
-            oxch[1 * 8 + r] = w.y;
-            oxch[2 * 8 + r] = w.z;
-            oxch[3 * 8 + r] = w.w;
+            oslot[0 * 8 + r] = (uint16_t)p01;
+            oslot[1 * 8 + r] = (uint16_t)(p01 >> 16);
+            oslot[2 * 8 + r] = (uint16_t)p23;
+            oslot[3 * 8 + r] = (uint16_t)(p23 >> 16);
+            oslot[4 * 8 + r] = (uint16_t)p45;
+            oslot[5 * 8 + r] = (uint16_t)(p45 >> 16);
+            oslot[6 * 8 + r] = (uint16_t)p67;
+            oslot[7 * 8 + r] = (uint16_t)(p67 >> 16);
             wave_lds_sync();
-            // word (r >> 1) of probes 0..3 and 4..7 of the group
-            const u32x4_t a = *reinterpret_cast<const u32x4_t *>(oxch + (r >> 1) * 8);
-            const u32x4_t b = *reinterpret_cast<const u32x4_t *>(oxch + (r >> 1) * 8 + 4);
-            const uint32_t a01 = __builtin_amdgcn_perm(a.y, a.x, sel);
-            const uint32_t a23 = __builtin_amdgcn_perm(a.w, a.z, sel);
-            const uint32_t b01 = __builtin_amdgcn_perm(b.y, b.x, sel);
-            const uint32_t b23 = __builtin_amdgcn_perm(b.w, b.z, sel);
-            uint32_t Llo = __builtin_amdgcn_perm(a23, a01, 0x05040100u);
-            uint32_t Hlo = __builtin_amdgcn_perm(b23, b01, 0x05040100u);
-            uint32_t Lhi = __builtin_amdgcn_perm(a23, a01, 0x07060302u);
-            uint32_t Hhi = __builtin_amdgcn_perm(b23, b01, 0x07060302u);
+            // x.k/2 = (byte r, byte r+8) of probes k and k+1 of the group, k even
+            const u32x4_t x = *reinterpret_cast<const u32x4_t *>(oxch + 4 * r);
+            uint32_t Llo = __builtin_amdgcn_perm(x.y, x.x, 0x06040200u);   // byte r, probes 0-3
+            uint32_t Lhi = __builtin_amdgcn_perm(x.y, x.x, 0x07050301u);   // byte r+8
+            uint32_t Hlo = __builtin_amdgcn_perm(x.w, x.z, 0x06040200u);   // probes 4-7
+            uint32_t Hhi = __builtin_amdgcn_perm(x.w, x.z, 0x07050301u);
             transpose8x8(Llo, Hlo);
             transpose8x8(Lhi, Hhi);
             if constexpr (kRestore && kNG == 0) {
                 if (g == (rprobe >> 3)) {   // uniform: the restore probe's group
-                    const uint32_t k = rprobe & 3u;
-                    const u32x4_t &wk = (rprobe & 4u) ? b : a;
-                    const uint32_t word = k == 0 ? wk.x : k == 1 ? wk.y : k == 2 ? wk.z : wk.w;
-                    rmask = (word >> (16u * (uint32_t)(r & 1))) & 0xFFFFu;
+                    const uint32_t k = rprobe & 7u;
+                    const uint32_t word = k < 2 ? x.x : k < 4 ? x.y : k < 6 ? x.z : x.w;
+                    rmask = (word >> (16u * (k & 1u))) & 0xFFFFu;
                 }
             }
             const double *tg = tbl + g * 256u;
@@ -316,6 +335,15 @@ __global__ __launch_bounds__(kUpdThreads) __attribute__((amdgpu_waves_per_eu(6, 
             }
         } else {
             for (uint32_t g = 0; g < ngroups; ++g) group(g);
+        }
+        if constexpr (kNG > 0 && kRestore) {
+            // The restore probe's bits for the lane's 16 params from their own Philox call
+            // (bytes r and r+8), instead of picking them out of whichever unrolled group
+            // holds that probe.
+            const U32x4 q = probe_block_bits(blk0 + lb, rprobe, step, k0, k1);
+            const uint32_t lo = (rr >> 2) ? q.y : q.x, hi = (rr >> 2) ? q.w : q.z;
+            const uint32_t b = rr & 3u;   // byte b of lo, byte b of hi, then zeros
+            rmask = __builtin_amdgcn_perm(hi, lo, b | ((4u + b) << 8) | 0x0C0C0000u);
         }
         apply_update<kBF16, kRestore>(theta, e0, n, s, eta, rmask, rabits);
     }
