@@ -40,6 +40,12 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_perturb.json")
 PERTURB_SOURCES = ["forward_only_amd/csrc/k_perturb.hip", "forward_only_amd/csrc/zo_device.hpp"]
 PHILOX_FILE = os.path.join(ROOT, "profiles", "philox_ceiling.json")
 PHILOX_SOURCES = ["forward_only_amd/csrc/zo_device.hpp", "forward_only_amd/ceiling/philox_ceiling.hip"]
+UPDATE_VALU_FILE = os.path.join(ROOT, "profiles", "update_valu.json")
+UPDATE_SOURCES = ["forward_only_amd/csrc/k_update.hip", "forward_only_amd/csrc/zo_device.hpp",
+                  "forward_only_amd/csrc/zo_launch.hpp"]
+# VALU issue limit: 256 CUs x 4 SIMDs x 2.4 GHz, one wave64 VALU instruction per SIMD every
+# 4 cycles (16 lanes per cycle).
+PEAK_VALU_WAVE_INSTS = 256 * 4 * 2.4e9 / 4
 
 
 def log(*a):
@@ -180,14 +186,38 @@ def copy_calibration():
                       "dispatches": 3}), flush=True)
 
 
-def update_roofline(M: int, n: int, pass_bytes: float, upd_ms):
-    """The update kernel beside its two ceilings: HBM bytes (one read and one write of theta)
-    and the Philox calls it makes to regenerate n probes' bits (n / 128 per parameter)."""
+def stored_update_valu(dtype: str, n: int, restore: bool):
+    """VALU instructions per parameter and 8-probe group of the update kernel, from the
+    committed rocprofv3 counter summary, if it was taken on the current kernel source and on
+    the same kernel form (dtype, probe count, restore folded in or not); else None."""
+    try:
+        with open(UPDATE_VALU_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if (t.get("source_sha256") != source_hash(UPDATE_SOURCES) or t.get("dtype") != dtype
+            or t.get("n_pert") != n or t.get("restore") != restore):
+        return None
+    return float(t["valu_insts_per_param_group"])
+
+
+def update_roofline(M: int, n: int, pass_bytes: float, upd_ms, dtype: str, restore: bool):
+    """The update kernel against the VALU issue limit that bounds it (its instruction count
+    from the counter summary x the work of one launch / the launch's time), beside its HBM
+    bytes (one read and one write of theta) and the Philox calls it makes to regenerate n
+    probes' bits (n / 128 per parameter)."""
     if not upd_ms:
         return None
     calls = M * n / 128.0 / (upd_ms * 1e-3)
     peak = stored_philox_peak()
-    return {"kernel": "k_update", "bound": "valu+lds",
+    per = stored_update_valu(dtype, n, restore)
+    insts = per * M * ((n + 7) // 8) / 64.0 if per is not None else None
+    achieved = insts / (upd_ms * 1e-3) if insts is not None else None
+    return {"kernel": "k_update", "bound": "alu",
+            "achieved": achieved, "peak": PEAK_VALU_WAVE_INSTS,
+            "unit": "wave64 VALU instructions/s",
+            "frac": (achieved / PEAK_VALU_WAVE_INSTS) if achieved is not None else None,
+            "valu_insts_per_param_group": per,
             "achieved_GBps": pass_bytes / (upd_ms * 1e-3) / 1e9,
             "hbm_frac": pass_bytes / (upd_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
             "probe_params_per_s": n * M / (upd_ms * 1e-3),
@@ -542,7 +572,8 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
                                  "frac_of_placement_ceiling": (achieved / placement_gbps
                                                                if placement_gbps else None)},
         "pass_roofline": pass_roofline,
-        "update_roofline": update_roofline(M, n, pass_bytes, upd_ms),
+        "update_roofline": update_roofline(M, n, pass_bytes, upd_ms, cfg.dtype,
+                                           mlp is None and schedule == "S2f"),
         "gen_probes": gen_probes,
         "nonfinite_probes": nonfinite,
         "cpu_baseline": cpu,
