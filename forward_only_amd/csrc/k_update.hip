@@ -63,24 +63,48 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // In-register transpose of an 8x8 bit matrix held as two dwords (rows 0-3 in L, rows
 // 4-7 in H, row k = byte k, column b = bit b): afterwards byte b holds column b.
-// Three masked delta swaps (distances 7, 14, 28 in the 64-bit view).
-// Each swap is t = (x ^ (x >> d)) & mask; x ^= t ^ (t << d): two shifts and two
-// three-input bit ops.
-__device__ __forceinline__ uint32_t delta_swap(uint32_t x, int d, uint32_t mask)
+// Three masked delta swaps, one per bit of the row and column index (distances 7, 14, 28
+// in the 64-bit view; they commute).  A swap is t = (x ^ (x >> d)) & mask;
+// x ^= t ^ (t << d).  For d = 7 and 14 the shifts act on the register pair as one 64-bit
+// value (no masked bit crosses the dword boundary), one v_lshrrev_b64 / v_lshlrev_b64
+// each instead of two 32-bit shifts; the compiler turns 64-bit shifts written in C into
+// 32-bit pairs or multiplies, so they are spelled out (plain ALU instructions, no memory
+// access).  The d = 28 swap exchanges L's high nibbles with H's
+// low nibbles: two shifts and two bit selects.
+template <int D>
+__device__ __forceinline__ uint64_t shr64(uint64_t x)
 {
-    const uint32_t t = ZO_BITOP3(x, x >> d, mask, kXorAnd);
-    return ZO_BITOP3(x, t, t << d, kXor3);
+    uint64_t r;
+    asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "n"(D), "v"(x));
+    return r;
+}
+template <int D>
+__device__ __forceinline__ uint64_t shl64(uint64_t x)
+{
+    uint64_t r;
+    asm("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "n"(D), "v"(x));
+    return r;
+}
+
+template <int D>
+__device__ __forceinline__ void delta_swap2(uint32_t &L, uint32_t &H, uint32_t mask)
+{
+    const uint64_t x = ((uint64_t)H << 32) | L;
+    const uint64_t s = shr64<D>(x);
+    const uint32_t tl = ZO_BITOP3(L, (uint32_t)s, mask, kXorAnd);
+    const uint32_t th = ZO_BITOP3(H, (uint32_t)(s >> 32), mask, kXorAnd);
+    const uint64_t u = shl64<D>(((uint64_t)th << 32) | tl);
+    L = ZO_BITOP3(L, tl, (uint32_t)u, kXor3);
+    H = ZO_BITOP3(H, th, (uint32_t)(u >> 32), kXor3);
 }
 
 __device__ __forceinline__ void transpose8x8(uint32_t &L, uint32_t &H)
 {
-    L = delta_swap(L, 7, 0x00AA00AAu);
-    H = delta_swap(H, 7, 0x00AA00AAu);
-    L = delta_swap(L, 14, 0x0000CCCCu);
-    H = delta_swap(H, 14, 0x0000CCCCu);
-    const uint32_t t = ZO_BITOP3(L, H << 4, 0xF0F0F0F0u, kXorAnd);
-    L = L ^ t;
-    H = H ^ (t >> 4);
+    delta_swap2<7>(L, H, 0x00AA00AAu);
+    delta_swap2<14>(L, H, 0x0000CCCCu);
+    const uint32_t l = L, h = H;
+    L = ZO_BITOP3(l, h << 4, 0xF0F0F0F0u, 0xD8);   // mask ? h << 4 : l
+    H = ZO_BITOP3(l >> 4, h, 0xF0F0F0F0u, 0xD8);   // mask ? h : l >> 4
 }
 
 // double -> fp32 rounded to odd: truncate toward zero, then set the last bit if anything
@@ -112,6 +136,20 @@ __device__ __forceinline__ float restore_step(uint32_t rmask, int q, uint32_t ra
 __device__ __forceinline__ uint32_t restore_bf16_pair(uint32_t w, float dlo, float dhi)
 {
     return pack_bf16x2(bf16lo_to_f32(w) + dlo, bf16hi_to_f32(w) + dhi);
+}
+
+// Table entry of byte q of x, the byte times 8 being its LDS byte offset: one shift with an
+// SDWA byte select.  The compiler emits that form for bytes 1-3 by itself but masks and
+// shifts byte 0 in two instructions, so byte 0's is spelled out (a plain ALU instruction).
+__device__ __forceinline__ double lookup(const double *tg, uint32_t x, int q)
+{
+    uint32_t off;
+    if (q == 0)
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
+            : "=v"(off) : "v"(x));
+    else
+        off = ((x >> (8 * q)) & 255u) << 3;
+    return *reinterpret_cast<const double *>(reinterpret_cast<const char *>(tg) + off);
 }
 
 // The lane's 16 params are the runs e0 .. e0+7 and e0+64 .. e0+71: s[q] and bit q of rmask
@@ -319,10 +357,10 @@ __global__ __launch_bounds__(kUpdThreads) __attribute__((amdgpu_waves_per_eu(kUp
             const double *tg = tbl + g * 256u;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                s[q] += tg[(Llo >> (8 * q)) & 255u];
-                s[4 + q] += tg[(Hlo >> (8 * q)) & 255u];
-                s[8 + q] += tg[(Lhi >> (8 * q)) & 255u];
-                s[12 + q] += tg[(Hhi >> (8 * q)) & 255u];
+                s[q] += lookup(tg, Llo, q);
+                s[4 + q] += lookup(tg, Hlo, q);
+                s[8 + q] += lookup(tg, Lhi, q);
+                s[12 + q] += lookup(tg, Hhi, q);
             }
         };
         if constexpr (kNG > 0) {
