@@ -72,11 +72,16 @@ hipError_t launch_zero_u32(uint32_t *p, uint32_t count, hipStream_t stream)
 }
 
 // ---- diagonal quadratic loss: 1/2 sum_j a_j theta_j^2 in fp64 ------------------------
-// Pass 1: kLossPartials workgroups; thread i of the grid takes the 8-element groups
-// i, i + G, i + 2G, ... (16-byte loads of theta and a; G = total threads), then the ragged
-// end one element at a time; each wave adds its lanes with a fixed butterfly and the
-// workgroup adds its waves in order.  Pass 2: one workgroup adds the partials the same
-// way.  The partition depends only on n, so the result is bit-reproducible.
+// Pass 1: kLossPartials workgroups of four waves; wave w of the grid takes the chunks of
+// kLossChunk params w, w + W, w + 2W, ... (W = total waves).  In a chunk, lane l reads
+// params 256k + 4l .. 256k + 4l + 3 for k = 0 .. 7: every load instruction moves one
+// contiguous KiB of a (and of fp32 theta; half a KiB of bf16 theta), and all sixteen of a
+// chunk's loads are issued before any is used, so each wave keeps 12-16 KiB in flight.
+// Then the ragged end (n mod kLossChunk params) one element per thread; each wave adds its
+// lanes with a fixed butterfly and the workgroup adds its waves in order.  Pass 2: one
+// workgroup adds the partials the same way.  The partition depends only on n, so the
+// result is bit-reproducible.
+constexpr uint32_t kLossChunk = 2048;
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -137,18 +142,51 @@ __global__ __launch_bounds__(256) void k_quad_loss_partial(const void *__restric
     double acc = 0.0;
     const uint64_t G = (uint64_t)gridDim.x * blockDim.x;
     const uint64_t tid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const uint64_t ngroups = n / 8;
-    const f32x4_t *a4 = reinterpret_cast<const f32x4_t *>(a);
-    for (uint64_t g = tid; g < ngroups; g += G) {
-        double t[8];
-        theta8<kBF16>(theta, g, t);
-        const f32x4_t a0 = a4[2 * g], a1 = a4[2 * g + 1];
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint64_t nwaves = (uint64_t)gridDim.x * (blockDim.x / 64u);
+    const uint64_t nchunks = n / kLossChunk;
+    for (uint64_t c = tid / 64u; c < nchunks; c += nwaves) {
+        const uint64_t p0 = c * kLossChunk + 4u * lane;   // + 256 k
+        const f32x4_t *ap = reinterpret_cast<const f32x4_t *>(a + p0);
+        f32x4_t av[8];
+        float tv[8][4];
+        if constexpr (kBF16) {
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            const u32x2_t *tp =
+                reinterpret_cast<const u32x2_t *>(static_cast<const uint16_t *>(theta) + p0);
+            u32x2_t w[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc += (double)a0[q] * t[q] * t[q];
+            for (int k = 0; k < 8; ++k) w[k] = __builtin_nontemporal_load(tp + 64 * k);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc += (double)a1[q] * t[4 + q] * t[4 + q];
+            for (int k = 0; k < 8; ++k) av[k] = __builtin_nontemporal_load(ap + 64 * k);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                tv[k][0] = bf16lo_to_f32(w[k][0]);
+                tv[k][1] = bf16hi_to_f32(w[k][0]);
+                tv[k][2] = bf16lo_to_f32(w[k][1]);
+                tv[k][3] = bf16hi_to_f32(w[k][1]);
+            }
+        } else {
+            const f32x4_t *tp = reinterpret_cast<const f32x4_t *>(static_cast<const float *>(theta) + p0);
+            f32x4_t x[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) x[k] = __builtin_nontemporal_load(tp + 64 * k);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) av[k] = __builtin_nontemporal_load(ap + 64 * k);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) tv[k][q] = x[k][q];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const double t = (double)tv[k][q];
+                acc += (double)av[k][q] * t * t;
+            }
     }
-    for (uint64_t j = ngroups * 8 + tid; j < n; j += G) {
+    for (uint64_t j = nchunks * kLossChunk + tid; j < n; j += G) {
         const double t = theta1<kBF16>(theta, j);
         acc += (double)a[j] * t * t;
     }
