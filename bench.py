@@ -67,7 +67,7 @@ def parse_args(argv=None):
     p.add_argument("--no-relocate", action="store_true",
                    help="keep theta on its first allocation (no placement search)")
     p.add_argument("--no-other-sizes", action="store_true",
-                   help="with the opt30b headline, skip the opt13b and flat125m measurements")
+                   help="with the opt30b headline, skip the opt13b, flat125m and mlp measurements")
     p.add_argument("--cpu-params-per-thread", type=int, default=1 << 20)
     p.add_argument("--cpu-threads", type=int, default=None)
     p.add_argument("--copy-calibration", action="store_true",
@@ -264,7 +264,7 @@ def main(argv=None):
 
 
 # Parameter-set sizes measured beside the 30B headline, and what each reports.
-OTHER_SIZES = ("opt13b", "flat125m")
+OTHER_SIZES = ("opt13b", "flat125m", "mlp")
 OTHER_KEYS = ("value", "unit", "steps", "warmup", "ms_per_step", "ms_per_step_median", "dtype",
               "config", "hbm_gbps", "hbm_frac_of_peak", "kernels_ms", "roofline",
               "pass_roofline", "update_roofline", "nonfinite_probes")
