@@ -327,8 +327,11 @@ def test_update_brute_force_all_sign_patterns(ctx):
 # ------------------------------------------------------------------------------------
 # loss kernel and argument checks
 # ------------------------------------------------------------------------------------
+# The loss kernel takes 2048-param chunks, one per wave of its 4096-wave grid at a time:
+# sizes below, at and just above one chunk, exact chunks, a ragged tail, and more chunks
+# than waves (each wave taking several).
 @pytest.mark.parametrize("kind", ["f32", "bf16"])
-@pytest.mark.parametrize("n", [0, 1, 4096, 1_000_003])
+@pytest.mark.parametrize("n", [0, 1, 2047, 2049, 4096, 1_000_003, 16_777_293])
 def test_quad_loss(ctx, kind, n):
     h = _theta(kind, n, seed=8, scale=0.5)
     a = np.power(10.0, np.random.default_rng(9).uniform(-2, 2, n)).astype(np.float32)
