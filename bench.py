@@ -59,7 +59,7 @@ def parse_args(argv=None):
     p.add_argument("--warmup", type=int, default=1)
     p.add_argument("--config", default="opt30b",
                    choices=["tiny", "flat125m", "mlp", "lowrank", "opt13b", "opt30b"])
-    p.add_argument("--schedule", default="S2f", choices=["S2f", "S4"],
+    p.add_argument("--schedule", default="S2f", choices=["S2f", "S4", "fused"],
                    help="S2f: two passes per probe (restore fused with the next probe's "
                         "move); S4: four passes per probe")
     p.add_argument("--no-cpu-baseline", action="store_true",
@@ -245,7 +245,8 @@ def main(argv=None):
 
     # CPU oracle leg first (host only; keeps the GPU phase uninterrupted).
     cpu = None
-    if not args.no_cpu_baseline and cfg.loss in ("synthetic", "quad"):
+    if (not args.no_cpu_baseline and cfg.loss in ("synthetic", "quad")
+            and args.schedule in ("S2f", "S4")):
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         log(f"[bench] cpu baseline: {threads} threads x {args.cpu_params_per_thread} params")
         cpu = cpu_baseline(cfg, args.cpu_params_per_thread, threads, args.schedule)
@@ -256,23 +257,28 @@ def main(argv=None):
         # the other parameter-set sizes of the same path, measured after the headline (its
         # buffer freed first), each with its own step count and one warmup step
         other = {}
-        for name in OTHER_SIZES:
-            r = run_workload(args, name, CONFIGS[name].steps, 1, cpu=None, gen_plane=False)
-            other[name] = {k: r[k] for k in OTHER_KEYS}
+        for key, name, schedule in OTHER_SIZES:
+            r = run_workload(args, name, CONFIGS[name].steps, 1, cpu=None, gen_plane=False,
+                             schedule=schedule)
+            other[key] = {k: r[k] for k in OTHER_KEYS}
         result["other_sizes"] = other
     print(json.dumps(result), flush=True)
 
 
-# Parameter-set sizes measured beside the 30B headline, and what each reports.
-OTHER_SIZES = ("opt13b", "flat125m", "mlp")
+# Parameter-set sizes measured beside the 30B headline (record key, workload, schedule; None:
+# the workload's own, S2f passes or the MLP's fused forward), and what each reports.
+OTHER_SIZES = (("opt13b", "opt13b", None), ("flat125m", "flat125m", None),
+               ("flat125m_fused", "flat125m", "fused"), ("mlp", "mlp", None))
 OTHER_KEYS = ("value", "unit", "steps", "warmup", "ms_per_step", "ms_per_step_median", "dtype",
               "config", "hbm_gbps", "hbm_frac_of_peak", "kernels_ms", "roofline",
               "pass_roofline", "update_roofline", "nonfinite_probes")
 
 
-def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = True) -> dict:
-    """Time K steps (after W warmup steps) of workload `name` on cuda:0; returns the bench
-    record (the device memory it used is released before it returns)."""
+def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = True,
+                 schedule: str | None = None) -> dict:
+    """Time K steps (after W warmup steps) of workload `name` on cuda:0 with `schedule`
+    (default: --schedule); returns the bench record (the device memory it used is released
+    before it returns)."""
     import numpy as np
     import torch
 
@@ -287,7 +293,9 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
 
-    schedule = args.schedule
+    schedule = schedule or args.schedule
+    if schedule == "fused" and cfg.loss != "quad":
+        raise SystemExit(f"--schedule fused applies to the quadratic workloads, not {name}")
     ctx = zo.zo_init(cfg.seed)
     log(f"[bench] {cfg.name}: M={M} {cfg.dtype} ({M * esize / 1e9:.2f} GB), n_pert={n}, "
         f"steps={K}, warmup={W}")
@@ -347,7 +355,7 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     per = {"perturb": [], "perturb2": [], "weights": [], "update": [], "loss": [], "mlp": [],
-           "mlp_probes": []}
+           "mlp_probes": [], "loss_probes": []}
 
     def timed(kind, fn, record):
         if record:
@@ -393,6 +401,15 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
             timed("update", lambda: zo.zo_update(ctx, theta, 0, s, c_buf, cfg.eta), record)
             return
         loss_into(L0, record)
+        if schedule == "fused":
+            # each probe applied while theta and a are read (four probes per pass), theta
+            # written only by the update
+            timed("loss_probes", lambda: zo.zo_quad_loss_probes(
+                ctx, theta, a_dev, 0, s, 0, n, a, out_plus=Lp, out_minus=Lm), record)
+            timed("weights", lambda: zo.zo_probe_weights(ctx, Lp, Lm, L0, a, cfg.delta,
+                                                         out=c_buf), record)
+            timed("update", lambda: zo.zo_update(ctx, theta, 0, s, c_buf, cfg.eta), record)
+            return
         if schedule == "S4":
             for i in range(n):
                 timed("perturb", lambda: zo.zo_perturb(ctx, theta, 0, s, i, +a), record)
@@ -492,26 +509,41 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
     kernel_ms_per_step = sum(times(list(per))) / K     # sum of every timed kernel call
     # every pass of either perturb entry point runs k_perturb_chunks (one or two probes)
     pert_ms, upd_ms, w_ms = avg_ms("perturb", "perturb2"), avg_ms("update"), avg_ms("weights")
-    passes = 0 if mlp is not None else (4 * n if schedule == "S4" else 2 * n)
+    passes = 0 if mlp is not None or schedule == "fused" else (4 * n if schedule == "S4" else 2 * n)
     pass_bytes = 2.0 * esize * M                      # one read + one write of theta
     step_bytes = (passes + 1) * pass_bytes            # the passes + the update
+    if schedule == "fused":                           # + the clean loss and the fused passes
+        step_bytes += (1 + (n + 3) // 4) * float(esize + 4) * M
     pass_roofline = None
     if pert_ms:
         pa = pass_bytes / (pert_ms * 1e-3) / 1e9
         pass_roofline = {"kernel": "k_perturb_chunks", "bound": "hbm", "achieved": pa,
                          "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": pa / PEAK_HBM_GBPS,
                          "bytes_per_pass": pass_bytes}
-    if mlp is not None:
+    if schedule == "fused":
+        lp_ms = avg_ms("loss_probes")
+        npass = (n + 3) // 4
+        fb = npass * float(esize + 4) * M              # theta and a read once per 4 probes
+        fa = fb / (lp_ms * 1e-3) / 1e9
+        achieved = fa
+        roofline = {"kernel": "k_quad_probes_partial (the quadratic loss at theta +/- alpha z "
+                              "of four probes per pass, theta and a read once; time of the "
+                              f"whole zo_quad_loss_probes call: {npass} passes and their sums)",
+                    "bound": "hbm", "achieved": fa, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": fa / PEAK_HBM_GBPS, "traffic": None,
+                    "losses_per_s": 2.0 * n / (lp_ms * 1e-3)}
+    elif mlp is not None:
         mlp_ms = avg_ms("mlp_probes")
         achieved = 2.0 * n * mlp["flop"] / (mlp_ms * 1e-3) / 1e12
         roofline = {"kernel": "k_mlp_tiles (MFMA fp32 GEMM of the MLP forward, both signs of "
-                              "eight probes per launch; time of the whole zo_mlp_loss_probes "
-                              "call: tiles, row and mean kernels of all n_pert probes)",
+                              "sixteen probes per launch sequence; time of the whole "
+                              "zo_mlp_loss_probes call: tiles, row and mean kernels of all "
+                              "n_pert probes)",
                     "bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS,
                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
                     "traffic": None}
     else:
-        achieved = pass_bytes / (pert_ms * 1e-3) / 1e9
+        achieved = pass_bytes / (pert_ms * 1e-3) / 1e9 if pert_ms else None
         roofline = None
         loss_times = times(["loss"])
         if loss_times and sum(loss_times) > sum(times(["perturb", "perturb2"])):
@@ -543,16 +575,20 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
         "data": "synthetic",
         "config": {"workload": (f"{cfg.name}: {M} {cfg.dtype} params in one flat buffer, "
                                 f"n_pert={n}, eps={cfg.eps}, eta={cfg.eta}, " +
-                                ("probes applied inside the MFMA forward, both signs of eight "
-                                 "probes per launch (no passes over theta) + update"
+                                ("probes applied inside the MFMA forward, both signs of sixteen "
+                                 "probes per launch sequence (no passes over theta) + update"
                                  if mlp is not None else
+                                 "probes applied while theta is read, four per pass of the "
+                                 "quadratic loss (no passes that write theta) + update"
+                                 if schedule == "fused" else
                                  f"schedule {schedule} ({passes} passes + update" +
                                  (" carrying the last restore)" if schedule == "S2f"
                                   else ")")) +
                                 ", probes regenerated, losses " +
                                 ("synthetic" if cfg.loss == "synthetic" else cfg.loss)),
                    "params": M, "n_pert": n,
-                   "schedule": "fused forward" if mlp is not None else schedule,
+                   "schedule": ("fused forward" if mlp is not None or schedule == "fused"
+                                else schedule),
                    "passes_per_step": passes + 1},
         "hbm_gbps": step_bytes / T / 1e9,
         "hbm_frac_of_peak": step_bytes / T / 1e9 / PEAK_HBM_GBPS,
@@ -560,7 +596,8 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
                        "perturb2_avg": avg_ms("perturb2"), "update_avg": upd_ms,
                        "weights_avg": w_ms, "loss_avg": avg_ms("loss"),
                        "mlp_forward_avg": avg_ms("mlp"),
-                       "mlp_probes_avg": avg_ms("mlp_probes")},
+                       "mlp_probes_avg": avg_ms("mlp_probes"),
+                       "loss_probes_avg": avg_ms("loss_probes")},
         "roofline": roofline or {"kernel": f"k_perturb_chunks ({cfg.dtype}, probes regenerated; "
                                            f"every zo_perturb / zo_perturb2 pass)",
                                  "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,

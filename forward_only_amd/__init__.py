@@ -27,6 +27,7 @@ __all__ = [
     "Context", "ZOError", "zo_init", "zo_destroy", "zo_bits_stride", "zo_gen_probes",
     "zo_perturb", "zo_perturb2", "zo_probe_weights", "zo_probe_weights_ex", "zo_update",
     "zo_restore_update", "zo_nonfinite_count", "zo_reset_nonfinite", "zo_quad_loss",
+    "zo_quad_loss_probes",
     "zo_lowrank_quad_loss", "zo_mlp_workspace_bytes", "zo_mlp_loss", "zo_mlp_loss_perturbed",
     "zo_mlp_loss_pair", "zo_mlp_probes_workspace_bytes", "zo_mlp_loss_probes",
     "zo_mlp_loss_pair_noalloc", "zo_stream_rmw", "zo_tune_placement", "zo_set_slice_bytes",
@@ -255,6 +256,31 @@ def zo_quad_loss(ctx: Context, theta: torch.Tensor, a: torch.Tensor,
     return out
 
 
+def zo_quad_loss_probes(ctx: Context, theta: torch.Tensor, a: torch.Tensor, offset: int,
+                        step: int, probe0: int, n_probes: int, alpha: float,
+                        bits: torch.Tensor | None = None, out_plus: torch.Tensor | None = None,
+                        out_minus: torch.Tensor | None = None, stream=None):
+    """The quadratic loss at theta +/- alpha * z_i for probes probe0 .. probe0 + n_probes - 1,
+    each probe applied while theta is read (theta is not written); returns (out_plus,
+    out_minus), float64 tensors of n_probes.  bits: None or (n_probes, zo_bits_stride(theta))
+    rows."""
+    if a.numel() != theta.numel():
+        raise ValueError("a and theta must have the same length")
+    for name, o in (("out_plus", out_plus), ("out_minus", out_minus)):
+        if o is not None and o.numel() < n_probes:
+            raise ValueError(f"{name} is too small")
+    if out_plus is None:
+        out_plus = torch.empty(max(n_probes, 1), dtype=torch.float64, device="cuda")
+    if out_minus is None:
+        out_minus = torch.empty(max(n_probes, 1), dtype=torch.float64, device="cuda")
+    _lib.check(_lib.lib().zo_quad_loss_probes(
+        ctx.handle, _dev(theta, "theta"), _dtype_code(theta), _dev(a, "a", torch.float32),
+        offset, theta.numel(), step, probe0, n_probes, float(alpha),
+        _rows(bits, n_probes, theta.numel()), _dev(out_plus, "out_plus", torch.float64),
+        _dev(out_minus, "out_minus", torch.float64), _stream(stream)), "zo_quad_loss_probes")
+    return out_plus, out_minus
+
+
 def zo_lowrank_quad_loss(ctx: Context, theta: torch.Tensor, a: torch.Tensor, U: torch.Tensor,
                          out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """1/2 sum a_j theta_j^2 + 1/2 ||U theta||^2 (U: [r, n] float32) into a float64 tensor."""
@@ -352,7 +378,7 @@ def zo_mlp_loss_probes(ctx: Context, params: torch.Tensor, offset: int, step: in
                        out_plus: torch.Tensor | None = None,
                        out_minus: torch.Tensor | None = None, stream=None):
     """The MLP losses at params +/- alpha * z_i for probes probe0 .. probe0 + n_probes - 1
-    (up to eight per launch sequence), without writing params; returns (out_plus, out_minus),
+    (up to sixteen per launch sequence), without writing params; returns (out_plus, out_minus),
     float64 tensors of n_probes.  bits: None or (n_probes, zo_bits_stride(params)) rows."""
     batch, d_in = X.shape
     if params.numel() != d_hid * d_in + d_hid + d_out * d_hid + d_out:

@@ -8,6 +8,8 @@
 #include "zo_launch.hpp"
 
 static_assert(ZO_MAX_NPERT == zo::kMaxNpert, "one probe-count limit");
+static_assert(2 * zo::kQuadProbes <= zo::kLowRankMax + 1,
+              "the loss partials hold both signs of every probe of a fused pass");
 
 // Scratch of zo_mlp_loss_pair_noalloc: the partial logits and row losses of both signs,
 // ZO_NOALLOC_SCRATCH_BYTES per device, held until the process ends.  Host code never
@@ -284,6 +286,25 @@ zo_status zo_quad_loss(zo_ctx *c, const void *d_theta, zo_dtype dtype, const flo
     if (n > 0 && (!d_theta || !d_a || !aligned16(d_theta) || !aligned16(d_a))) return ZO_EINVAL;
     return from_hip(zo::launch_quad_loss(d_theta, dtype == ZO_BF16, d_a, n, c->d_partials, d_out,
                                          as_stream(stream)));
+}
+
+zo_status zo_quad_loss_probes(zo_ctx *c, const void *d_theta, zo_dtype dtype, const float *d_a,
+                              uint64_t offset, uint64_t n, uint32_t step, uint32_t probe0,
+                              uint32_t n_probes, float alpha, const uint8_t *d_bits,
+                              double *d_out_plus, double *d_out_minus, void *stream)
+{
+    if (!ctx_ok(c)) return ZO_EINVAL;
+    if (dtype != ZO_FP32 && dtype != ZO_BF16) return ZO_EINVAL;
+    if (n_probes == 0) return ZO_OK;
+    if (!d_out_plus || !d_out_minus) return ZO_EINVAL;
+    if (n_probes - 1 > UINT32_MAX - probe0) return ZO_EINVAL;   // probe indices wrap
+    if (!range_ok(offset, n)) return ZO_EINVAL;
+    if (n > 0 && (!d_theta || !d_a || !aligned16(d_theta) || !aligned16(d_a))) return ZO_EINVAL;
+    if (d_bits && !aligned16(d_bits)) return ZO_EINVAL;
+    return from_hip(zo::launch_quad_loss_probes(d_theta, dtype == ZO_BF16, d_a, offset, n,
+                                                key_of(c), step, probe0, n_probes, alpha,
+                                                n > 0 ? d_bits : nullptr, c->d_partials,
+                                                d_out_plus, d_out_minus, as_stream(stream)));
 }
 
 zo_status zo_lowrank_quad_loss(zo_ctx *c, const void *d_theta, zo_dtype dtype,

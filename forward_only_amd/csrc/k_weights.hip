@@ -82,6 +82,14 @@ hipError_t launch_zero_u32(uint32_t *p, uint32_t count, hipStream_t stream)
 // workgroup adds the partials the same way.  The partition depends only on n, so the
 // result is bit-reproducible.
 constexpr uint32_t kLossChunk = 2048;
+
+// One term of the sum, a_j t_j^2 added to acc: (a t) t with one rounding for the product
+// a t and one fused multiply-add, spelled out so that every kernel accumulating this sum
+// (the plain loss and the probes' losses below) rounds it identically.
+__device__ __forceinline__ double quad_term(double acc, float a, double t)
+{
+    return __builtin_fma((double)a * t, t, acc);
+}
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -181,15 +189,10 @@ __global__ __launch_bounds__(256) void k_quad_loss_partial(const void *__restric
 #pragma unroll
         for (int k = 0; k < 8; ++k)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const double t = (double)tv[k][q];
-                acc += (double)av[k][q] * t * t;
-            }
+            for (int q = 0; q < 4; ++q) acc = quad_term(acc, av[k][q], (double)tv[k][q]);
     }
-    for (uint64_t j = nchunks * kLossChunk + tid; j < n; j += G) {
-        const double t = theta1<kBF16>(theta, j);
-        acc += (double)a[j] * t * t;
-    }
+    for (uint64_t j = nchunks * kLossChunk + tid; j < n; j += G)
+        acc = quad_term(acc, a[j], theta1<kBF16>(theta, j));
     const double s = block_sum256(acc, red);
     if (threadIdx.x == 0) part[blockIdx.x] = s;
 }
@@ -203,6 +206,215 @@ __global__ __launch_bounds__(256) void k_sum_partials(const double *__restrict__
     for (uint32_t i = threadIdx.x; i < count; i += blockDim.x) acc += part[i];
     const double s = block_sum256(acc, red);
     if (threadIdx.x == 0) *out = scale * s;
+}
+
+// ---- the same loss at theta +/- alpha z_i of several probes, theta read once ------------
+// For each of up to kQuadProbes consecutive probes and both signs: the value an in-place
+// zo_perturb would store (one fp32 add of the signed alpha; for bf16, widen, add, round to
+// nearest even) squared into the sum -- theta itself is never written.  The partition into
+// chunks, each lane's order of terms, the tail and both reductions are those of
+// k_quad_loss_partial / k_sum_partials, per probe and sign, so each loss equals zo_perturb
+// followed by zo_quad_loss bit for bit.  Signs: per chunk (16 blocks of 128 params) the
+// wave's lanes produce the 16 x kQuadProbes blocks' bits once (one Philox call or one
+// 16-byte row read per lane) into an LDS slice laid out [block][word][probe], and each lane
+// reads, per group of 4 params, one 16-byte vector holding that word of every probe.
+template <bool kBF16>
+__device__ __forceinline__ void quad_terms4(double (&acc)[2 * kQuadProbes], const float (&x)[4],
+                                            const float (&av)[4], const uint32_t (&w)[kQuadProbes],
+                                            uint32_t sh, uint32_t abits)
+{
+#pragma unroll
+    for (uint32_t i = 0; i < kQuadProbes; ++i) {
+        const uint32_t nm = ~(w[i] >> sh);   // bit q: sign of the lane's param q
+        float d[4], vp[4], vm[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) d[q] = signed_alpha(nm, q, abits);   // +alpha if set
+        if constexpr (kBF16) {
+#pragma unroll
+            for (int q = 0; q < 4; q += 2) {
+                const uint32_t p = pack_bf16x2(x[q] + d[q], x[q + 1] + d[q + 1]);
+                const uint32_t m = pack_bf16x2(x[q] + (-d[q]), x[q + 1] + (-d[q + 1]));
+                vp[q] = bf16lo_to_f32(p);
+                vp[q + 1] = bf16hi_to_f32(p);
+                vm[q] = bf16lo_to_f32(m);
+                vm[q + 1] = bf16hi_to_f32(m);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                vp[q] = x[q] + d[q];
+                vm[q] = x[q] + (-d[q]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc[2 * i] = quad_term(acc[2 * i], av[q], (double)vp[q]);
+            acc[2 * i + 1] = quad_term(acc[2 * i + 1], av[q], (double)vm[q]);
+        }
+    }
+}
+
+template <bool kBF16, bool kBits>
+__global__ __launch_bounds__(256) void k_quad_probes_partial(
+    const void *__restrict__ theta, const float *__restrict__ a, uint64_t n, uint64_t blk0,
+    uint32_t step, uint32_t probe0, uint32_t nvalid, uint32_t k0, uint32_t k1, uint32_t abits,
+    const uint8_t *__restrict__ bits, uint64_t stride, double *__restrict__ part)
+{
+    __shared__ double red[4];
+    __shared__ __attribute__((aligned(16))) uint32_t xch[4][16 * 4 * kQuadProbes];
+    double acc[2 * kQuadProbes];
+#pragma unroll
+    for (uint32_t s = 0; s < 2 * kQuadProbes; ++s) acc[s] = 0.0;
+    const uint64_t G = (uint64_t)gridDim.x * blockDim.x;
+    const uint64_t tid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint32_t lane = threadIdx.x & 63u;
+    uint32_t *wx = xch[threadIdx.x >> 6];
+    const uint64_t nwaves = (uint64_t)gridDim.x * (blockDim.x / 64u);
+    const uint64_t nchunks = n / kLossChunk;
+    const uint32_t sh = 4u * (lane & 7u);            // the lane's nibble in its sign word
+    const uint32_t wsel = (lane & 31u) >> 3;          // which word of the block
+    for (uint64_t c = tid / 64u; c < nchunks; c += nwaves) {
+        const uint64_t p0 = c * kLossChunk + 4u * lane;   // + 256 k
+        const f32x4_t *ap = reinterpret_cast<const f32x4_t *>(a + p0);
+        f32x4_t av[8];
+        float xv[8][4];
+        if constexpr (kBF16) {
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            const u32x2_t *tp =
+                reinterpret_cast<const u32x2_t *>(static_cast<const uint16_t *>(theta) + p0);
+            u32x2_t w[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) w[k] = __builtin_nontemporal_load(tp + 64 * k);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) av[k] = __builtin_nontemporal_load(ap + 64 * k);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                xv[k][0] = bf16lo_to_f32(w[k][0]);
+                xv[k][1] = bf16hi_to_f32(w[k][0]);
+                xv[k][2] = bf16lo_to_f32(w[k][1]);
+                xv[k][3] = bf16hi_to_f32(w[k][1]);
+            }
+        } else {
+            const f32x4_t *tp = reinterpret_cast<const f32x4_t *>(static_cast<const float *>(theta) + p0);
+            f32x4_t x[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) x[k] = __builtin_nontemporal_load(tp + 64 * k);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) av[k] = __builtin_nontemporal_load(ap + 64 * k);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) xv[k][q] = x[k][q];
+        }
+        {   // the chunk's 16 blocks x kQuadProbes probes of sign bits: one per lane
+            const uint32_t b = lane & 15u, i = lane >> 4;
+            const uint64_t blk = c * (kLossChunk / kBlockParams) + b;   // local block
+            uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+            if (i < nvalid) {
+                if constexpr (kBits) {
+                    const u32x4_t r = *reinterpret_cast<const u32x4_t *>(bits + (uint64_t)i * stride + blk * 16u);
+                    w0 = r[0]; w1 = r[1]; w2 = r[2]; w3 = r[3];
+                } else {
+                    const U32x4 r = probe_block_bits(blk0 + blk, probe0 + i, step, k0, k1);
+                    w0 = r.x; w1 = r.y; w2 = r.z; w3 = r.w;
+                }
+            }
+            wave_lds_sync();   // the previous chunk's reads precede these writes
+            wx[(b * 4u + 0u) * kQuadProbes + i] = w0;
+            wx[(b * 4u + 1u) * kQuadProbes + i] = w1;
+            wx[(b * 4u + 2u) * kQuadProbes + i] = w2;
+            wx[(b * 4u + 3u) * kQuadProbes + i] = w3;
+            wave_lds_sync();
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t blk = 2u * (uint32_t)k + (lane >> 5);   // block of params 256k + 4l
+            const u32x4_t wq = *reinterpret_cast<const u32x4_t *>(wx + (blk * 4u + wsel) * kQuadProbes);
+            const uint32_t w[kQuadProbes] = {wq[0], wq[1], wq[2], wq[3]};
+            const float x[4] = {xv[k][0], xv[k][1], xv[k][2], xv[k][3]};
+            const float aa[4] = {av[k][0], av[k][1], av[k][2], av[k][3]};
+            quad_terms4<kBF16>(acc, x, aa, w, sh, abits);
+        }
+    }
+    for (uint64_t j = nchunks * kLossChunk + tid; j < n; j += G) {   // ragged end
+        const float xj = (float)theta1<kBF16>(theta, j);
+#pragma unroll
+        for (uint32_t i = 0; i < kQuadProbes; ++i) {
+            uint32_t bit = 0;
+            if (i < nvalid) {
+                if constexpr (kBits) {
+                    bit = (bits[(uint64_t)i * stride + (j >> 3)] >> (j & 7u)) & 1u;
+                } else {
+                    const U32x4 r = probe_block_bits(blk0 + j / kBlockParams, probe0 + i, step, k0, k1);
+                    const uint32_t wsl = (uint32_t)(j >> 5) & 3u;
+                    const uint32_t word = wsl == 0 ? r.x : wsl == 1 ? r.y : wsl == 2 ? r.z : r.w;
+                    bit = (word >> (j & 31u)) & 1u;
+                }
+            }
+            const float d = signed_alpha(~bit, 0, abits);
+            float vp, vm;
+            if constexpr (kBF16) {
+                const uint32_t pm = pack_bf16x2(xj + d, xj + (-d));
+                vp = bf16lo_to_f32(pm);
+                vm = bf16hi_to_f32(pm);
+            } else {
+                vp = xj + d;
+                vm = xj + (-d);
+            }
+            acc[2 * i] = quad_term(acc[2 * i], a[j], (double)vp);
+            acc[2 * i + 1] = quad_term(acc[2 * i + 1], a[j], (double)vm);
+        }
+    }
+#pragma unroll
+    for (uint32_t s = 0; s < 2 * kQuadProbes; ++s) {
+        const double v = block_sum256(acc[s], red);
+        if (threadIdx.x == 0) part[(uint64_t)s * kLossPartials + blockIdx.x] = v;
+    }
+}
+
+// Slot s of the fused pass (probe s / 2, sign s % 2): the partials summed exactly as
+// k_sum_partials sums them, into out_plus / out_minus.
+__global__ __launch_bounds__(256) void k_sum_partials_slots(const double *__restrict__ part,
+                                                            uint32_t count, double scale,
+                                                            double *__restrict__ out_plus,
+                                                            double *__restrict__ out_minus)
+{
+    __shared__ double red[4];
+    const uint32_t s = blockIdx.x;
+    part += (uint64_t)s * count;
+    double acc = 0.0;
+    for (uint32_t i = threadIdx.x; i < count; i += blockDim.x) acc += part[i];
+    const double v = block_sum256(acc, red);
+    if (threadIdx.x == 0) ((s & 1u) ? out_minus : out_plus)[s >> 1] = scale * v;
+}
+
+hipError_t launch_quad_loss_probes(const void *theta, bool bf16, const float *a, uint64_t offset,
+                                   uint64_t n, Key key, uint32_t step, uint32_t probe0,
+                                   uint32_t nprobes, float alpha, const uint8_t *bits,
+                                   double *partials, double *out_plus, double *out_minus,
+                                   hipStream_t stream)
+{
+    const uint64_t stride = (n + kBlockParams - 1) / kBlockParams * 16u;
+    const uint32_t abits = __builtin_bit_cast(uint32_t, alpha);
+    for (uint32_t done = 0; done < nprobes; done += kQuadProbes) {
+        const uint32_t nvalid = nprobes - done < kQuadProbes ? nprobes - done : kQuadProbes;
+        const uint8_t *b = bits ? bits + (uint64_t)done * stride : nullptr;
+#define ZO_QP(BF, BI)                                                                         \
+    hipLaunchKernelGGL((k_quad_probes_partial<BF, BI>), dim3(kLossPartials), dim3(256), 0,     \
+                       stream, theta, a, n, offset / kBlockParams, step, probe0 + done, nvalid, \
+                       key.k0, key.k1, abits, b, stride, partials)
+        if (bf16) {
+            if (b) ZO_QP(true, true); else ZO_QP(true, false);
+        } else {
+            if (b) ZO_QP(false, true); else ZO_QP(false, false);
+        }
+#undef ZO_QP
+        hipLaunchKernelGGL(k_sum_partials_slots, dim3(2 * nvalid), dim3(256), 0, stream, partials,
+                           kLossPartials, 0.5, out_plus + done, out_minus + done);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_quad_loss(const void *theta, bool bf16, const float *a, uint64_t n,

@@ -76,6 +76,15 @@ hipError_t launch_zero_u32(uint32_t *p, uint32_t count, hipStream_t stream);
 constexpr uint32_t kLossPartials = 1024;
 hipError_t launch_quad_loss(const void *theta, bool bf16, const float *a, uint64_t n,
                             double *partials, double *out, hipStream_t stream);
+constexpr uint32_t kQuadProbes = 4;   // probes per pass of the fused quadratic losses
+// The same loss at theta +/- alpha z_i for n_probes consecutive probes from probe0, theta
+// read once per kQuadProbes probes and never written; each loss bit-equal to zo_perturb
+// followed by launch_quad_loss.  `partials` as for launch_quad_loss (2 kQuadProbes slots).
+hipError_t launch_quad_loss_probes(const void *theta, bool bf16, const float *a, uint64_t offset,
+                                   uint64_t n, Key key, uint32_t step, uint32_t probe0,
+                                   uint32_t nprobes, float alpha, const uint8_t *bits,
+                                   double *partials, double *out_plus, double *out_minus,
+                                   hipStream_t stream);
 
 // 1/2 sum a_j theta_j^2 + 1/2 ||U theta||^2, U row-major [r][n], r <= kLowRankMax;
 // `partials` holds kLossPartials * (kLowRankMax + 1) doubles.

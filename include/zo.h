@@ -222,6 +222,29 @@ zo_status zo_reset_nonfinite(zo_ctx *ctx, void *stream);
 zo_status zo_quad_loss(zo_ctx *ctx, const void *d_theta, zo_dtype dtype, const float *d_a,
                        uint64_t n, double *d_out, void *stream);
 
+/* Both losses of n_probes consecutive probes of the same quadratic with each probe applied
+ * while theta is read (the perturbation-fused forward of the flowchart's "N forward passes"
+ * box for this workload, "Pretraining Transformers Without Backprop: What Two Zero-Order
+ * Papers Actually Measure"; the central difference of "How 1.5-SPSA Works" on "Stanford's
+ * 1.5-SPSA Trains OPT-30B Without Backpropagation"): d_out_plus[i] = L(theta + alpha z_i) and
+ * d_out_minus[i] = L(theta - alpha z_i), i = probe0 + 0 .. n_probes-1, where each perturbed
+ * element is the value zo_perturb(+/-alpha) would store from the given theta (one fp32 add;
+ * bf16: widen, add, round to nearest even).  theta is read once per four probes and never
+ * written; each loss equals zo_perturb followed by zo_quad_loss bit for bit (same partition,
+ * order of terms and reductions).  Layouts as zo_quad_loss; offset as zo_perturb (a multiple
+ * of 128: the global index of theta[0]); d_bits: NULL to regenerate the signs, else
+ * n_probes packed rows of zo_bits_stride(n) bytes each (row i for probe probe0 + i), 16-byte
+ * aligned; d_out_plus, d_out_minus: device, n_probes doubles each.  Uses the context's loss
+ * partials, so calls on one context are ordered by their streams.  Errors (ZO_EINVAL): as
+ * zo_quad_loss, offset % 128 != 0 or range overflow, probe indices wrapping past 2^32,
+ * misaligned d_bits, NULL outputs (with n_probes > 0).  n_probes == 0 is a no-op; n == 0
+ * writes zeros. */
+zo_status zo_quad_loss_probes(zo_ctx *ctx, const void *d_theta, zo_dtype dtype,
+                              const float *d_a, uint64_t offset, uint64_t n, uint32_t step,
+                              uint32_t probe0, uint32_t n_probes, float alpha,
+                              const uint8_t *d_bits, double *d_out_plus, double *d_out_minus,
+                              void *stream);
+
 /* Low-rank-plus-diagonal quadratic loss L = 1/2 sum_j a_j theta_j^2 + 1/2 ||U theta||^2,
  * fp64 accumulation, deterministic.  A synthetic model whose curvature along a probe,
  * sum_j a_j + ||U z||^2, differs from probe to probe -- the landscape on which the clean-pass
