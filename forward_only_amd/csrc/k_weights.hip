@@ -83,12 +83,17 @@ hipError_t launch_zero_u32(uint32_t *p, uint32_t count, hipStream_t stream)
 // result is bit-reproducible.
 constexpr uint32_t kLossChunk = 2048;
 
-// One term of the sum, a_j t_j^2 added to acc: (a t) t with one rounding for the product
-// a t and one fused multiply-add, spelled out so that every kernel accumulating this sum
-// (the plain loss and the probes' losses below) rounds it identically.
+// One term of the sum, a_j t_j^2 added to acc with a single rounding: t is a widened fp32
+// value, so t^2 (at most 48 significant bits) is exact in fp64 and fma(a, t^2, acc) rounds
+// the exact a t^2 + acc once.  Spelled out so that every kernel accumulating this sum (the
+// plain loss and the probes' losses below) rounds it identically.
+__device__ __forceinline__ double quad_term_sq(double acc, double a, double t2)
+{
+    return __builtin_fma(a, t2, acc);
+}
 __device__ __forceinline__ double quad_term(double acc, float a, double t)
 {
-    return __builtin_fma((double)a * t, t, acc);
+    return quad_term_sq(acc, (double)a, t * t);
 }
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -218,38 +223,42 @@ __global__ __launch_bounds__(256) void k_sum_partials(const double *__restrict__
 // wave's lanes produce the 16 x kQuadProbes blocks' bits once (one Philox call or one
 // 16-byte row read per lane) into an LDS slice laid out [block][word][probe], and each lane
 // reads, per group of 4 params, one 16-byte vector holding that word of every probe.
+// The four params' terms for every probe and sign.  A perturbed value is one of two
+// candidates, rnd(x + alpha) and rnd(x - alpha) (what zo_perturb stores for a set and for a
+// clear sign bit under +alpha, and the other way round under -alpha), so both are formed
+// and squared once per param and each probe's sign bit picks between them.
 template <bool kBF16>
 __device__ __forceinline__ void quad_terms4(double (&acc)[2 * kQuadProbes], const float (&x)[4],
                                             const float (&av)[4], const uint32_t (&w)[kQuadProbes],
-                                            uint32_t sh, uint32_t abits)
+                                            uint32_t sh, float alpha)
 {
+    float xa[4], xb[4];
+    if constexpr (kBF16) {
 #pragma unroll
-    for (uint32_t i = 0; i < kQuadProbes; ++i) {
-        const uint32_t nm = ~(w[i] >> sh);   // bit q: sign of the lane's param q
-        float d[4], vp[4], vm[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) d[q] = signed_alpha(nm, q, abits);   // +alpha if set
-        if constexpr (kBF16) {
-#pragma unroll
-            for (int q = 0; q < 4; q += 2) {
-                const uint32_t p = pack_bf16x2(x[q] + d[q], x[q + 1] + d[q + 1]);
-                const uint32_t m = pack_bf16x2(x[q] + (-d[q]), x[q + 1] + (-d[q + 1]));
-                vp[q] = bf16lo_to_f32(p);
-                vp[q + 1] = bf16hi_to_f32(p);
-                vm[q] = bf16lo_to_f32(m);
-                vm[q + 1] = bf16hi_to_f32(m);
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                vp[q] = x[q] + d[q];
-                vm[q] = x[q] + (-d[q]);
-            }
+        for (int q = 0; q < 4; q += 2) {
+            const uint32_t pa = pack_bf16x2(x[q] + alpha, x[q + 1] + alpha);
+            const uint32_t pb = pack_bf16x2(x[q] + (-alpha), x[q + 1] + (-alpha));
+            xa[q] = bf16lo_to_f32(pa);
+            xa[q + 1] = bf16hi_to_f32(pa);
+            xb[q] = bf16lo_to_f32(pb);
+            xb[q + 1] = bf16hi_to_f32(pb);
         }
+    } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            acc[2 * i] = quad_term(acc[2 * i], av[q], (double)vp[q]);
-            acc[2 * i + 1] = quad_term(acc[2 * i + 1], av[q], (double)vm[q]);
+            xa[q] = x[q] + alpha;
+            xb[q] = x[q] + (-alpha);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const double ta = (double)xa[q], tb = (double)xb[q];
+        const double sa = ta * ta, sb = tb * tb, ad = (double)av[q];
+#pragma unroll
+        for (uint32_t i = 0; i < kQuadProbes; ++i) {
+            const bool set = (w[i] >> (sh + (uint32_t)q)) & 1u;
+            acc[2 * i] = quad_term_sq(acc[2 * i], ad, set ? sa : sb);
+            acc[2 * i + 1] = quad_term_sq(acc[2 * i + 1], ad, set ? sb : sa);
         }
     }
 }
@@ -257,7 +266,7 @@ __device__ __forceinline__ void quad_terms4(double (&acc)[2 * kQuadProbes], cons
 template <bool kBF16, bool kBits>
 __global__ __launch_bounds__(256) void k_quad_probes_partial(
     const void *__restrict__ theta, const float *__restrict__ a, uint64_t n, uint64_t blk0,
-    uint32_t step, uint32_t probe0, uint32_t nvalid, uint32_t k0, uint32_t k1, uint32_t abits,
+    uint32_t step, uint32_t probe0, uint32_t nvalid, uint32_t k0, uint32_t k1, float alpha,
     const uint8_t *__restrict__ bits, uint64_t stride, double *__restrict__ part)
 {
     __shared__ double red[4];
@@ -333,7 +342,7 @@ __global__ __launch_bounds__(256) void k_quad_probes_partial(
             const uint32_t w[kQuadProbes] = {wq[0], wq[1], wq[2], wq[3]};
             const float x[4] = {xv[k][0], xv[k][1], xv[k][2], xv[k][3]};
             const float aa[4] = {av[k][0], av[k][1], av[k][2], av[k][3]};
-            quad_terms4<kBF16>(acc, x, aa, w, sh, abits);
+            quad_terms4<kBF16>(acc, x, aa, w, sh, alpha);
         }
     }
     for (uint64_t j = nchunks * kLossChunk + tid; j < n; j += G) {   // ragged end
@@ -351,18 +360,17 @@ __global__ __launch_bounds__(256) void k_quad_probes_partial(
                     bit = (word >> (j & 31u)) & 1u;
                 }
             }
-            const float d = signed_alpha(~bit, 0, abits);
-            float vp, vm;
+            float xa, xb;
             if constexpr (kBF16) {
-                const uint32_t pm = pack_bf16x2(xj + d, xj + (-d));
-                vp = bf16lo_to_f32(pm);
-                vm = bf16hi_to_f32(pm);
+                const uint32_t pab = pack_bf16x2(xj + alpha, xj + (-alpha));
+                xa = bf16lo_to_f32(pab);
+                xb = bf16hi_to_f32(pab);
             } else {
-                vp = xj + d;
-                vm = xj + (-d);
+                xa = xj + alpha;
+                xb = xj + (-alpha);
             }
-            acc[2 * i] = quad_term(acc[2 * i], a[j], (double)vp);
-            acc[2 * i + 1] = quad_term(acc[2 * i + 1], a[j], (double)vm);
+            acc[2 * i] = quad_term(acc[2 * i], a[j], (double)(bit ? xa : xb));
+            acc[2 * i + 1] = quad_term(acc[2 * i + 1], a[j], (double)(bit ? xb : xa));
         }
     }
 #pragma unroll
@@ -395,14 +403,13 @@ hipError_t launch_quad_loss_probes(const void *theta, bool bf16, const float *a,
                                    hipStream_t stream)
 {
     const uint64_t stride = (n + kBlockParams - 1) / kBlockParams * 16u;
-    const uint32_t abits = __builtin_bit_cast(uint32_t, alpha);
     for (uint32_t done = 0; done < nprobes; done += kQuadProbes) {
         const uint32_t nvalid = nprobes - done < kQuadProbes ? nprobes - done : kQuadProbes;
         const uint8_t *b = bits ? bits + (uint64_t)done * stride : nullptr;
 #define ZO_QP(BF, BI)                                                                         \
     hipLaunchKernelGGL((k_quad_probes_partial<BF, BI>), dim3(kLossPartials), dim3(256), 0,     \
                        stream, theta, a, n, offset / kBlockParams, step, probe0 + done, nvalid, \
-                       key.k0, key.k1, abits, b, stride, partials)
+                       key.k0, key.k1, alpha, b, stride, partials)
         if (bf16) {
             if (b) ZO_QP(true, true); else ZO_QP(true, false);
         } else {
