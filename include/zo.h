@@ -34,8 +34,8 @@
  *    valid empty call that launches nothing and returns ZO_OK.
  *  - Threading: one host thread uses a context at a time.  Calls on different streams
  *    that touch the same parameter buffer race, as any two kernels would.  The quadratic
- *    loss calls (zo_quad_loss, zo_lowrank_quad_loss) stage partial sums in a scratch
- *    buffer owned by the context: two of them on one context must not overlap on
+ *    loss calls (zo_quad_loss, zo_quad_loss_probes, zo_lowrank_quad_loss) stage partial
+ *    sums in a scratch buffer owned by the context: two of them on one context must not overlap on
  *    different streams (the non-finite counter is updated atomically and may be shared).
  *  - Devices: a context belongs to the device that was current at zo_init; every call
  *    on it must be made with that device current, or it returns ZO_EINVAL.
