@@ -32,6 +32,7 @@ void ora_update_f32(float *th, uint64_t n, uint64_t offset, uint64_t seed, uint3
 void ora_update_bf16(uint16_t *th, uint64_t n, uint64_t offset, uint64_t seed, uint32_t step,
                      const float *c, uint32_t npert, float eta, const uint8_t *bits);
 float ora_bf16_to_f32(uint16_t h);
+double ora_quad_loss_f32(const float *th, const float *a, uint64_t n);
 uint16_t ora_f32_to_bf16(float f);
 
 #define FAIL(...)                                     \
@@ -190,7 +191,51 @@ int main(void)
         HIPCHK(hipFree(dc));
     }
 
-    /* 6. documented argument errors (nothing launched) */
+    /* 6. the quadratic loss at theta +/- alpha z_i of three probes, theta read once and not
+     *    written: each loss within the fp64 summation bound of the oracle's perturb + loss */
+    {
+        const uint64_t n = 30011, offset = 256;
+        const uint32_t np = 3, step = 4, probe0 = 6;
+        const float alpha = 0x1p-10f;
+        float *h = malloc(n * 4), *a = malloc(n * 4), *w = malloc(n * 4), *g = malloc(n * 4);
+        float *dt = NULL, *da = NULL;
+        double *dp = NULL, *dm = NULL, lp[3], lm[3];
+        for (uint64_t i = 0; i < n; ++i) {
+            h[i] = (float)((sm_uniform() - 0.5) * 2.0);
+            a[i] = (float)(0.1 + sm_uniform());
+        }
+        HIPCHK(hipMalloc((void **)&dt, n * 4));
+        HIPCHK(hipMalloc((void **)&da, n * 4));
+        HIPCHK(hipMalloc((void **)&dp, np * 8));
+        HIPCHK(hipMalloc((void **)&dm, np * 8));
+        HIPCHK(hipMemcpy(dt, h, n * 4, hipMemcpyHostToDevice));
+        HIPCHK(hipMemcpy(da, a, n * 4, hipMemcpyHostToDevice));
+        ZOCHK(zo_quad_loss_probes(ctx, dt, ZO_FP32, da, offset, n, step, probe0, np, alpha, NULL,
+                                  dp, dm, NULL));
+        HIPCHK(hipMemcpy(lp, dp, np * 8, hipMemcpyDeviceToHost));
+        HIPCHK(hipMemcpy(lm, dm, np * 8, hipMemcpyDeviceToHost));
+        HIPCHK(hipMemcpy(g, dt, n * 4, hipMemcpyDeviceToHost));
+        if (memcmp(g, h, n * 4) != 0) FAIL("fused losses wrote theta");
+        for (uint32_t i = 0; i < np; ++i) {
+            for (int sgn = 0; sgn < 2; ++sgn) {
+                memcpy(w, h, n * 4);
+                ora_perturb_f32(w, n, offset, seed, step, probe0 + i, sgn ? -alpha : alpha, NULL);
+                const double ref = ora_quad_loss_f32(w, a, n), got = sgn ? lm[i] : lp[i];
+                if (fabs(got - ref) > 4.0 * (double)n * 0x1p-53 * fabs(ref))
+                    FAIL("fused quadratic loss");
+            }
+        }
+        HIPCHK(hipFree(dt));
+        HIPCHK(hipFree(da));
+        HIPCHK(hipFree(dp));
+        HIPCHK(hipFree(dm));
+        free(h);
+        free(a);
+        free(w);
+        free(g);
+    }
+
+    /* 7. documented argument errors (nothing launched) */
     {
         float *d = NULL;
         HIPCHK(hipMalloc((void **)&d, 1024 * 4));
