@@ -70,14 +70,18 @@ __device__ __forceinline__ float with_sign(float v, uint32_t bit, float alpha)
     return v + (bit ? alpha : -alpha);
 }
 
+// The sign bit of parameter j under probe p.probe + i.
+__device__ __forceinline__ uint32_t param_bit(const PertArgs &p, uint32_t i, uint64_t j)
+{
+    return (quad_bits(p, i, j & ~(uint64_t)3) >> (j & 3)) & 1u;
+}
+
 // Parameter j as the forward of probe p.probe + i with step `alpha` reads it.
 __device__ __forceinline__ float param(const float *params, uint64_t j, const PertArgs &p,
                                        uint32_t i, float alpha, bool pert)
 {
     const float v = params[j];
-    if (!pert) return v;
-    const uint32_t b = quad_bits(p, i, j & ~(uint64_t)3) >> (j & 3);
-    return with_sign(v, b & 1u, alpha);
+    return pert ? with_sign(v, param_bit(p, i, j), alpha) : v;
 }
 
 __device__ __forceinline__ float gelu_exact(float x)
@@ -169,17 +173,23 @@ __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
         } else {
             uint32_t q[kNB];
             bits4(j, q);
+            const uint32_t abits = __builtin_bit_cast(uint32_t, pa.alpha);
 #pragma unroll
             for (int i = 0; i < kNP; ++i) {
-                f32x4_t bp;
+                // d = +alpha where the bit is set, -alpha where clear (alpha's sign bit
+                // flipped): w + d is with_sign(w, bit, alpha), w + (-d) the -alpha value
+                const uint32_t nq = ~q[i];
+                f32x4_t d, bp;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) bp[t] = with_sign(b[t], (q[i] >> t) & 1u, pa.alpha);
+                for (int t = 0; t < 4; ++t) {
+                    d[t] = signed_alpha(nq, t, abits);
+                    bp[t] = b[t] + d[t];
+                }
                 mfma4(acc[kPer * i], a, bp);
                 if constexpr (kPair) {
                     f32x4_t bm;
 #pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        bm[t] = with_sign(b[t], (q[i] >> t) & 1u, -pa.alpha);
+                    for (int t = 0; t < 4; ++t) bm[t] = b[t] + (-d[t]);
                     mfma4(acc[kPer * i + 1], a, bm);
                 }
             }
@@ -233,18 +243,35 @@ __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
     const uint64_t pset = (uint64_t)n_tiles * batch * d_out;   // one slot's partial logits
     partial += (uint64_t)blockIdx.y * (kNP > 0 ? kNP * (kPair ? 2 : 1) : 1) * pset;
     const uint32_t n = n0 + li;
+    const float b1v = params[b1_at + n];
+    uint32_t sb1[kNB], sw2[kNB];   // per probe: the sign bits of b1[n] and of W2[.][n]
 #pragma unroll
     for (int slot = 0; slot < kNS; ++slot) {
         const uint32_t pi = (uint32_t)(slot / kPer);
         const float alpha = (slot % kPer) ? -pa.alpha : pa.alpha;
         const f32x4_t &c = acc[slot];
         double *out = partial + (uint64_t)slot * pset;
-        const float bias = param(params, b1_at + n, pa, pi, alpha, kPert);
+        // the sign bits of b1[n] and of W2[o][n] (bit o), once per probe for both signs
+        uint32_t b1bit = 0, w2bits = 0;
+        if constexpr (kPert) {
+            if (slot % kPer == 0) {
+                b1bit = param_bit(pa, pi, b1_at + n);
+                for (uint32_t o = 0; o < d_out; ++o)
+                    w2bits |= param_bit(pa, pi, w2_at + (uint64_t)o * d_hid + n) << o;
+                sb1[pi] = b1bit;
+                sw2[pi] = w2bits;
+            } else {
+                b1bit = sb1[pi];
+                w2bits = sw2[pi];
+            }
+        }
+        const float bias = kPert ? with_sign(b1v, b1bit, alpha) : b1v;
         float g[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) g[r] = gelu_exact(c[r] + bias);
         for (uint32_t o = 0; o < d_out; ++o) {
-            const float w2 = param(params, w2_at + (uint64_t)o * d_hid + n, pa, pi, alpha, kPert);
+            const float w2v = params[w2_at + (uint64_t)o * d_hid + n];
+            const float w2 = kPert ? with_sign(w2v, (w2bits >> o) & 1u, alpha) : w2v;
             float p[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) p[r] = g[r] * w2;
