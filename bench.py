@@ -536,7 +536,7 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
         mlp_ms = avg_ms("mlp_probes")
         achieved = 2.0 * n * mlp["flop"] / (mlp_ms * 1e-3) / 1e12
         roofline = {"kernel": "k_mlp_tiles (MFMA fp32 GEMM of the MLP forward, both signs of "
-                              "sixteen probes per launch sequence; time of the whole "
+                              "up to 64 probes per launch sequence; time of the whole "
                               "zo_mlp_loss_probes call: tiles, row and mean kernels of all "
                               "n_pert probes)",
                     "bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS,
@@ -575,7 +575,7 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
         "data": "synthetic",
         "config": {"workload": (f"{cfg.name}: {M} {cfg.dtype} params in one flat buffer, "
                                 f"n_pert={n}, eps={cfg.eps}, eta={cfg.eta}, " +
-                                ("probes applied inside the MFMA forward, both signs of sixteen "
+                                ("probes applied inside the MFMA forward, both signs of up to 64 "
                                  "probes per launch sequence (no passes over theta) + update"
                                  if mlp is not None else
                                  "probes applied while theta is read, four per pass of the "

@@ -378,7 +378,7 @@ def zo_mlp_loss_probes(ctx: Context, params: torch.Tensor, offset: int, step: in
                        out_plus: torch.Tensor | None = None,
                        out_minus: torch.Tensor | None = None, stream=None):
     """The MLP losses at params +/- alpha * z_i for probes probe0 .. probe0 + n_probes - 1
-    (up to sixteen per launch sequence), without writing params; returns (out_plus, out_minus),
+    (up to 64 per launch sequence), without writing params; returns (out_plus, out_minus),
     float64 tensors of n_probes.  bits: None or (n_probes, zo_bits_stride(params)) rows."""
     batch, d_in = X.shape
     if params.numel() != d_hid * d_in + d_hid + d_out * d_hid + d_out:

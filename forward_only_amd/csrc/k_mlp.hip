@@ -4,13 +4,15 @@
 //   H = GELU(X W1^T + b1),  logits = H W2^T + b2,  loss = mean_b (logsumexp - logit[label]).
 // Flat parameters: W1 [d_hid x d_in] row-major, b1 [d_hid], W2 [d_out x d_hid], b2 [d_out].
 //
-// Kernel 1 (k_mlp_tiles): one wave per 16x16 tile of H, v_mfma_f32_16x16x4f32 over K =
-//   d_in (fp32 in, fp32 accumulate).  Lane l holds A = X[m0 + l%16][k], B = W1[n0 + l%16][k]
-//   for k = k0 + 4*(l/16) + t, t = 0..3 (one float4 load per operand per 16 k; the order
-//   of k inside an MFMA is free as long as both operands agree).  The accumulator gives
-//   lane l rows m0 + 4*(l/16) + r (r = 0..3) of column n0 + l%16.  Epilogue: + b1, exact
-//   GELU (erf), times W2[o][n], summed over the tile's 16 columns with a fixed butterfly,
-//   written as fp64 partial logits at [row][output][tile column block].
+// Kernel 1 (k_mlp_tiles): one wave per kT x kT tile of H (kT = 32 with v_mfma_f32_32x32x2f32
+//   where the batch and d_hid allow, else 16 with v_mfma_f32_16x16x4f32) over K = d_in (fp32
+//   in, fp32 accumulate).  Lane l holds A = X[m0 + l%kT][k], B = W1[n0 + l%kT][k] for
+//   k = k0 + (kT/4)*(l/kT) + e, e < kT/4 (one or two float4 loads per operand per 16 k;
+//   the order of k inside an MFMA is free as long as both operands agree).  The
+//   accumulator gives lane l rows of column n0 + l%kT.  Epilogue: + b1, exact GELU (erf),
+//   times W2[o][n], summed over the tile's kT columns with a fixed reduce-scatter tree,
+//   written as fp64 partial logits at [row][output][tile column block].  The 32-wide form
+//   does twice the MFMA work per operand element a lane loads and perturbs.
 //   Workgroups are remapped so that the tiles run by one XCD (workgroup id mod 8) are a
 //   contiguous range of column blocks: each XCD's L2 then holds 1/8 of W1 plus X.
 // Kernel 2 (k_mlp_rows): one wave per row; lane l sums the partial logits of column
@@ -41,6 +43,7 @@
 namespace zo {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // Sign source for the fused variant: Philox of (global block, probe, step) or stored rows.
 struct PertArgs {
@@ -89,39 +92,81 @@ __device__ __forceinline__ float gelu_exact(float x)
     return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
 }
 
+// Tile shapes: one wave computes a kT x kT tile of H with v_mfma_f32_16x16x4f32 (kT = 16) or
+// v_mfma_f32_32x32x2f32 (kT = 32).  Per 16-k group lane l loads kT/4 consecutive k of its X
+// row and its W1 row (k = k0 + (kT/4)*(l/kT) + e), and MFMA e takes element e from every
+// lane, so each k of the group enters exactly one MFMA.  The accumulator gives lane l the
+// kT*kT/64 entries D[8*(r/4) + 4*(l/kT) + r%4][l%kT], r = 0 .. kT*kT/64 - 1 (for kT = 16
+// that is rows 4*(l/16) + r).
+template <int kT> struct TileAcc;
+template <> struct TileAcc<16> { typedef f32x4_t type; };
+template <> struct TileAcc<32> { typedef f32x16_t type; };
+
+// Sum of v[.] over the kT lanes of a column group (equal lane / kT) by a fixed tree that
+// scatters the rows while it adds: each halving stage passes the half of the values this
+// lane does not keep to its partner at lane distance s and adds the partner's copy of the
+// half it keeps; once one value is left the remaining stages add whole.  Lanes with
+// li % (kT / kOut) == 0 end with row index li / (kT / kOut) in v[0].
+template <int kT, int kOut, int kS = kT / 2, int kCnt = kOut>
+__device__ __forceinline__ void sum_columns(float (&v)[kOut], uint32_t li)
+{
+    if constexpr (kS >= 1) {
+        if constexpr (kCnt > 1) {
+            constexpr int h = kCnt / 2;
+            const bool up = (li & (uint32_t)kS) != 0;
+#pragma unroll
+            for (int r = 0; r < h; ++r) {
+                const float send = up ? v[r] : v[r + h];
+                const float keep = up ? v[r + h] : v[r];
+                v[r] = keep + __shfl_xor(send, kS, kT);
+            }
+            sum_columns<kT, kOut, kS / 2, h>(v, li);
+        } else {
+            v[0] = v[0] + __shfl_xor(v[0], kS, kT);
+            sum_columns<kT, kOut, kS / 2, 1>(v, li);
+        }
+    }
+}
+
 // kNP: probes of the launch (0: the clean loss, no perturbation); kPair: both signs per
 // probe.  kNS accumulator slots, slot s = probe s / kPer, sign s % kPer.
-template <int kNP, bool kPair>
+template <int kT, int kNP, bool kPair>
 __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
                                                   const float *__restrict__ params,
                                                   uint32_t batch, uint32_t d_in, uint32_t d_hid,
                                                   uint32_t d_out, double *__restrict__ partial,
                                                   PertArgs pa)
 {
+    constexpr int kE = kT / 4;          // k values per lane and 16-k group
+    constexpr int kV = kE / 4;          // float4 loads per operand and group
+    constexpr int kOut = kT * kT / 64;  // accumulator entries per lane
+    typedef typename TileAcc<kT>::type acc_t;
+    struct Op { f32x4_t v[kV]; };
+
     const uint32_t lane = threadIdx.x;
-    const uint32_t m_tiles = batch / 16, n_tiles = d_hid / 16;
+    const uint32_t m_tiles = batch / kT, n_tiles = d_hid / kT;
     const uint32_t total = m_tiles * n_tiles;
     uint32_t t = blockIdx.x;
     if ((total & 7u) == 0) t = (t & 7u) * (total >> 3) + (t >> 3);  // XCD-contiguous tiles
-    const uint32_t m0 = (t % m_tiles) * 16, nt = t / m_tiles, n0 = nt * 16;
-    const uint32_t li = lane & 15u, kq = lane >> 4;
+    const uint32_t m0 = (t % m_tiles) * kT, nt = t / m_tiles, n0 = nt * kT;
+    const uint32_t li = lane % kT, kq = lane / kT;
     // this wave's probes: kNP of them from pa.probe + blockIdx.y * kNP (slots likewise)
     if constexpr (kNP > 0) {
         pa.probe += blockIdx.y * (uint32_t)kNP;
         if (pa.bits) pa.bits += (uint64_t)blockIdx.y * kNP * pa.bits_stride;
     }
 
-    const float *xrow = X + (uint64_t)(m0 + li) * d_in + 4u * kq;
-    const uint64_t wrow = (uint64_t)(n0 + li) * d_in + 4u * kq;   // flat index in params
+    const float *xrow = X + (uint64_t)(m0 + li) * d_in + (uint32_t)kE * kq;
+    const uint64_t wrow = (uint64_t)(n0 + li) * d_in + (uint32_t)kE * kq;   // flat index in params
     const float *wptr = params + wrow;
 
     constexpr bool kPert = kNP > 0;
     constexpr int kPer = kPair ? 2 : 1;
     constexpr int kNS = kPert ? kNP * kPer : 1;
     constexpr int kNB = kPert ? kNP : 1;
-    f32x4_t acc[kNS];
+    acc_t acc[kNS];
 #pragma unroll
-    for (int s = 0; s < kNS; ++s) acc[s] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < kNS; ++s) acc[s] = acc_t{};
     uint64_t cached_blk = ~(uint64_t)0;
     // the four Philox words of the cached block, one array per word (an array of 4-word
     // structs picked by a run-time word index ends up in scratch memory)
@@ -129,14 +174,17 @@ __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
 #pragma unroll
     for (int i = 0; i < kNB; ++i) cwx[i] = cwy[i] = cwz[i] = cww[i] = 0u;
 
-    // Sign bits of the 4 params j .. j+3 of W1 (j a multiple of 4) of each probe of the
-    // launch, in the low 4 bits of q[i].  The probes share the parameters, so one block
-    // change refreshes all their Philox words.
-    auto bits4 = [&](uint64_t j, uint32_t (&q)[kNB]) {
+    // Sign bits of the kE params j .. j+kE-1 of W1 (j a multiple of kE) of each probe of
+    // the launch, in the low kE bits of q[i].  The probes share the parameters, so one
+    // block change refreshes all their Philox words.
+    constexpr uint32_t kMask = (1u << kE) - 1u;
+    auto bits_of = [&](uint64_t j, uint32_t (&q)[kNB]) {
         if (pa.bits) {
 #pragma unroll
-            for (int i = 0; i < kNB; ++i)
-                q[i] = (uint32_t)(pa.bits[(uint64_t)i * pa.bits_stride + (j >> 3)] >> (j & 4)) & 0xFu;
+            for (int i = 0; i < kNB; ++i) {
+                const uint32_t byte = pa.bits[(uint64_t)i * pa.bits_stride + (j >> 3)];
+                q[i] = kE == 8 ? byte : (byte >> (j & 4)) & kMask;
+            }
             return;
         }
         const uint64_t g = pa.offset + j;
@@ -157,40 +205,46 @@ __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
         for (int i = 0; i < kNB; ++i) {
             const uint32_t lo = odd ? cwy[i] : cwx[i];
             const uint32_t hi = odd ? cww[i] : cwz[i];
-            q[i] = ((high ? hi : lo) >> (g & 31)) & 0xFu;
+            q[i] = ((high ? hi : lo) >> (g & 31)) & kMask;
         }
     };
-    auto mfma4 = [](f32x4_t &c, const f32x4_t &a, const f32x4_t &b) {
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+    auto mfma_group = [](acc_t &c, const Op &a, const Op &b) {
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+            if constexpr (kT == 16)
+                c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e / 4][e % 4], b.v[e / 4][e % 4],
+                                                         c, 0, 0, 0);
+            else
+                c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[e / 4][e % 4], b.v[e / 4][e % 4],
+                                                         c, 0, 0, 0);
+        }
     };
     // One 16-k group: operand a of X, operand b of W1 at flat index j.
-    auto group = [&](const f32x4_t &a, const f32x4_t &b, uint64_t j) {
+    auto group = [&](const Op &a, const Op &b, uint64_t j) {
         if constexpr (!kPert) {
-            mfma4(acc[0], a, b);
+            mfma_group(acc[0], a, b);
         } else {
             uint32_t q[kNB];
-            bits4(j, q);
+            bits_of(j, q);
             const uint32_t abits = __builtin_bit_cast(uint32_t, pa.alpha);
 #pragma unroll
             for (int i = 0; i < kNP; ++i) {
                 // d = +alpha where the bit is set, -alpha where clear (alpha's sign bit
                 // flipped): w + d is with_sign(w, bit, alpha), w + (-d) the -alpha value
                 const uint32_t nq = ~q[i];
-                f32x4_t d, bp;
+                float d[kE];
+                Op bp;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    d[t] = signed_alpha(nq, t, abits);
-                    bp[t] = b[t] + d[t];
+                for (int e = 0; e < kE; ++e) {
+                    d[e] = signed_alpha(nq, e, abits);
+                    bp.v[e / 4][e % 4] = b.v[e / 4][e % 4] + d[e];
                 }
-                mfma4(acc[kPer * i], a, bp);
+                mfma_group(acc[kPer * i], a, bp);
                 if constexpr (kPair) {
-                    f32x4_t bm;
+                    Op bm;
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) bm[t] = b[t] + (-d[t]);
-                    mfma4(acc[kPer * i + 1], a, bm);
+                    for (int e = 0; e < kE; ++e) bm.v[e / 4][e % 4] = b.v[e / 4][e % 4] + (-d[e]);
+                    mfma_group(acc[kPer * i + 1], a, bm);
                 }
             }
         }
@@ -199,19 +253,25 @@ __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
     // Stages of kStage K-groups (16 k each): the loads of stage s+1 are in flight while
     // stage s runs through the MFMAs, so memory latency is paid once per kernel rather
     // than once per 16 k.  With several probes each stage carries 2*kNP times the MFMA work,
-    // so shorter stages suffice (and keep the registers from spilling).  The k order, and
-    // with it every accumulator's sequence, does not depend on the staging.
-    constexpr uint32_t kStage = kNP >= 8 ? 2 : kNP >= 2 ? 4 : 8;
+    // and wide tiles load twice the operands per group, so shorter stages suffice (and keep
+    // the registers from spilling).  The k order, and with it every accumulator's sequence,
+    // does not depend on the staging.
+    constexpr uint32_t kStage16 = kNP >= 8 ? 2 : kNP >= 2 ? 4 : 8;
+    constexpr uint32_t kStage = kT == 16 ? kStage16 : kStage16 / 2;
     const uint32_t kfull = (d_in / (16u * kStage)) * (16u * kStage);
-    f32x4_t a0[kStage], b0[kStage], a1[kStage], b1[kStage];
-    auto load_stage = [&](f32x4_t (&a)[kStage], f32x4_t (&b)[kStage], uint32_t kb) {
+    Op a0[kStage], b0[kStage], a1[kStage], b1[kStage];
+    auto load_op = [](Op &o, const float *p) {
+#pragma unroll
+        for (int v = 0; v < kV; ++v) o.v[v] = *reinterpret_cast<const f32x4_t *>(p + 4 * v);
+    };
+    auto load_stage = [&](Op (&a)[kStage], Op (&b)[kStage], uint32_t kb) {
 #pragma unroll
         for (uint32_t g = 0; g < kStage; ++g) {
-            a[g] = *reinterpret_cast<const f32x4_t *>(xrow + kb + 16u * g);
-            b[g] = *reinterpret_cast<const f32x4_t *>(wptr + kb + 16u * g);
+            load_op(a[g], xrow + kb + 16u * g);
+            load_op(b[g], wptr + kb + 16u * g);
         }
     };
-    auto run_stage = [&](f32x4_t (&a)[kStage], f32x4_t (&b)[kStage], uint32_t kb) {
+    auto run_stage = [&](Op (&a)[kStage], Op (&b)[kStage], uint32_t kb) {
 #pragma unroll
         for (uint32_t g = 0; g < kStage; ++g) group(a[g], b[g], wrow + kb + 16u * g);
     };
@@ -231,25 +291,30 @@ __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
             kb = next2;
         }
     }
-    for (uint32_t k0 = kfull; k0 < d_in; k0 += 16) {      // K not a multiple of 128
-        const f32x4_t a = *reinterpret_cast<const f32x4_t *>(xrow + k0);
-        const f32x4_t b = *reinterpret_cast<const f32x4_t *>(wptr + k0);
+    for (uint32_t k0 = kfull; k0 < d_in; k0 += 16) {      // K not a multiple of the stage
+        Op a, b;
+        load_op(a, xrow + k0);
+        load_op(b, wptr + k0);
         group(a, b, wrow + k0);
     }
 
-    // epilogue: column n = n0 + li, rows m0 + 4*kq + r
+    // epilogue: column n = n0 + li; the row of entry r is m0 + 8*(r/4) + 4*kq + r%4
     const uint64_t b1_at = (uint64_t)d_hid * d_in;
     const uint64_t w2_at = b1_at + d_hid;
     const uint64_t pset = (uint64_t)n_tiles * batch * d_out;   // one slot's partial logits
     partial += (uint64_t)blockIdx.y * (kNP > 0 ? kNP * (kPair ? 2 : 1) : 1) * pset;
     const uint32_t n = n0 + li;
     const float b1v = params[b1_at + n];
+    // after sum_columns: the lanes that write, and the row each holds
+    constexpr uint32_t kRep = (uint32_t)(kT / kOut);
+    const uint32_t ridx = li / kRep;
+    const uint32_t row = m0 + 8u * (ridx / 4u) + 4u * kq + ridx % 4u;
     uint32_t sb1[kNB], sw2[kNB];   // per probe: the sign bits of b1[n] and of W2[.][n]
 #pragma unroll
     for (int slot = 0; slot < kNS; ++slot) {
         const uint32_t pi = (uint32_t)(slot / kPer);
         const float alpha = (slot % kPer) ? -pa.alpha : pa.alpha;
-        const f32x4_t &c = acc[slot];
+        const acc_t &c = acc[slot];
         double *out = partial + (uint64_t)slot * pset;
         // the sign bits of b1[n] and of W2[o][n] (bit o), once per probe for both signs
         uint32_t b1bit = 0, w2bits = 0;
@@ -266,26 +331,18 @@ __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
             }
         }
         const float bias = kPert ? with_sign(b1v, b1bit, alpha) : b1v;
-        float g[4];
+        float g[kOut];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) g[r] = gelu_exact(c[r] + bias);
+        for (int r = 0; r < kOut; ++r) g[r] = gelu_exact(c[r] + bias);
         for (uint32_t o = 0; o < d_out; ++o) {
             const float w2v = params[w2_at + (uint64_t)o * d_hid + n];
             const float w2 = kPert ? with_sign(w2v, (w2bits >> o) & 1u, alpha) : w2v;
-            float p[4];
+            float p[kOut];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p[r] = g[r] * w2;
-            // sum over the 16 columns of the tile (lanes with equal kq), fixed butterfly
-#pragma unroll
-            for (int s = 8; s >= 1; s >>= 1) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) p[r] = p[r] + __shfl_xor(p[r], s, 16);
-            }
-            if (li == 0) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    out[((uint64_t)(m0 + 4u * kq + (uint32_t)r) * d_out + o) * n_tiles + nt] = (double)p[r];
-            }
+            for (int r = 0; r < kOut; ++r) p[r] = g[r] * w2;
+            sum_columns<kT, kOut>(p, li);      // over the tile's kT columns
+            if (li % kRep == 0)
+                out[((uint64_t)row * d_out + o) * n_tiles + nt] = (double)p[0];
         }
     }
 }
@@ -295,13 +352,13 @@ __global__ __launch_bounds__(256) void k_mlp_rows(const double *__restrict__ par
                                                   const float *__restrict__ params,
                                                   const int64_t *__restrict__ labels,
                                                   uint32_t batch, uint32_t d_in, uint32_t d_hid,
-                                                  uint32_t d_out, double *__restrict__ rowloss,
-                                                  PertArgs pa, uint32_t per)
+                                                  uint32_t d_out, uint32_t n_tiles,
+                                                  double *__restrict__ rowloss, PertArgs pa,
+                                                  uint32_t per)
 {
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t m = blockIdx.x * 4u + (threadIdx.x >> 6);
     if (m >= batch) return;
-    const uint32_t n_tiles = d_hid / 16;
     // slot blockIdx.y: probe pa.probe + blockIdx.y / per, -alpha for the odd slots of pairs
     const uint32_t pi = blockIdx.y / per;
     const float alpha = (blockIdx.y % per) ? -pa.alpha : pa.alpha;
@@ -349,22 +406,33 @@ __global__ __launch_bounds__(256) void k_mlp_mean(const double *__restrict__ row
 }
 
 // One launch sequence: tiles (kNP probes per wave, `groups` probe groups), row losses, means.
-template <int kNP, bool kPair>
+template <int kT, int kNP, bool kPair>
 static void launch_chain(const float *params, const float *X, const int64_t *labels,
                          uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out,
                          double *partial, double *out, double *out2, const PertArgs &pa,
                          hipStream_t stream, uint32_t groups = 1)
 {
-    const uint32_t tiles = (batch / 16) * (d_hid / 16);
+    const uint32_t n_tiles = d_hid / kT;
+    const uint32_t tiles = (batch / kT) * n_tiles;
     const uint32_t per = kPair ? 2u : 1u;
     const uint32_t nslot = kNP > 0 ? (uint32_t)kNP * per * groups : 1u;
-    double *rowloss = partial + (uint64_t)nslot * (d_hid / 16) * batch * d_out;
-    hipLaunchKernelGGL((k_mlp_tiles<kNP, kPair>), dim3(tiles, groups), dim3(64), 0, stream, X,
-                       params, batch, d_in, d_hid, d_out, partial, pa);
+    double *rowloss = partial + (uint64_t)nslot * n_tiles * batch * d_out;
+    hipLaunchKernelGGL((k_mlp_tiles<kT, kNP, kPair>), dim3(tiles, groups), dim3(64), 0, stream,
+                       X, params, batch, d_in, d_hid, d_out, partial, pa);
     hipLaunchKernelGGL(k_mlp_rows<(kNP > 0)>, dim3((batch + 3) / 4, nslot), dim3(256), 0, stream,
-                       partial, params, labels, batch, d_in, d_hid, d_out, rowloss, pa, per);
+                       partial, params, labels, batch, d_in, d_hid, d_out, n_tiles, rowloss, pa,
+                       per);
     hipLaunchKernelGGL(k_mlp_mean, dim3(nslot), dim3(256), 0, stream, rowloss, batch, out, out2,
                        per);
+}
+
+// Every launch for one shape uses the same tile kernel, so the k order of each hidden unit's
+// accumulation, and with it every loss, is the same in all the MLP entry points: 32 x 32
+// tiles where the batch and the hidden width allow (half the operand arithmetic and loads
+// per MFMA flop of the 16 x 16 form), 16 x 16 tiles otherwise.
+static bool wide_tiles(uint32_t batch, uint32_t d_hid)
+{
+    return batch % 32u == 0 && d_hid % 32u == 0;
 }
 
 static PertArgs pert_args(const MlpPerturb *pert, Key key, uint64_t nparams)
@@ -386,23 +454,37 @@ static uint64_t mlp_params(uint32_t d_in, uint32_t d_hid, uint32_t d_out)
     return (uint64_t)d_hid * d_in + d_hid + (uint64_t)d_out * d_hid + d_out;
 }
 
+template <int kT>
+static void launch_mlp_loss_t(const float *params, const float *X, const int64_t *labels,
+                              uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out,
+                              double *partial, double *out, const PertArgs &pa, bool pert,
+                              hipStream_t stream, double *out_minus)
+{
+    if (pert) {
+        if (out_minus)
+            launch_chain<kT, 1, true>(params, X, labels, batch, d_in, d_hid, d_out, partial,
+                                      out, out_minus, pa, stream);
+        else
+            launch_chain<kT, 1, false>(params, X, labels, batch, d_in, d_hid, d_out, partial,
+                                       out, nullptr, pa, stream);
+    } else {
+        launch_chain<kT, 0, false>(params, X, labels, batch, d_in, d_hid, d_out, partial, out,
+                                   nullptr, pa, stream);
+    }
+}
+
 hipError_t launch_mlp_loss(const float *params, const float *X, const int64_t *labels,
                            uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out,
                            double *partial, double *out, const MlpPerturb *pert, Key key,
                            hipStream_t stream, double *out_minus)
 {
     const PertArgs pa = pert_args(pert, key, mlp_params(d_in, d_hid, d_out));
-    if (pert) {
-        if (out_minus)
-            launch_chain<1, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, out,
-                                  out_minus, pa, stream);
-        else
-            launch_chain<1, false>(params, X, labels, batch, d_in, d_hid, d_out, partial, out,
-                                   nullptr, pa, stream);
-    } else {
-        launch_chain<0, false>(params, X, labels, batch, d_in, d_hid, d_out, partial, out,
-                               nullptr, pa, stream);
-    }
+    if (wide_tiles(batch, d_hid))
+        launch_mlp_loss_t<32>(params, X, labels, batch, d_in, d_hid, d_out, partial, out, pa,
+                              pert != nullptr, stream, out_minus);
+    else
+        launch_mlp_loss_t<16>(params, X, labels, batch, d_in, d_hid, d_out, partial, out, pa,
+                              pert != nullptr, stream, out_minus);
     return hipGetLastError();
 }
 
@@ -426,7 +508,7 @@ hipError_t launch_mlp_loss_probes(const float *params, const float *X, const int
 {
     const uint64_t nparams = mlp_params(d_in, d_hid, d_out);
     const uint32_t pw = mlp_probes_per_wave();
-    // launch sequences of 16 probes, then 8, 4, 2, 1 for the rest, each with min(pw, size)
+    // launch sequences of 64 probes, then 32, 16, ..., 1 for the rest, each with min(pw, size)
     // probes per wave; each reuses the workspace from its start (they run in stream order)
     for (uint32_t done = 0; done < nprobes;) {
         const uint32_t left = nprobes - done;
@@ -438,11 +520,21 @@ hipError_t launch_mlp_loss_probes(const float *params, const float *X, const int
         if (pert.bits) p.bits = pert.bits + (uint64_t)done * ((nparams + 127) / 128 * 16);
         const PertArgs pa = pert_args(&p, key, nparams);
         double *op = out_plus + done, *om = out_minus + done;
-        switch (w) {
-        case 8: launch_chain<8, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 8); break;
-        case 4: launch_chain<4, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 4); break;
-        case 2: launch_chain<2, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 2); break;
-        default: launch_chain<1, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k); break;
+        if (wide_tiles(batch, d_hid)) {
+            // at most 4 probes per wave: 8 would hold 256 accumulator registers
+            switch (w) {
+            case 8:
+            case 4: launch_chain<32, 4, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 4); break;
+            case 2: launch_chain<32, 2, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 2); break;
+            default: launch_chain<32, 1, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k); break;
+            }
+        } else {
+            switch (w) {
+            case 8: launch_chain<16, 8, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 8); break;
+            case 4: launch_chain<16, 4, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 4); break;
+            case 2: launch_chain<16, 2, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 2); break;
+            default: launch_chain<16, 1, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k); break;
+            }
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

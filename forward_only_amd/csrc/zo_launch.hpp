@@ -110,10 +110,10 @@ hipError_t launch_mlp_loss(const float *params, const float *X, const int64_t *l
 
 // Both losses of probes pert.probe .. pert.probe + nprobes - 1 (out_plus[i], out_minus[i]),
 // up to kMlpProbesPerLaunch probes per launch sequence, kMlpProbesPerWave of them per wave
-// sharing every operand load (ZO_MLP_PROBES_PER_WAVE overrides: 1, 2, 4, 8); pert.bits (if
+// sharing every operand load (ZO_MLP_PROBES_PER_WAVE overrides: 1, 2, 4, 8; 4 at most on 32-wide tiles); pert.bits (if
 // given) holds nprobes packed rows.  The workspace holds 2 * min(nprobes,
 // kMlpProbesPerLaunch) slots of partial logits and row losses.
-constexpr uint32_t kMlpProbesPerLaunch = 16;
+constexpr uint32_t kMlpProbesPerLaunch = 64;
 constexpr uint32_t kMlpProbesPerWave = 2;
 hipError_t launch_mlp_loss_probes(const float *params, const float *X, const int64_t *labels,
                                   uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out,

@@ -266,7 +266,9 @@ zo_status zo_lowrank_quad_loss(zo_ctx *ctx, const void *d_theta, zo_dtype dtype,
  * [batch x d_in] row-major, 16-byte aligned.  d_labels: device int64 [batch], each in
  * [0, d_out) (an out-of-range label makes the loss NaN).  The GEMM runs on MFMA in fp32;
  * the partial logits and the cross-entropy are reduced in fp64 in a fixed order
- * (deterministic).  d_workspace: device, 8-byte aligned, at least
+ * (deterministic).  The GEMM's tiles are 32 x 32 where batch and d_hid are multiples of 32,
+ * 16 x 16 otherwise, in every MLP entry point alike, so that the entry points agree bit for
+ * bit at any one shape.  d_workspace: device, 8-byte aligned, at least
  * zo_mlp_workspace_bytes(...) bytes (enough for every MLP call, zo_mlp_loss_pair
  * included), owned by the caller.  d_loss: device, one double.
  * Limits: batch, d_in, d_hid multiples of 16; 1 <= d_out <= 16.
@@ -311,8 +313,8 @@ zo_status zo_mlp_loss_pair(zo_ctx *ctx, const float *d_params, uint64_t offset, 
  * d_loss_plus[i] at theta + alpha * z_{probe0+i} and d_loss_minus[i] at
  * theta - alpha * z_{probe0+i} (device, n_probes doubles each), each equal bit for bit to
  * zo_mlp_loss_perturbed of that probe and sign: the step's forwards of "How 1.5-SPSA Works"
- * (n_pert probes, two losses each) as launch sequences of up to sixteen probes, each wave of
- * the MFMA GEMM running two probes (ZO_MLP_PROBES_PER_WAVE: 1, 2, 4 or 8) so that every X
+ * (n_pert probes, two losses each) as launch sequences of up to 64 probes, each wave of
+ * the MFMA GEMM running two probes (ZO_MLP_PROBES_PER_WAVE: 1, 2, 4 or 8; at most 4 on 32 x 32 tiles) so that every X
  * and W1 operand it loads feeds both signs of each.  d_bits: NULL
  * (regenerate) or n_probes packed rows over the parameters, row i = probe probe0 + i
  * (zo_bits_stride(params) bytes apart, 16-byte aligned).  d_workspace: device, 8-byte aligned,

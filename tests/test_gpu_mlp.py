@@ -18,7 +18,11 @@ from workloads import CONFIGS, gen
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(16, 16, 16, 2), (32, 48, 64, 3), (48, 32, 128, 16), (128, 768, 3072, 2)]
+# 16 x 16 tiles where the batch or the hidden width is not a multiple of 32, 32 x 32 tiles
+# otherwise; K below one 16-k group's multiple of the staging, with a ragged group count, and
+# the workload's shape
+SHAPES = [(16, 16, 16, 2), (32, 48, 64, 3), (48, 32, 128, 16), (64, 208, 96, 16),
+          (128, 768, 3072, 2)]
 
 
 @pytest.fixture(scope="module")
@@ -64,7 +68,8 @@ def test_mlp_config_loss(ctx):
     assert abs(got - ref) <= 1e-5 * abs(ref), (got, ref)
 
 
-@pytest.mark.parametrize("shape", [(16, 16, 16, 2), (32, 48, 64, 3), (128, 768, 3072, 2)])
+@pytest.mark.parametrize("shape", [(16, 16, 16, 2), (32, 48, 64, 3), (64, 208, 96, 16),
+                                   (128, 768, 3072, 2)])
 @pytest.mark.parametrize("mode", ["regen", "bits"])
 def test_fused_perturbation_equals_perturb_then_forward(ctx, shape, mode):
     batch, d_in, d_hid, d_out = shape
@@ -88,7 +93,7 @@ def test_fused_perturbation_equals_perturb_then_forward(ctx, shape, mode):
 
 
 @pytest.mark.parametrize("shape", [(16, 16, 16, 2), (32, 48, 64, 3), (48, 144, 128, 16),
-                                   (128, 768, 3072, 2)])
+                                   (64, 208, 96, 16), (128, 768, 3072, 2)])
 @pytest.mark.parametrize("mode", ["regen", "bits"])
 def test_pair_equals_two_fused_calls(ctx, shape, mode):
     """zo_mlp_loss_pair gives exactly the two single fused losses (+alpha, -alpha), in
@@ -111,9 +116,9 @@ def test_pair_equals_two_fused_calls(ctx, shape, mode):
 
 
 @pytest.mark.parametrize("shape", [(16, 16, 16, 2), (32, 48, 64, 3), (48, 144, 128, 16),
-                                   (128, 768, 3072, 2)])
+                                   (64, 208, 96, 16), (128, 768, 3072, 2)])
 @pytest.mark.parametrize("mode", ["regen", "bits"])
-@pytest.mark.parametrize("nprobes", [1, 3, 8, 13, 21])
+@pytest.mark.parametrize("nprobes", [1, 3, 8, 13, 21, 70])
 def test_probes_equal_pairs(ctx, shape, mode, nprobes):
     """zo_mlp_loss_probes gives, for every probe of the batch, exactly the losses of
     zo_mlp_loss_pair (21 probes run as launch sequences of 16, 4 and 1 probes, 13 as 8, 4
@@ -140,9 +145,9 @@ def test_probes_argument_checks(ctx):
     t, x, yl = _dev(theta, X, y)
     L = zo._lib.lib()
     need = zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 5)
-    sixteen = zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 16)
-    assert zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 100) == sixteen   # 16 per launch
-    assert need * 16 == sixteen * 5
+    full = zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 64)
+    assert zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 100) == full   # 64 per launch
+    assert need * 64 == full * 5
     assert zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 1) == zo.zo_mlp_workspace_bytes(16, 16, 16, 2)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     out = torch.empty(10, dtype=torch.float64, device="cuda")
