@@ -227,6 +227,15 @@ __global__ __launch_bounds__(256) void k_sum_partials(const double *__restrict__
 // candidates, rnd(x + alpha) and rnd(x - alpha) (what zo_perturb stores for a set and for a
 // clear sign bit under +alpha, and the other way round under -alpha), so both are formed
 // and squared once per param and each probe's sign bit picks between them.
+// m ? a : b for a lane mask m of all ones or all zeros, word by word.
+__device__ __forceinline__ double select_f64(uint32_t m, double a, double b)
+{
+    const uint64_t ua = __builtin_bit_cast(uint64_t, a), ub = __builtin_bit_cast(uint64_t, b);
+    const uint32_t lo = ((uint32_t)ua & m) | ((uint32_t)ub & ~m);
+    const uint32_t hi = ((uint32_t)(ua >> 32) & m) | ((uint32_t)(ub >> 32) & ~m);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 template <bool kBF16>
 __device__ __forceinline__ void quad_terms4(double (&acc)[2 * kQuadProbes], const float (&x)[4],
                                             const float (&av)[4], const uint32_t (&w)[kQuadProbes],
@@ -256,9 +265,12 @@ __device__ __forceinline__ void quad_terms4(double (&acc)[2 * kQuadProbes], cons
         const double sa = ta * ta, sb = tb * tb, ad = (double)av[q];
 #pragma unroll
         for (uint32_t i = 0; i < kQuadProbes; ++i) {
-            const bool set = (w[i] >> (sh + (uint32_t)q)) & 1u;
-            acc[2 * i] = quad_term_sq(acc[2 * i], ad, set ? sa : sb);
-            acc[2 * i + 1] = quad_term_sq(acc[2 * i + 1], ad, set ? sb : sa);
+            // all ones where the probe's bit is set: one bit-field extract, then bitwise
+            // selects of the two squares (a compare and two conditional moves per square
+            // otherwise)
+            const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)w[i], sh + (uint32_t)q, 1u);
+            acc[2 * i] = quad_term_sq(acc[2 * i], ad, select_f64(m, sa, sb));
+            acc[2 * i + 1] = quad_term_sq(acc[2 * i + 1], ad, select_f64(m, sb, sa));
         }
     }
 }
