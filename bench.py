@@ -354,7 +354,7 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
     a = applied_eps(cfg.eps)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    per = {"perturb": [], "perturb2": [], "weights": [], "update": [], "loss": [], "mlp": [],
+    per = {"perturb": [], "perturb2": [], "weights": [], "update": [], "loss": [],
            "mlp_probes": [], "loss_probes": []}
 
     def timed(kind, fn, record):
@@ -374,42 +374,32 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
             timed("loss", lambda: zo.zo_lowrank_quad_loss(ctx, theta, a_dev, U_dev, out=out),
                   record)
 
-    def mlp_loss(out, probe, alpha, s, record):
-        if probe is None:
-            timed("mlp", lambda: zo.zo_mlp_loss(ctx, theta, mlp["X"], mlp["y"], mlp["d_hid"],
-                                                 mlp["d_out"], workspace=mlp["ws"], out=out),
-                  record)
-        else:
-            timed("mlp", lambda: zo.zo_mlp_loss_perturbed(
-                ctx, theta, 0, s, probe, alpha, mlp["X"], mlp["y"], mlp["d_hid"],
-                mlp["d_out"], workspace=mlp["ws"], out=out), record)
-
-    def mlp_probes(op, om, s, record):
+    def mlp_probes(op, om, oc, s, record):
         timed("mlp_probes", lambda: zo.zo_mlp_loss_probes(
             ctx, theta, 0, s, 0, n, a, mlp["X"], mlp["y"], mlp["d_hid"], mlp["d_out"],
-            workspace=mlp["ws"], out_plus=op, out_minus=om), record)
+            workspace=mlp["ws"], out_plus=op, out_minus=om, out_clean=oc), record)
 
     def one_step(s, record):
         L0, Lp, Lm = L0s[s], Lps[s], Lms[s]
         if mlp is not None:
             # the forward applies each probe while reading the weights: no passes over
-            # theta; one paired launch sequence gives both losses of a probe
-            mlp_loss(L0, None, 0.0, s, record)
-            mlp_probes(Lp, Lm, s, record)
+            # theta; one launch sequence gives both losses of every probe and the clean loss
+            mlp_probes(Lp, Lm, L0, s, record)
+            timed("weights", lambda: zo.zo_probe_weights(ctx, Lp, Lm, L0, a, cfg.delta,
+                                                         out=c_buf), record)
+            timed("update", lambda: zo.zo_update(ctx, theta, 0, s, c_buf, cfg.eta), record)
+            return
+        if schedule == "fused":
+            # each probe applied while theta and a are read (four probes per pass, the first
+            # pass also summing the clean loss), theta written only by the update
+            timed("loss_probes", lambda: zo.zo_quad_loss_probes(
+                ctx, theta, a_dev, 0, s, 0, n, a, out_plus=Lp, out_minus=Lm, out_clean=L0),
+                record)
             timed("weights", lambda: zo.zo_probe_weights(ctx, Lp, Lm, L0, a, cfg.delta,
                                                          out=c_buf), record)
             timed("update", lambda: zo.zo_update(ctx, theta, 0, s, c_buf, cfg.eta), record)
             return
         loss_into(L0, record)
-        if schedule == "fused":
-            # each probe applied while theta and a are read (four probes per pass), theta
-            # written only by the update
-            timed("loss_probes", lambda: zo.zo_quad_loss_probes(
-                ctx, theta, a_dev, 0, s, 0, n, a, out_plus=Lp, out_minus=Lm), record)
-            timed("weights", lambda: zo.zo_probe_weights(ctx, Lp, Lm, L0, a, cfg.delta,
-                                                         out=c_buf), record)
-            timed("update", lambda: zo.zo_update(ctx, theta, 0, s, c_buf, cfg.eta), record)
-            return
         if schedule == "S4":
             for i in range(n):
                 timed("perturb", lambda: zo.zo_perturb(ctx, theta, 0, s, i, +a), record)
@@ -512,8 +502,8 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
     passes = 0 if mlp is not None or schedule == "fused" else (4 * n if schedule == "S4" else 2 * n)
     pass_bytes = 2.0 * esize * M                      # one read + one write of theta
     step_bytes = (passes + 1) * pass_bytes            # the passes + the update
-    if schedule == "fused":                           # + the clean loss and the fused passes
-        step_bytes += (1 + (n + 3) // 4) * float(esize + 4) * M
+    if schedule == "fused":                           # + the fused passes (the first one also
+        step_bytes += ((n + 3) // 4) * float(esize + 4) * M   # sums the clean loss)
     pass_roofline = None
     if pert_ms:
         pa = pass_bytes / (pert_ms * 1e-3) / 1e9
@@ -527,18 +517,19 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
         fa = fb / (lp_ms * 1e-3) / 1e9
         achieved = fa
         roofline = {"kernel": "k_quad_probes_partial (the quadratic loss at theta +/- alpha z "
-                              "of four probes per pass, theta and a read once; time of the "
-                              f"whole zo_quad_loss_probes call: {npass} passes and their sums)",
+                              "of four probes per pass, theta and a read once, the first pass "
+                              "also summing the clean loss; time of the whole "
+                              f"zo_quad_loss_probes call: {npass} passes and their sums)",
                     "bound": "hbm", "achieved": fa, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": fa / PEAK_HBM_GBPS, "traffic": None,
-                    "losses_per_s": 2.0 * n / (lp_ms * 1e-3)}
+                    "losses_per_s": (2.0 * n + 1.0) / (lp_ms * 1e-3)}
     elif mlp is not None:
         mlp_ms = avg_ms("mlp_probes")
-        achieved = 2.0 * n * mlp["flop"] / (mlp_ms * 1e-3) / 1e12
+        achieved = (2.0 * n + 1.0) * mlp["flop"] / (mlp_ms * 1e-3) / 1e12
         roofline = {"kernel": "k_mlp_tiles (MFMA fp32 GEMM of the MLP forward, both signs of "
-                              "up to 64 probes per launch sequence; time of the whole "
-                              "zo_mlp_loss_probes call: tiles, row and mean kernels of all "
-                              "n_pert probes)",
+                              "up to 64 probes per launch sequence and the clean loss; time "
+                              "of the whole zo_mlp_loss_probes call: tiles, row and mean "
+                              "kernels of all n_pert probes' 2 n_pert + 1 forwards)",
                     "bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS,
                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
                     "traffic": None}
@@ -576,10 +567,12 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
         "config": {"workload": (f"{cfg.name}: {M} {cfg.dtype} params in one flat buffer, "
                                 f"n_pert={n}, eps={cfg.eps}, eta={cfg.eta}, " +
                                 ("probes applied inside the MFMA forward, both signs of up to 64 "
-                                 "probes per launch sequence (no passes over theta) + update"
+                                 "probes and the clean loss per launch sequence (no passes over "
+                                 "theta) + update"
                                  if mlp is not None else
                                  "probes applied while theta is read, four per pass of the "
-                                 "quadratic loss (no passes that write theta) + update"
+                                 "quadratic loss, the clean loss in the first pass (no passes "
+                                 "that write theta) + update"
                                  if schedule == "fused" else
                                  f"schedule {schedule} ({passes} passes + update" +
                                  (" carrying the last restore)" if schedule == "S2f"
@@ -595,7 +588,6 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
         "kernels_ms": {"pass_avg": pert_ms, "perturb_avg": avg_ms("perturb"),
                        "perturb2_avg": avg_ms("perturb2"), "update_avg": upd_ms,
                        "weights_avg": w_ms, "loss_avg": avg_ms("loss"),
-                       "mlp_forward_avg": avg_ms("mlp"),
                        "mlp_probes_avg": avg_ms("mlp_probes"),
                        "loss_probes_avg": avg_ms("loss_probes")},
         "roofline": roofline or {"kernel": f"k_perturb_chunks ({cfg.dtype}, probes regenerated; "

@@ -259,13 +259,17 @@ def zo_quad_loss(ctx: Context, theta: torch.Tensor, a: torch.Tensor,
 def zo_quad_loss_probes(ctx: Context, theta: torch.Tensor, a: torch.Tensor, offset: int,
                         step: int, probe0: int, n_probes: int, alpha: float,
                         bits: torch.Tensor | None = None, out_plus: torch.Tensor | None = None,
-                        out_minus: torch.Tensor | None = None, stream=None):
+                        out_minus: torch.Tensor | None = None,
+                        out_clean: torch.Tensor | None = None, stream=None):
     """The quadratic loss at theta +/- alpha * z_i for probes probe0 .. probe0 + n_probes - 1,
     each probe applied while theta is read (theta is not written); returns (out_plus,
     out_minus), float64 tensors of n_probes.  bits: None or (n_probes, zo_bits_stride(theta))
-    rows."""
+    rows.  out_clean (one float64, optional) also receives the loss at theta itself, equal to
+    zo_quad_loss, from the first pass over theta."""
     if a.numel() != theta.numel():
         raise ValueError("a and theta must have the same length")
+    if out_clean is not None and out_clean.numel() < 1:
+        raise ValueError("out_clean is too small")
     for name, o in (("out_plus", out_plus), ("out_minus", out_minus)):
         if o is not None and o.numel() < n_probes:
             raise ValueError(f"{name} is too small")
@@ -277,7 +281,9 @@ def zo_quad_loss_probes(ctx: Context, theta: torch.Tensor, a: torch.Tensor, offs
         ctx.handle, _dev(theta, "theta"), _dtype_code(theta), _dev(a, "a", torch.float32),
         offset, theta.numel(), step, probe0, n_probes, float(alpha),
         _rows(bits, n_probes, theta.numel()), _dev(out_plus, "out_plus", torch.float64),
-        _dev(out_minus, "out_minus", torch.float64), _stream(stream)), "zo_quad_loss_probes")
+        _dev(out_minus, "out_minus", torch.float64),
+        None if out_clean is None else _dev(out_clean, "out_clean", torch.float64),
+        _stream(stream)), "zo_quad_loss_probes")
     return out_plus, out_minus
 
 
@@ -376,10 +382,15 @@ def zo_mlp_loss_probes(ctx: Context, params: torch.Tensor, offset: int, step: in
                        d_hid: int, d_out: int, bits: torch.Tensor | None = None,
                        workspace: torch.Tensor | None = None,
                        out_plus: torch.Tensor | None = None,
-                       out_minus: torch.Tensor | None = None, stream=None):
+                       out_minus: torch.Tensor | None = None,
+                       out_clean: torch.Tensor | None = None, stream=None):
     """The MLP losses at params +/- alpha * z_i for probes probe0 .. probe0 + n_probes - 1
     (up to 64 per launch sequence), without writing params; returns (out_plus, out_minus),
-    float64 tensors of n_probes.  bits: None or (n_probes, zo_bits_stride(params)) rows."""
+    float64 tensors of n_probes.  bits: None or (n_probes, zo_bits_stride(params)) rows.
+    out_clean (one float64, optional) also receives the loss at params itself, equal to
+    zo_mlp_loss, from the first launch sequence."""
+    if out_clean is not None and out_clean.numel() < 1:
+        raise ValueError("out_clean is too small")
     batch, d_in = X.shape
     if params.numel() != d_hid * d_in + d_hid + d_out * d_hid + d_out:
         raise ValueError("params must hold the MLP's parameters")
@@ -401,6 +412,7 @@ def zo_mlp_loss_probes(ctx: Context, params: torch.Tensor, offset: int, step: in
         _dev(labels, "labels", torch.int64), batch, d_in, d_hid, d_out,
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _dev(out_plus, "out_plus", torch.float64), _dev(out_minus, "out_minus", torch.float64),
+        None if out_clean is None else _dev(out_clean, "out_clean", torch.float64),
         _stream(stream)), "zo_mlp_loss_probes")
     return out_plus, out_minus
 

@@ -42,7 +42,7 @@ SIGNATURES = {
     "zo_reset_nonfinite": (_int, [_vp, _vp]),
     "zo_quad_loss": (_int, [_vp, _vp, _int, _vp, _u64, _vp, _vp]),
     "zo_quad_loss_probes": (_int, [_vp, _vp, _int, _vp, _u64, _u64, _u32, _u32, _u32, _f32, _vp,
-                                   _vp, _vp, _vp]),
+                                   _vp, _vp, _vp, _vp]),
     "zo_lowrank_quad_loss": (_int, [_vp, _vp, _int, _vp, _vp, _u32, _u64, _vp, _vp]),
     "zo_mlp_workspace_bytes": (_u64, [_u32, _u32, _u32, _u32]),
     "zo_mlp_loss": (_int, [_vp, _vp, _vp, _vp, _u32, _u32, _u32, _u32, _vp, _u64, _vp, _vp]),
@@ -52,7 +52,7 @@ SIGNATURES = {
                                 _u32, _u32, _u32, _vp, _u64, _vp, _vp, _vp]),
     "zo_mlp_probes_workspace_bytes": (_u64, [_u32, _u32, _u32, _u32, _u32]),
     "zo_mlp_loss_probes": (_int, [_vp, _vp, _u64, _u32, _u32, _u32, _f32, _vp, _vp, _vp, _u32,
-                                  _u32, _u32, _u32, _vp, _u64, _vp, _vp, _vp]),
+                                  _u32, _u32, _u32, _vp, _u64, _vp, _vp, _vp, _vp]),
     "zo_mlp_loss_pair_noalloc": (_int, [_vp, _vp, _u64, _u32, _u32, _f32, _vp, _vp, _vp, _u32,
                                         _u32, _u32, _u32, _vp, _vp, _vp]),
     "zo_stream_rmw": (_int, [_vp, _vp, _u64, _u32, _vp]),

@@ -8,8 +8,8 @@
 #include "zo_launch.hpp"
 
 static_assert(ZO_MAX_NPERT == zo::kMaxNpert, "one probe-count limit");
-static_assert(2 * zo::kQuadProbes <= zo::kLowRankMax + 1,
-              "the loss partials hold both signs of every probe of a fused pass");
+static_assert(2 * zo::kQuadProbes + 1 <= zo::kLowRankMax + 1,
+              "the loss partials hold both signs of every probe of a fused pass and the clean loss");
 
 // Scratch of zo_mlp_loss_pair_noalloc: the partial logits and row losses of both signs,
 // ZO_NOALLOC_SCRATCH_BYTES per device, held until the process ends.  Host code never
@@ -291,20 +291,22 @@ zo_status zo_quad_loss(zo_ctx *c, const void *d_theta, zo_dtype dtype, const flo
 zo_status zo_quad_loss_probes(zo_ctx *c, const void *d_theta, zo_dtype dtype, const float *d_a,
                               uint64_t offset, uint64_t n, uint32_t step, uint32_t probe0,
                               uint32_t n_probes, float alpha, const uint8_t *d_bits,
-                              double *d_out_plus, double *d_out_minus, void *stream)
+                              double *d_out_plus, double *d_out_minus, double *d_out_clean,
+                              void *stream)
 {
     if (!ctx_ok(c)) return ZO_EINVAL;
     if (dtype != ZO_FP32 && dtype != ZO_BF16) return ZO_EINVAL;
-    if (n_probes == 0) return ZO_OK;
-    if (!d_out_plus || !d_out_minus) return ZO_EINVAL;
-    if (n_probes - 1 > UINT32_MAX - probe0) return ZO_EINVAL;   // probe indices wrap
+    if (n_probes == 0 && !d_out_clean) return ZO_OK;
+    if (n_probes > 0 && (!d_out_plus || !d_out_minus)) return ZO_EINVAL;
+    if (n_probes > 0 && n_probes - 1 > UINT32_MAX - probe0) return ZO_EINVAL;   // indices wrap
     if (!range_ok(offset, n)) return ZO_EINVAL;
     if (n > 0 && (!d_theta || !d_a || !aligned16(d_theta) || !aligned16(d_a))) return ZO_EINVAL;
     if (d_bits && !aligned16(d_bits)) return ZO_EINVAL;
     return from_hip(zo::launch_quad_loss_probes(d_theta, dtype == ZO_BF16, d_a, offset, n,
                                                 key_of(c), step, probe0, n_probes, alpha,
                                                 n > 0 ? d_bits : nullptr, c->d_partials,
-                                                d_out_plus, d_out_minus, as_stream(stream)));
+                                                d_out_plus, d_out_minus, d_out_clean,
+                                                as_stream(stream)));
 }
 
 zo_status zo_lowrank_quad_loss(zo_ctx *c, const void *d_theta, zo_dtype dtype,
@@ -331,9 +333,10 @@ uint64_t zo_mlp_probes_workspace_bytes(uint32_t batch, uint32_t d_in, uint32_t d
                                        uint32_t d_out, uint32_t n_probes)
 {
     (void)d_in;
-    // partial logits and row losses of both signs of up to kMlpProbesPerLaunch probes
+    // partial logits and row losses of both signs of up to kMlpProbesPerLaunch probes and of
+    // the clean loss
     const uint64_t k = n_probes < zo::kMlpProbesPerLaunch ? n_probes : zo::kMlpProbesPerLaunch;
-    return 2u * k * ((uint64_t)(d_hid / 16u) * batch * d_out + batch) * sizeof(double);
+    return (2u * k + 1u) * ((uint64_t)(d_hid / 16u) * batch * d_out + batch) * sizeof(double);
 }
 
 static zo_status mlp_checks(zo_ctx *c, const float *d_params, const float *d_X,
@@ -407,17 +410,18 @@ zo_status zo_mlp_loss_probes(zo_ctx *c, const float *d_params, uint64_t offset, 
                              const uint8_t *d_bits, const float *d_X, const int64_t *d_labels,
                              uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out,
                              void *d_workspace, uint64_t workspace_bytes, double *d_loss_plus,
-                             double *d_loss_minus, void *stream)
+                             double *d_loss_minus, double *d_loss_clean, void *stream)
 {
     if (!ctx_ok(c)) return ZO_EINVAL;
-    if (n_probes == 0) return ZO_OK;
+    if (n_probes == 0 && !d_loss_clean) return ZO_OK;
     const zo_status st = mlp_checks(c, d_params, d_X, d_labels, batch, d_in, d_hid, d_out,
-                                    d_workspace, UINT64_MAX, d_loss_plus);
+                                    d_workspace, UINT64_MAX,
+                                    n_probes > 0 ? d_loss_plus : d_loss_clean);
     if (st != ZO_OK) return st;
-    if (!d_loss_minus) return ZO_EINVAL;
+    if (n_probes > 0 && !d_loss_minus) return ZO_EINVAL;
     if (workspace_bytes < zo_mlp_probes_workspace_bytes(batch, d_in, d_hid, d_out, n_probes))
         return ZO_EINVAL;
-    if (n_probes - 1 > UINT32_MAX - probe0) return ZO_EINVAL;   // probe indices wrap
+    if (n_probes > 0 && n_probes - 1 > UINT32_MAX - probe0) return ZO_EINVAL;   // indices wrap
     if (d_bits && !aligned16(d_bits)) return ZO_EINVAL;
     const uint64_t nparams = (uint64_t)d_hid * d_in + d_hid + (uint64_t)d_out * d_hid + d_out;
     if (!range_ok(offset, nparams)) return ZO_EINVAL;
@@ -425,7 +429,7 @@ zo_status zo_mlp_loss_probes(zo_ctx *c, const float *d_params, uint64_t offset, 
     return from_hip(zo::launch_mlp_loss_probes(d_params, d_X, d_labels, batch, d_in, d_hid, d_out,
                                                static_cast<double *>(d_workspace), pert, n_probes,
                                                key_of(c), d_loss_plus, d_loss_minus,
-                                               as_stream(stream)));
+                                               d_loss_clean, as_stream(stream)));
 }
 
 zo_status zo_mlp_loss_pair_noalloc(zo_ctx *c, const float *d_params, uint64_t offset,

@@ -128,14 +128,23 @@ __device__ __forceinline__ void sum_columns(float (&v)[kOut], uint32_t li)
     }
 }
 
-// kNP: probes of the launch (0: the clean loss, no perturbation); kPair: both signs per
-// probe.  kNS accumulator slots, slot s = probe s / kPer, sign s % kPer.
-template <int kT, int kNP, bool kPair>
-__global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
-                                                  const float *__restrict__ params,
-                                                  uint32_t batch, uint32_t d_in, uint32_t d_hid,
-                                                  uint32_t d_out, double *__restrict__ partial,
-                                                  PertArgs pa)
+// K-groups per staging step of a wave with kNP probes (see tile_body).
+template <int kT, int kNP>
+constexpr uint32_t stage_groups()
+{
+    constexpr uint32_t s16 = kNP >= 8 ? 2 : kNP >= 2 ? 4 : 8;
+    return kT == 16 ? s16 : s16 / 2;
+}
+
+// One wave's tile.  kNP: probes of the wave (0: the clean loss, no perturbation); kPair:
+// both signs per probe; kStage: K-groups per staging step.  kNS accumulator slots, slot s =
+// probe s / kPer, sign s % kPer, written from `partial` on (one slot of partial logits
+// apart).
+template <int kT, int kNP, bool kPair, uint32_t kStage>
+__device__ __forceinline__ void tile_body(const float *__restrict__ X,
+                                          const float *__restrict__ params, uint32_t batch,
+                                          uint32_t d_in, uint32_t d_hid, uint32_t d_out,
+                                          double *__restrict__ partial, PertArgs pa)
 {
     constexpr int kE = kT / 4;          // k values per lane and 16-k group
     constexpr int kV = kE / 4;          // float4 loads per operand and group
@@ -150,11 +159,6 @@ __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
     if ((total & 7u) == 0) t = (t & 7u) * (total >> 3) + (t >> 3);  // XCD-contiguous tiles
     const uint32_t m0 = (t % m_tiles) * kT, nt = t / m_tiles, n0 = nt * kT;
     const uint32_t li = lane % kT, kq = lane / kT;
-    // this wave's probes: kNP of them from pa.probe + blockIdx.y * kNP (slots likewise)
-    if constexpr (kNP > 0) {
-        pa.probe += blockIdx.y * (uint32_t)kNP;
-        if (pa.bits) pa.bits += (uint64_t)blockIdx.y * kNP * pa.bits_stride;
-    }
 
     const float *xrow = X + (uint64_t)(m0 + li) * d_in + (uint32_t)kE * kq;
     const uint64_t wrow = (uint64_t)(n0 + li) * d_in + (uint32_t)kE * kq;   // flat index in params
@@ -256,8 +260,6 @@ __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
     // and wide tiles load twice the operands per group, so shorter stages suffice (and keep
     // the registers from spilling).  The k order, and with it every accumulator's sequence,
     // does not depend on the staging.
-    constexpr uint32_t kStage16 = kNP >= 8 ? 2 : kNP >= 2 ? 4 : 8;
-    constexpr uint32_t kStage = kT == 16 ? kStage16 : kStage16 / 2;
     const uint32_t kfull = (d_in / (16u * kStage)) * (16u * kStage);
     Op a0[kStage], b0[kStage], a1[kStage], b1[kStage];
     auto load_op = [](Op &o, const float *p) {
@@ -302,7 +304,6 @@ __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
     const uint64_t b1_at = (uint64_t)d_hid * d_in;
     const uint64_t w2_at = b1_at + d_hid;
     const uint64_t pset = (uint64_t)n_tiles * batch * d_out;   // one slot's partial logits
-    partial += (uint64_t)blockIdx.y * (kNP > 0 ? kNP * (kPair ? 2 : 1) : 1) * pset;
     const uint32_t n = n0 + li;
     const float b1v = params[b1_at + n];
     // after sum_columns: the lanes that write, and the row each holds
@@ -347,6 +348,36 @@ __global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
     }
 }
 
+// Tiles of kNP probes per wave (gridDim.y groups of them: group y takes probes pa.probe +
+// y kNP onwards and slots y kNS onwards); the workgroups with blockIdx.y == clean_group
+// compute the clean loss into the slot after the probes' (kNP = 0: every wave does).
+template <int kT, int kNP, bool kPair>
+__global__ __launch_bounds__(64) void k_mlp_tiles(const float *__restrict__ X,
+                                                  const float *__restrict__ params,
+                                                  uint32_t batch, uint32_t d_in, uint32_t d_hid,
+                                                  uint32_t d_out, double *__restrict__ partial,
+                                                  PertArgs pa, uint32_t clean_group)
+{
+    if constexpr (kNP > 0) {
+        constexpr uint32_t kNS = (uint32_t)kNP * (kPair ? 2u : 1u);
+        const uint64_t pset = (uint64_t)(d_hid / kT) * batch * d_out;
+        if (blockIdx.y == clean_group) {   // staged like the probes' waves: same registers
+            tile_body<kT, 0, false, stage_groups<kT, kNP>()>(
+                X, params, batch, d_in, d_hid, d_out,
+                partial + (uint64_t)clean_group * kNS * pset, pa);
+            return;
+        }
+        pa.probe += blockIdx.y * (uint32_t)kNP;
+        if (pa.bits) pa.bits += (uint64_t)blockIdx.y * kNP * pa.bits_stride;
+        tile_body<kT, kNP, kPair, stage_groups<kT, kNP>()>(
+            X, params, batch, d_in, d_hid, d_out, partial + (uint64_t)blockIdx.y * kNS * pset,
+            pa);
+    } else {
+        tile_body<kT, 0, false, stage_groups<kT, 0>()>(X, params, batch, d_in, d_hid, d_out,
+                                                        partial, pa);
+    }
+}
+
 template <bool kPert>
 __global__ __launch_bounds__(256) void k_mlp_rows(const double *__restrict__ partial,
                                                   const float *__restrict__ params,
@@ -354,12 +385,14 @@ __global__ __launch_bounds__(256) void k_mlp_rows(const double *__restrict__ par
                                                   uint32_t batch, uint32_t d_in, uint32_t d_hid,
                                                   uint32_t d_out, uint32_t n_tiles,
                                                   double *__restrict__ rowloss, PertArgs pa,
-                                                  uint32_t per)
+                                                  uint32_t per, uint32_t nprobe_slots)
 {
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t m = blockIdx.x * 4u + (threadIdx.x >> 6);
     if (m >= batch) return;
-    // slot blockIdx.y: probe pa.probe + blockIdx.y / per, -alpha for the odd slots of pairs
+    // slot blockIdx.y: probe pa.probe + blockIdx.y / per, -alpha for the odd slots of pairs;
+    // the slot after the probes' (if any) is the clean loss
+    const bool pert = kPert && blockIdx.y < nprobe_slots;
     const uint32_t pi = blockIdx.y / per;
     const float alpha = (blockIdx.y % per) ? -pa.alpha : pa.alpha;
     partial += (uint64_t)blockIdx.y * n_tiles * batch * d_out;
@@ -373,7 +406,7 @@ __global__ __launch_bounds__(256) void k_mlp_rows(const double *__restrict__ par
         for (uint32_t t = lane; t < n_tiles; t += 64) s += row[t];
 #pragma unroll
         for (int w = 32; w >= 1; w >>= 1) s += __shfl_xor(s, w, 64);
-        s += (double)param(params, b2_at + o, pa, pi, alpha, kPert);
+        s += (double)param(params, b2_at + o, pa, pi, alpha, pert);
         z[o] = s;
         zmax = s > zmax ? s : zmax;
     }
@@ -388,12 +421,16 @@ __global__ __launch_bounds__(256) void k_mlp_rows(const double *__restrict__ par
 
 __global__ __launch_bounds__(256) void k_mlp_mean(const double *__restrict__ rowloss,
                                                   uint32_t batch, double *__restrict__ out,
-                                                  double *__restrict__ out2, uint32_t per)
+                                                  double *__restrict__ out2, uint32_t per,
+                                                  uint32_t nprobe_slots,
+                                                  double *__restrict__ out_clean)
 {
     __shared__ double red[256];
-    // slot blockIdx.x: probe blockIdx.x / per; the -alpha slot of a pair writes to out2
+    // slot blockIdx.x: probe blockIdx.x / per; the -alpha slot of a pair writes to out2; the
+    // slot after the probes' writes out_clean
     rowloss += (uint64_t)blockIdx.x * batch;
-    out = ((blockIdx.x % per) ? out2 : out) + blockIdx.x / per;
+    out = blockIdx.x >= nprobe_slots ? out_clean
+                                     : ((blockIdx.x % per) ? out2 : out) + blockIdx.x / per;
     double acc = 0.0;
     for (uint32_t m = threadIdx.x; m < batch; m += blockDim.x) acc += rowloss[m];
     red[threadIdx.x] = acc;
@@ -405,25 +442,28 @@ __global__ __launch_bounds__(256) void k_mlp_mean(const double *__restrict__ row
     if (threadIdx.x == 0) *out = red[0] / (double)batch;
 }
 
-// One launch sequence: tiles (kNP probes per wave, `groups` probe groups), row losses, means.
+// One launch sequence: tiles (kNP probes per wave, `groups` probe groups, and with
+// out_clean one more group for the clean loss), row losses, means.
 template <int kT, int kNP, bool kPair>
 static void launch_chain(const float *params, const float *X, const int64_t *labels,
                          uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out,
                          double *partial, double *out, double *out2, const PertArgs &pa,
-                         hipStream_t stream, uint32_t groups = 1)
+                         hipStream_t stream, uint32_t groups = 1, double *out_clean = nullptr)
 {
     const uint32_t n_tiles = d_hid / kT;
     const uint32_t tiles = (batch / kT) * n_tiles;
     const uint32_t per = kPair ? 2u : 1u;
-    const uint32_t nslot = kNP > 0 ? (uint32_t)kNP * per * groups : 1u;
-    double *rowloss = partial + (uint64_t)nslot * n_tiles * batch * d_out;
-    hipLaunchKernelGGL((k_mlp_tiles<kT, kNP, kPair>), dim3(tiles, groups), dim3(64), 0, stream,
-                       X, params, batch, d_in, d_hid, d_out, partial, pa);
-    hipLaunchKernelGGL(k_mlp_rows<(kNP > 0)>, dim3((batch + 3) / 4, nslot), dim3(256), 0, stream,
-                       partial, params, labels, batch, d_in, d_hid, d_out, n_tiles, rowloss, pa,
-                       per);
-    hipLaunchKernelGGL(k_mlp_mean, dim3(nslot), dim3(256), 0, stream, rowloss, batch, out, out2,
-                       per);
+    const uint32_t nslot = kNP > 0 ? (uint32_t)kNP * per * groups : 1u;   // probe slots
+    const uint32_t clean = (kNP > 0 && out_clean) ? 1u : 0u;
+    double *rowloss = partial + (uint64_t)(nslot + clean) * n_tiles * batch * d_out;
+    hipLaunchKernelGGL((k_mlp_tiles<kT, kNP, kPair>), dim3(tiles, groups + clean), dim3(64), 0,
+                       stream, X, params, batch, d_in, d_hid, d_out, partial, pa,
+                       clean ? groups : 0xFFFFFFFFu);
+    hipLaunchKernelGGL(k_mlp_rows<(kNP > 0)>, dim3((batch + 3) / 4, nslot + clean), dim3(256), 0,
+                       stream, partial, params, labels, batch, d_in, d_hid, d_out, n_tiles,
+                       rowloss, pa, per, nslot);
+    hipLaunchKernelGGL(k_mlp_mean, dim3(nslot + clean), dim3(256), 0, stream, rowloss, batch, out,
+                       out2, per, nslot, out_clean);
 }
 
 // Every launch for one shape uses the same tile kernel, so the k order of each hidden unit's
@@ -504,10 +544,13 @@ hipError_t launch_mlp_loss_probes(const float *params, const float *X, const int
                                   uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out,
                                   double *partial, const MlpPerturb &pert, uint32_t nprobes,
                                   Key key, double *out_plus, double *out_minus,
-                                  hipStream_t stream)
+                                  double *out_clean, hipStream_t stream)
 {
     const uint64_t nparams = mlp_params(d_in, d_hid, d_out);
     const uint32_t pw = mlp_probes_per_wave();
+    if (nprobes == 0 && out_clean)
+        return launch_mlp_loss(params, X, labels, batch, d_in, d_hid, d_out, partial, out_clean,
+                               nullptr, key, stream);
     // launch sequences of 64 probes, then 32, 16, ..., 1 for the rest, each with min(pw, size)
     // probes per wave; each reuses the workspace from its start (they run in stream order)
     for (uint32_t done = 0; done < nprobes;) {
@@ -520,20 +563,21 @@ hipError_t launch_mlp_loss_probes(const float *params, const float *X, const int
         if (pert.bits) p.bits = pert.bits + (uint64_t)done * ((nparams + 127) / 128 * 16);
         const PertArgs pa = pert_args(&p, key, nparams);
         double *op = out_plus + done, *om = out_minus + done;
+        double *oc = done == 0 ? out_clean : nullptr;   // the first sequence adds the clean loss
         if (wide_tiles(batch, d_hid)) {
             // at most 4 probes per wave: 8 would hold 256 accumulator registers
             switch (w) {
             case 8:
-            case 4: launch_chain<32, 4, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 4); break;
-            case 2: launch_chain<32, 2, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 2); break;
-            default: launch_chain<32, 1, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k); break;
+            case 4: launch_chain<32, 4, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 4, oc); break;
+            case 2: launch_chain<32, 2, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 2, oc); break;
+            default: launch_chain<32, 1, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k, oc); break;
             }
         } else {
             switch (w) {
-            case 8: launch_chain<16, 8, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 8); break;
-            case 4: launch_chain<16, 4, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 4); break;
-            case 2: launch_chain<16, 2, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 2); break;
-            default: launch_chain<16, 1, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k); break;
+            case 8: launch_chain<16, 8, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 8, oc); break;
+            case 4: launch_chain<16, 4, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 4, oc); break;
+            case 2: launch_chain<16, 2, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k / 2, oc); break;
+            default: launch_chain<16, 1, true>(params, X, labels, batch, d_in, d_hid, d_out, partial, op, om, pa, stream, k, oc); break;
             }
         }
         const hipError_t e = hipGetLastError();

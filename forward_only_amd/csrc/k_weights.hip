@@ -223,10 +223,6 @@ __global__ __launch_bounds__(256) void k_sum_partials(const double *__restrict__
 // wave's lanes produce the 16 x kQuadProbes blocks' bits once (one Philox call or one
 // 16-byte row read per lane) into an LDS slice laid out [block][word][probe], and each lane
 // reads, per group of 4 params, one 16-byte vector holding that word of every probe.
-// The four params' terms for every probe and sign.  A perturbed value is one of two
-// candidates, rnd(x + alpha) and rnd(x - alpha) (what zo_perturb stores for a set and for a
-// clear sign bit under +alpha, and the other way round under -alpha), so both are formed
-// and squared once per param and each probe's sign bit picks between them.
 // m ? a : b for a lane mask m of all ones or all zeros, word by word.
 __device__ __forceinline__ double select_f64(uint32_t m, double a, double b)
 {
@@ -236,8 +232,14 @@ __device__ __forceinline__ double select_f64(uint32_t m, double a, double b)
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-template <bool kBF16>
-__device__ __forceinline__ void quad_terms4(double (&acc)[2 * kQuadProbes], const float (&x)[4],
+// The four params' terms for every probe and sign.  A perturbed value is one of two
+// candidates, rnd(x + alpha) and rnd(x - alpha) (what zo_perturb stores for a set and for a
+// clear sign bit under +alpha, and the other way round under -alpha), so both are formed
+// and squared once per param and each probe's sign bit picks between them.  With kClean the
+// last accumulator also takes the unperturbed terms, as the single-probe loss kernel forms
+// them.
+template <bool kBF16, bool kClean>
+__device__ __forceinline__ void quad_terms4(double (&acc)[2 * kQuadProbes + kClean], const float (&x)[4],
                                             const float (&av)[4], const uint32_t (&w)[kQuadProbes],
                                             uint32_t sh, float alpha)
 {
@@ -263,6 +265,7 @@ __device__ __forceinline__ void quad_terms4(double (&acc)[2 * kQuadProbes], cons
     for (int q = 0; q < 4; ++q) {
         const double ta = (double)xa[q], tb = (double)xb[q];
         const double sa = ta * ta, sb = tb * tb, ad = (double)av[q];
+        if constexpr (kClean) acc[2 * kQuadProbes] = quad_term(acc[2 * kQuadProbes], av[q], (double)x[q]);
 #pragma unroll
         for (uint32_t i = 0; i < kQuadProbes; ++i) {
             // all ones where the probe's bit is set: one bit-field extract, then bitwise
@@ -275,7 +278,7 @@ __device__ __forceinline__ void quad_terms4(double (&acc)[2 * kQuadProbes], cons
     }
 }
 
-template <bool kBF16, bool kBits>
+template <bool kBF16, bool kBits, bool kClean>
 __global__ __launch_bounds__(256) void k_quad_probes_partial(
     const void *__restrict__ theta, const float *__restrict__ a, uint64_t n, uint64_t blk0,
     uint32_t step, uint32_t probe0, uint32_t nvalid, uint32_t k0, uint32_t k1, float alpha,
@@ -283,9 +286,10 @@ __global__ __launch_bounds__(256) void k_quad_probes_partial(
 {
     __shared__ double red[4];
     __shared__ __attribute__((aligned(16))) uint32_t xch[4][16 * 4 * kQuadProbes];
-    double acc[2 * kQuadProbes];
+    constexpr uint32_t kNAcc = 2 * kQuadProbes + kClean;   // slot 2 kQuadProbes: the clean loss
+    double acc[kNAcc];
 #pragma unroll
-    for (uint32_t s = 0; s < 2 * kQuadProbes; ++s) acc[s] = 0.0;
+    for (uint32_t s = 0; s < kNAcc; ++s) acc[s] = 0.0;
     const uint64_t G = (uint64_t)gridDim.x * blockDim.x;
     const uint64_t tid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const uint32_t lane = threadIdx.x & 63u;
@@ -354,11 +358,12 @@ __global__ __launch_bounds__(256) void k_quad_probes_partial(
             const uint32_t w[kQuadProbes] = {wq[0], wq[1], wq[2], wq[3]};
             const float x[4] = {xv[k][0], xv[k][1], xv[k][2], xv[k][3]};
             const float aa[4] = {av[k][0], av[k][1], av[k][2], av[k][3]};
-            quad_terms4<kBF16>(acc, x, aa, w, sh, alpha);
+            quad_terms4<kBF16, kClean>(acc, x, aa, w, sh, alpha);
         }
     }
     for (uint64_t j = nchunks * kLossChunk + tid; j < n; j += G) {   // ragged end
         const float xj = (float)theta1<kBF16>(theta, j);
+        if constexpr (kClean) acc[2 * kQuadProbes] = quad_term(acc[2 * kQuadProbes], a[j], (double)xj);
 #pragma unroll
         for (uint32_t i = 0; i < kQuadProbes; ++i) {
             uint32_t bit = 0;
@@ -386,50 +391,62 @@ __global__ __launch_bounds__(256) void k_quad_probes_partial(
         }
     }
 #pragma unroll
-    for (uint32_t s = 0; s < 2 * kQuadProbes; ++s) {
+    for (uint32_t s = 0; s < kNAcc; ++s) {
         const double v = block_sum256(acc[s], red);
         if (threadIdx.x == 0) part[(uint64_t)s * kLossPartials + blockIdx.x] = v;
     }
 }
 
-// Slot s of the fused pass (probe s / 2, sign s % 2): the partials summed exactly as
-// k_sum_partials sums them, into out_plus / out_minus.
+// Slot s < nprobe_slots of the fused pass (probe s / 2, sign s % 2), and for one more
+// workgroup the clean slot 2 kQuadProbes: the partials summed exactly as k_sum_partials
+// sums them, into out_plus / out_minus / out_clean.
 __global__ __launch_bounds__(256) void k_sum_partials_slots(const double *__restrict__ part,
                                                             uint32_t count, double scale,
                                                             double *__restrict__ out_plus,
-                                                            double *__restrict__ out_minus)
+                                                            double *__restrict__ out_minus,
+                                                            uint32_t nprobe_slots,
+                                                            double *__restrict__ out_clean)
 {
     __shared__ double red[4];
-    const uint32_t s = blockIdx.x;
+    const uint32_t s = blockIdx.x < nprobe_slots ? blockIdx.x : 2 * kQuadProbes;
     part += (uint64_t)s * count;
     double acc = 0.0;
     for (uint32_t i = threadIdx.x; i < count; i += blockDim.x) acc += part[i];
     const double v = block_sum256(acc, red);
-    if (threadIdx.x == 0) ((s & 1u) ? out_minus : out_plus)[s >> 1] = scale * v;
+    if (threadIdx.x == 0) {
+        double *out = blockIdx.x >= nprobe_slots ? out_clean : (s & 1u) ? out_minus + (s >> 1)
+                                                                        : out_plus + (s >> 1);
+        *out = scale * v;
+    }
 }
 
 hipError_t launch_quad_loss_probes(const void *theta, bool bf16, const float *a, uint64_t offset,
                                    uint64_t n, Key key, uint32_t step, uint32_t probe0,
                                    uint32_t nprobes, float alpha, const uint8_t *bits,
                                    double *partials, double *out_plus, double *out_minus,
-                                   hipStream_t stream)
+                                   double *out_clean, hipStream_t stream)
 {
     const uint64_t stride = (n + kBlockParams - 1) / kBlockParams * 16u;
+    if (nprobes == 0 && out_clean) return launch_quad_loss(theta, bf16, a, n, partials, out_clean, stream);
     for (uint32_t done = 0; done < nprobes; done += kQuadProbes) {
         const uint32_t nvalid = nprobes - done < kQuadProbes ? nprobes - done : kQuadProbes;
         const uint8_t *b = bits ? bits + (uint64_t)done * stride : nullptr;
-#define ZO_QP(BF, BI)                                                                         \
-    hipLaunchKernelGGL((k_quad_probes_partial<BF, BI>), dim3(kLossPartials), dim3(256), 0,     \
+        const bool clean = out_clean && done == 0;   // the first pass also sums the clean loss
+#define ZO_QP(BF, BI, CL)                                                                     \
+    hipLaunchKernelGGL((k_quad_probes_partial<BF, BI, CL>), dim3(kLossPartials), dim3(256), 0, \
                        stream, theta, a, n, offset / kBlockParams, step, probe0 + done, nvalid, \
                        key.k0, key.k1, alpha, b, stride, partials)
+#define ZO_QP2(BF, BI) do { if (clean) ZO_QP(BF, BI, true); else ZO_QP(BF, BI, false); } while (0)
         if (bf16) {
-            if (b) ZO_QP(true, true); else ZO_QP(true, false);
+            if (b) ZO_QP2(true, true); else ZO_QP2(true, false);
         } else {
-            if (b) ZO_QP(false, true); else ZO_QP(false, false);
+            if (b) ZO_QP2(false, true); else ZO_QP2(false, false);
         }
+#undef ZO_QP2
 #undef ZO_QP
-        hipLaunchKernelGGL(k_sum_partials_slots, dim3(2 * nvalid), dim3(256), 0, stream, partials,
-                           kLossPartials, 0.5, out_plus + done, out_minus + done);
+        hipLaunchKernelGGL(k_sum_partials_slots, dim3(2 * nvalid + (clean ? 1u : 0u)), dim3(256),
+                           0, stream, partials, kLossPartials, 0.5, out_plus + done,
+                           out_minus + done, 2 * nvalid, out_clean);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

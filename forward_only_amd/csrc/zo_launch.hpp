@@ -79,12 +79,14 @@ hipError_t launch_quad_loss(const void *theta, bool bf16, const float *a, uint64
 constexpr uint32_t kQuadProbes = 4;   // probes per pass of the fused quadratic losses
 // The same loss at theta +/- alpha z_i for n_probes consecutive probes from probe0, theta
 // read once per kQuadProbes probes and never written; each loss bit-equal to zo_perturb
-// followed by launch_quad_loss.  `partials` as for launch_quad_loss (2 kQuadProbes slots).
+// followed by launch_quad_loss.  With out_clean the first pass also sums the loss at theta
+// itself, bit-equal to launch_quad_loss.  `partials` as for launch_quad_loss (2 kQuadProbes
+// + 1 slots).
 hipError_t launch_quad_loss_probes(const void *theta, bool bf16, const float *a, uint64_t offset,
                                    uint64_t n, Key key, uint32_t step, uint32_t probe0,
                                    uint32_t nprobes, float alpha, const uint8_t *bits,
                                    double *partials, double *out_plus, double *out_minus,
-                                   hipStream_t stream);
+                                   double *out_clean, hipStream_t stream);
 
 // 1/2 sum a_j theta_j^2 + 1/2 ||U theta||^2, U row-major [r][n], r <= kLowRankMax;
 // `partials` holds kLossPartials * (kLowRankMax + 1) doubles.
@@ -111,15 +113,17 @@ hipError_t launch_mlp_loss(const float *params, const float *X, const int64_t *l
 // Both losses of probes pert.probe .. pert.probe + nprobes - 1 (out_plus[i], out_minus[i]),
 // up to kMlpProbesPerLaunch probes per launch sequence, kMlpProbesPerWave of them per wave
 // sharing every operand load (ZO_MLP_PROBES_PER_WAVE overrides: 1, 2, 4, 8; 4 at most on 32-wide tiles); pert.bits (if
-// given) holds nprobes packed rows.  The workspace holds 2 * min(nprobes,
-// kMlpProbesPerLaunch) slots of partial logits and row losses.
+// given) holds nprobes packed rows.  With out_clean the first launch sequence also computes
+// the loss at the unperturbed parameters (bit-equal to launch_mlp_loss without pert).  The
+// workspace holds 2 * min(nprobes, kMlpProbesPerLaunch) + 1 slots of partial logits and row
+// losses.
 constexpr uint32_t kMlpProbesPerLaunch = 64;
 constexpr uint32_t kMlpProbesPerWave = 2;
 hipError_t launch_mlp_loss_probes(const float *params, const float *X, const int64_t *labels,
                                   uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out,
                                   double *partial, const MlpPerturb &pert, uint32_t nprobes,
                                   Key key, double *out_plus, double *out_minus,
-                                  hipStream_t stream);
+                                  double *out_clean, hipStream_t stream);
 
 // Diagnostic: every 16-byte word of buf (bytes % 16 == 0) <- word ^ mask, in place;
 // slice_bytes > 0 (a multiple of 8 KiB) issues it as one launch per slice of that size.

@@ -92,7 +92,7 @@ def spsa_step(ctx, theta: torch.Tensor, *, step: int, npert: int, eps: float, et
 def spsa_step_fused(ctx, theta: torch.Tensor, *, step: int, npert: int, eps: float, eta: float,
                     delta: float, loss_at, offset: int = 0, bits=None,
                     buffers: dict | None = None, loss_pair_at=None,
-                    loss_probes_at=None) -> dict:
+                    loss_probes_at=None, probes_give_clean: bool = False) -> dict:
     """One step whose forward applies each probe while reading the parameters.
 
     loss_at(probe, alpha, row, out) writes the loss at theta + alpha * z_probe (probe None:
@@ -100,7 +100,10 @@ def spsa_step_fused(ctx, theta: torch.Tensor, *, step: int, npert: int, eps: flo
     zo_mlp_loss_perturbed: no perturb or restore pass over the parameters at all.  With
     loss_pair_at(probe, alpha, row, out_plus, out_minus) (zo_mlp_loss_pair) each probe's two
     losses come from one call; with loss_probes_at(probe0, n, alpha, rows, out_plus,
-    out_minus) (zo_mlp_loss_probes) all probes' losses come from one call.
+    out_minus) (zo_mlp_loss_probes) all probes' losses come from one call; with
+    probes_give_clean it is called with a seventh argument, the clean loss's output, which it
+    fills from the same call (the out_clean of zo_mlp_loss_probes / zo_quad_loss_probes), and
+    loss_at is not called.
     """
     a = applied_eps(eps)
     b = buffers if buffers is not None else {}
@@ -108,9 +111,12 @@ def spsa_step_fused(ctx, theta: torch.Tensor, *, step: int, npert: int, eps: flo
     L0 = b.get("L0") if b.get("L0") is not None else torch.empty(1, dtype=torch.float64, device=dev)
     Lp = b.get("Lp") if b.get("Lp") is not None else torch.empty(npert, dtype=torch.float64, device=dev)
     Lm = b.get("Lm") if b.get("Lm") is not None else torch.empty(npert, dtype=torch.float64, device=dev)
-    loss_at(None, 0.0, None, L0)
-    if loss_probes_at is not None and npert > 0:
-        loss_probes_at(0, npert, +a, bits, Lp, Lm)
+    if loss_probes_at is not None and probes_give_clean:
+        loss_probes_at(0, npert, +a, bits, Lp, Lm, L0)
+    else:
+        loss_at(None, 0.0, None, L0)
+        if loss_probes_at is not None and npert > 0:
+            loss_probes_at(0, npert, +a, bits, Lp, Lm)
     for i in range(npert if loss_probes_at is None else 0):
         row = None if bits is None else bits[i]
         if loss_pair_at is not None:

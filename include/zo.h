@@ -234,16 +234,19 @@ zo_status zo_quad_loss(zo_ctx *ctx, const void *d_theta, zo_dtype dtype, const f
  * order of terms and reductions).  Layouts as zo_quad_loss; offset as zo_perturb (a multiple
  * of 128: the global index of theta[0]); d_bits: NULL to regenerate the signs, else
  * n_probes packed rows of zo_bits_stride(n) bytes each (row i for probe probe0 + i), 16-byte
- * aligned; d_out_plus, d_out_minus: device, n_probes doubles each.  Uses the context's loss
- * partials, so calls on one context are ordered by their streams.  Errors (ZO_EINVAL): as
- * zo_quad_loss, offset % 128 != 0 or range overflow, probe indices wrapping past 2^32,
- * misaligned d_bits, NULL outputs (with n_probes > 0).  n_probes == 0 is a no-op; n == 0
- * writes zeros. */
+ * aligned; d_out_plus, d_out_minus: device, n_probes doubles each.  d_out_clean: NULL, or
+ * one device double that also receives the loss at theta itself (the step's clean pass),
+ * equal bit for bit to zo_quad_loss, summed in the first pass over theta instead of a pass
+ * of its own.  Uses the context's loss partials, so calls on one context are ordered by
+ * their streams.  Errors (ZO_EINVAL): as zo_quad_loss, offset % 128 != 0 or range overflow,
+ * probe indices wrapping past 2^32, misaligned d_bits, NULL outputs (with n_probes > 0).
+ * n_probes == 0 computes only the clean loss (nothing without d_out_clean); n == 0 writes
+ * zeros. */
 zo_status zo_quad_loss_probes(zo_ctx *ctx, const void *d_theta, zo_dtype dtype,
                               const float *d_a, uint64_t offset, uint64_t n, uint32_t step,
                               uint32_t probe0, uint32_t n_probes, float alpha,
                               const uint8_t *d_bits, double *d_out_plus, double *d_out_minus,
-                              void *stream);
+                              double *d_out_clean, void *stream);
 
 /* Low-rank-plus-diagonal quadratic loss L = 1/2 sum_j a_j theta_j^2 + 1/2 ||U theta||^2,
  * fp64 accumulation, deterministic.  A synthetic model whose curvature along a probe,
@@ -317,11 +320,14 @@ zo_status zo_mlp_loss_pair(zo_ctx *ctx, const float *d_params, uint64_t offset, 
  * the MFMA GEMM running two probes (ZO_MLP_PROBES_PER_WAVE: 1, 2, 4 or 8; at most 4 on 32 x 32 tiles) so that every X
  * and W1 operand it loads feeds both signs of each.  d_bits: NULL
  * (regenerate) or n_probes packed rows over the parameters, row i = probe probe0 + i
- * (zo_bits_stride(params) bytes apart, 16-byte aligned).  d_workspace: device, 8-byte aligned,
- * at least zo_mlp_probes_workspace_bytes(batch, d_in, d_hid, d_out, n_probes) bytes.  Other
- * arguments and limits as zo_mlp_loss_perturbed.  n_probes == 0 is an empty call.
- * Errors (ZO_EINVAL): as zo_mlp_loss_pair, a workspace below that size, probe indices past
- * 2^32 - 1, misaligned d_bits. */
+ * (zo_bits_stride(params) bytes apart, 16-byte aligned).  d_loss_clean: NULL, or one device
+ * double that also receives the loss at the unperturbed parameters (the step's clean pass),
+ * equal bit for bit to zo_mlp_loss, computed by one more group of waves in the first launch
+ * sequence.  d_workspace: device, 8-byte aligned, at least
+ * zo_mlp_probes_workspace_bytes(batch, d_in, d_hid, d_out, n_probes) bytes.  Other
+ * arguments and limits as zo_mlp_loss_perturbed.  n_probes == 0 computes only the clean
+ * loss (nothing without d_loss_clean).  Errors (ZO_EINVAL): as zo_mlp_loss_pair, a
+ * workspace below that size, probe indices past 2^32 - 1, misaligned d_bits. */
 uint64_t zo_mlp_probes_workspace_bytes(uint32_t batch, uint32_t d_in, uint32_t d_hid,
                                        uint32_t d_out, uint32_t n_probes);
 zo_status zo_mlp_loss_probes(zo_ctx *ctx, const float *d_params, uint64_t offset, uint32_t step,
@@ -329,7 +335,7 @@ zo_status zo_mlp_loss_probes(zo_ctx *ctx, const float *d_params, uint64_t offset
                              const uint8_t *d_bits, const float *d_X, const int64_t *d_labels,
                              uint32_t batch, uint32_t d_in, uint32_t d_hid, uint32_t d_out,
                              void *d_workspace, uint64_t workspace_bytes, double *d_loss_plus,
-                             double *d_loss_minus, void *stream);
+                             double *d_loss_minus, double *d_loss_clean, void *stream);
 
 /* zo_mlp_loss_pair for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the same kernels and the

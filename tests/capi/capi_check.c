@@ -192,14 +192,16 @@ int main(void)
     }
 
     /* 6. the quadratic loss at theta +/- alpha z_i of three probes, theta read once and not
-     *    written: each loss within the fp64 summation bound of the oracle's perturb + loss */
+     *    written: each loss within the fp64 summation bound of the oracle's perturb + loss;
+     *    the clean loss from the same pass equal to zo_quad_loss and within that bound of
+     *    the oracle's loss at theta */
     {
         const uint64_t n = 30011, offset = 256;
         const uint32_t np = 3, step = 4, probe0 = 6;
         const float alpha = 0x1p-10f;
         float *h = malloc(n * 4), *a = malloc(n * 4), *w = malloc(n * 4), *g = malloc(n * 4);
         float *dt = NULL, *da = NULL;
-        double *dp = NULL, *dm = NULL, lp[3], lm[3];
+        double *dp = NULL, *dm = NULL, *dc = NULL, *dq = NULL, lp[3], lm[3], lc, lq;
         for (uint64_t i = 0; i < n; ++i) {
             h[i] = (float)((sm_uniform() - 0.5) * 2.0);
             a[i] = (float)(0.1 + sm_uniform());
@@ -208,10 +210,20 @@ int main(void)
         HIPCHK(hipMalloc((void **)&da, n * 4));
         HIPCHK(hipMalloc((void **)&dp, np * 8));
         HIPCHK(hipMalloc((void **)&dm, np * 8));
+        HIPCHK(hipMalloc((void **)&dc, 8));
+        HIPCHK(hipMalloc((void **)&dq, 8));
         HIPCHK(hipMemcpy(dt, h, n * 4, hipMemcpyHostToDevice));
         HIPCHK(hipMemcpy(da, a, n * 4, hipMemcpyHostToDevice));
         ZOCHK(zo_quad_loss_probes(ctx, dt, ZO_FP32, da, offset, n, step, probe0, np, alpha, NULL,
-                                  dp, dm, NULL));
+                                  dp, dm, dc, NULL));
+        ZOCHK(zo_quad_loss(ctx, dt, ZO_FP32, da, n, dq, NULL));
+        HIPCHK(hipMemcpy(&lc, dc, 8, hipMemcpyDeviceToHost));
+        HIPCHK(hipMemcpy(&lq, dq, 8, hipMemcpyDeviceToHost));
+        if (memcmp(&lc, &lq, 8) != 0) FAIL("fused clean loss differs from zo_quad_loss");
+        {
+            const double ref = ora_quad_loss_f32(h, a, n);
+            if (fabs(lc - ref) > 4.0 * (double)n * 0x1p-53 * fabs(ref)) FAIL("fused clean loss");
+        }
         HIPCHK(hipMemcpy(lp, dp, np * 8, hipMemcpyDeviceToHost));
         HIPCHK(hipMemcpy(lm, dm, np * 8, hipMemcpyDeviceToHost));
         HIPCHK(hipMemcpy(g, dt, n * 4, hipMemcpyDeviceToHost));
@@ -229,6 +241,8 @@ int main(void)
         HIPCHK(hipFree(da));
         HIPCHK(hipFree(dp));
         HIPCHK(hipFree(dm));
+        HIPCHK(hipFree(dc));
+        HIPCHK(hipFree(dq));
         free(h);
         free(a);
         free(w);

@@ -121,17 +121,20 @@ def test_pair_equals_two_fused_calls(ctx, shape, mode):
 @pytest.mark.parametrize("nprobes", [1, 3, 8, 13, 21, 70])
 def test_probes_equal_pairs(ctx, shape, mode, nprobes):
     """zo_mlp_loss_probes gives, for every probe of the batch, exactly the losses of
-    zo_mlp_loss_pair (21 probes run as launch sequences of 16, 4 and 1 probes, 13 as 8, 4
-    and 1, each with several probes per wave); parameters untouched."""
+    zo_mlp_loss_pair (70 probes run as launch sequences of 64, 4 and 2 probes, 21 as 16, 4
+    and 1, 13 as 8, 4 and 1, each with several probes per wave), and with out_clean exactly
+    zo_mlp_loss from the first sequence's extra wave group; parameters untouched."""
     batch, d_in, d_hid, d_out = shape
     theta, X, y = _problem(*shape, seed=57 + sum(shape) + nprobes)
     t, x, yl = _dev(theta, X, y)
     M = theta.size
     probe0, step, alpha = 5, 6, 1e-3
     rows = zo.zo_gen_probes(ctx, step, probe0, nprobes, 0, M) if mode == "bits" else None
+    clean = torch.full((1,), np.nan, dtype=torch.float64, device="cuda")
     lp, lm = zo.zo_mlp_loss_probes(ctx, t, 0, step, probe0, nprobes, alpha, x, yl, d_hid, d_out,
-                                   bits=rows)
+                                   bits=rows, out_clean=clean)
     gp, gm = lp.cpu().numpy(), lm.cpu().numpy()
+    assert clean.item() == zo.zo_mlp_loss(ctx, t, x, yl, d_hid, d_out).item()
     for i in range(nprobes):
         sp, sm = zo.zo_mlp_loss_pair(ctx, t, 0, step, probe0 + i, alpha, x, yl, d_hid, d_out,
                                      bits=None if rows is None else rows[i])
@@ -144,22 +147,28 @@ def test_probes_argument_checks(ctx):
     theta, X, y = _problem(16, 16, 16, 2, seed=1)
     t, x, yl = _dev(theta, X, y)
     L = zo._lib.lib()
+    # one slot (partial logits and row losses of one loss) per sign and probe of the first
+    # launch sequence (64 probes), plus one for the clean loss; the pair call holds two
+    unit = zo.zo_mlp_workspace_bytes(16, 16, 16, 2) // 2
     need = zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 5)
-    full = zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 64)
-    assert zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 100) == full   # 64 per launch
-    assert need * 64 == full * 5
-    assert zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 1) == zo.zo_mlp_workspace_bytes(16, 16, 16, 2)
+    assert need == 11 * unit
+    assert zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 64) == 129 * unit
+    assert zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 100) == 129 * unit   # 64 per launch
+    assert zo.zo_mlp_probes_workspace_bytes(16, 16, 16, 2, 0) == unit
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-    out = torch.empty(10, dtype=torch.float64, device="cuda")
-    args = lambda n, minus, wbytes=need, probe0=0: L.zo_mlp_loss_probes(  # noqa: E731
+    out = torch.full((12,), np.nan, dtype=torch.float64, device="cuda")
+    args = lambda n, minus, wbytes=need, probe0=0, clean=None: L.zo_mlp_loss_probes(  # noqa: E731
         ctx.handle, t.data_ptr(), 0, 0, probe0, n, 1e-3, None, x.data_ptr(), yl.data_ptr(), 16,
-        16, 16, 2, ws.data_ptr(), wbytes, out.data_ptr(), minus, None)
+        16, 16, 2, ws.data_ptr(), wbytes, out.data_ptr(), minus, clean, None)
     assert args(5, None) == zo.ZO_EINVAL                                  # no -alpha outputs
     assert args(5, out.data_ptr() + 40, wbytes=need - 8) == zo.ZO_EINVAL  # workspace
     assert args(5, out.data_ptr() + 40, probe0=2 ** 32 - 3) == zo.ZO_EINVAL  # probe wraps
     assert args(0, None) == zo.ZO_OK                                      # empty
     assert args(5, out.data_ptr() + 40) == zo.ZO_OK
+    assert args(0, None, wbytes=unit, clean=out.data_ptr() + 80) == zo.ZO_OK   # clean only
+    assert args(0, None, wbytes=unit - 8, clean=out.data_ptr() + 80) == zo.ZO_EINVAL
     torch.cuda.synchronize()
+    assert out[10].item() == zo.zo_mlp_loss(ctx, t, x, yl, 16, 2).item()
     with pytest.raises(ValueError):
         zo.zo_mlp_loss_probes(ctx, t, 0, 0, 0, 5, 1e-3, x, yl, 16, 2,
                               bits=zo.zo_gen_probes(ctx, 0, 0, 4, 0, theta.size))  # 4 rows for 5
@@ -199,9 +208,9 @@ def test_mlp_argument_checks(ctx):
 
 
 def test_pair_step_equals_single_call_step():
-    """A whole MLP-workload step with paired forwards, and one with all probes in one batched
-    call, equal the step with single fused forwards bit for bit: losses, weights and the
-    updated parameters."""
+    """A whole MLP-workload step with paired forwards, one with all probes in one batched
+    call, and one whose batched call also gives the clean loss, equal the step with single
+    fused forwards bit for bit: losses, weights and the updated parameters."""
     cfg = CONFIGS["mlp"]
     e = cfg.extra
     npert, step = 32, 3
@@ -209,7 +218,7 @@ def test_pair_step_equals_single_call_step():
     X, y = gen.mlp_data(cfg)
     x, yl = to_dev_f32(X), torch.from_numpy(y).cuda()
     results = []
-    for form in ("single", "paired", "batched"):
+    for form in ("single", "paired", "batched", "batched+clean"):
         local = zo.zo_init(cfg.seed)
         t = to_dev_f32(theta)
         ws = torch.empty(zo.zo_mlp_probes_workspace_bytes(e["batch"], e["d_in"], e["d_hid"],
@@ -227,15 +236,17 @@ def test_pair_step_equals_single_call_step():
             zo.zo_mlp_loss_pair(local, t, 0, step, probe, alpha, x, yl, e["d_hid"], e["d_out"],
                                 bits=row, workspace=ws, out_plus=op, out_minus=om)
 
-        def probes_at(probe0, n, alpha, rows, op, om):
+        def probes_at(probe0, n, alpha, rows, op, om, oc=None):
             zo.zo_mlp_loss_probes(local, t, 0, step, probe0, n, alpha, x, yl, e["d_hid"],
-                                  e["d_out"], bits=rows, workspace=ws, out_plus=op, out_minus=om)
+                                  e["d_out"], bits=rows, workspace=ws, out_plus=op, out_minus=om,
+                                  out_clean=oc)
 
         out = spsa_step_fused(local, t, step=step, npert=npert, eps=cfg.eps, eta=cfg.eta,
                               delta=cfg.delta, loss_at=loss_at,
                               loss_pair_at=pair_at if form == "paired" else None,
-                              loss_probes_at=probes_at if form == "batched" else None)
-        results.append((out["Lp"].cpu().numpy(), out["Lm"].cpu().numpy(),
+                              loss_probes_at=probes_at if form.startswith("batched") else None,
+                              probes_give_clean=form == "batched+clean")
+        results.append((out["L0"].cpu().numpy(), out["Lp"].cpu().numpy(), out["Lm"].cpu().numpy(),
                         out["c"].cpu().numpy(), t.cpu().numpy()))
         local.close()
     for other in results[1:]:
@@ -253,8 +264,8 @@ def test_mlp_config_fused_step(ctx, mode):
     smallest curvature |h_i| of this workload's 64 probes is ~10 against a loss-difference
     term of ~0.3); theta within the update tolerance plus eta * sum of those bounds; the
     GPU's parameters are untouched by the 64 x 2 perturbed forwards (only the update moves
-    them).  The GPU side runs the benchmark's calls: the clean loss and one batched call for
-    all 64 probes' losses."""
+    them).  The GPU side runs the benchmark's call: one batched call for all 64 probes'
+    losses and the clean loss."""
     cfg = CONFIGS["mlp"]
     e = cfg.extra
     npert, step = cfg.npert, 0
@@ -273,13 +284,15 @@ def test_mlp_config_fused_step(ctx, mode):
             zo.zo_mlp_loss_perturbed(local, t, 0, step, probe, alpha, x, yl, e["d_hid"],
                                      e["d_out"], bits=row, workspace=ws, out=out)
 
-    def probes_at(probe0, n, alpha, rows, op, om):
+    def probes_at(probe0, n, alpha, rows, op, om, oc):
         zo.zo_mlp_loss_probes(local, t, 0, step, probe0, n, alpha, x, yl, e["d_hid"],
-                              e["d_out"], bits=rows, workspace=ws, out_plus=op, out_minus=om)
+                              e["d_out"], bits=rows, workspace=ws, out_plus=op, out_minus=om,
+                              out_clean=oc)
 
     bits = zo.zo_gen_probes(local, step, 0, npert, 0, cfg.M) if mode == "bits" else None
     out = spsa_step_fused(local, t, step=step, npert=npert, eps=cfg.eps, eta=cfg.eta,
-                          delta=cfg.delta, loss_at=loss_at, bits=bits, loss_probes_at=probes_at)
+                          delta=cfg.delta, loss_at=loss_at, bits=bits, loss_probes_at=probes_at,
+                          probes_give_clean=True)
     a = float(np.float32(cfg.eps))
     lossf = lambda p: oracle.mlp_loss(p, X, y, e["d_hid"], e["d_out"])  # noqa: E731
     L0 = lossf(theta)

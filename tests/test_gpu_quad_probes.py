@@ -54,9 +54,12 @@ def test_fused_losses_equal_perturb_then_loss(ctx, kind, n, offset, nprobes, mod
     t, ad = _dev(kind, h), to_dev_f32(a)
     step, probe0, alpha = 7, 11, 1e-3
     rows = zo.zo_gen_probes(ctx, step, probe0, nprobes, offset, n) if mode == "bits" else None
-    lp, lm = zo.zo_quad_loss_probes(ctx, t, ad, offset, step, probe0, nprobes, alpha, bits=rows)
+    clean = torch.full((1,), np.nan, dtype=torch.float64, device="cuda")
+    lp, lm = zo.zo_quad_loss_probes(ctx, t, ad, offset, step, probe0, nprobes, alpha, bits=rows,
+                                    out_clean=clean)
     gp, gm = lp.cpu().numpy(), lm.cpu().numpy()
     assert np.array_equal(_host(kind, t), h)                 # theta is not written
+    assert clean.item() == zo.zo_quad_loss(ctx, t, ad).item()   # the clean loss, same bits
     for i in range(nprobes):
         row = None if rows is None else rows[i]
         for sign, got in ((+1.0, gp[i]), (-1.0, gm[i])):
@@ -89,9 +92,10 @@ def test_fused_losses_argument_checks(ctx):
     op = torch.empty(4, dtype=torch.float64, device="cuda")
     om = torch.empty(4, dtype=torch.float64, device="cuda")
     L = zo._lib.lib()
-    args = lambda off=0, bits=None, plus=op.data_ptr(), minus=om.data_ptr(), p0=0, k=4: (  # noqa: E731
+    oc = torch.full((1,), np.nan, dtype=torch.float64, device="cuda")
+    args = lambda off=0, bits=None, plus=op.data_ptr(), minus=om.data_ptr(), p0=0, k=4, clean=None: (  # noqa: E731
         L.zo_quad_loss_probes(ctx.handle, t.data_ptr(), zo.ZO_FP32, a.data_ptr(), off, 1024, 1,
-                              p0, k, 1e-3, bits, plus, minus, None))
+                              p0, k, 1e-3, bits, plus, minus, clean, None))
     assert args() == zo.ZO_OK
     assert args(off=64) == zo.ZO_EINVAL                       # offset not a block multiple
     assert args(bits=t.data_ptr() + 4) == zo.ZO_EINVAL        # misaligned rows
@@ -99,6 +103,9 @@ def test_fused_losses_argument_checks(ctx):
     assert args(minus=None) == zo.ZO_EINVAL
     assert args(p0=0xFFFFFFFE, k=4) == zo.ZO_EINVAL           # probe indices wrap
     assert args(plus=None, minus=None, k=0) == zo.ZO_OK       # no probes: nothing to do
+    assert args(plus=None, minus=None, k=0, clean=oc.data_ptr()) == zo.ZO_OK   # clean only
+    torch.cuda.synchronize()
+    assert oc.item() == zo.zo_quad_loss(ctx, t, a).item() == 0.0     # theta is zero
     with pytest.raises(ValueError):
         zo.zo_quad_loss_probes(ctx, t, a[:10], 0, 1, 0, 2, 1e-3)
     with pytest.raises(ValueError):
@@ -108,8 +115,9 @@ def test_fused_losses_argument_checks(ctx):
 @pytest.mark.parametrize("kind", ["f32", "bf16"])
 def test_fused_step_equals_s4_step_on_exact_inputs(ctx, kind):
     """Where every move is exact (dyadic theta and eps), the fused step (losses at theta +/-
-    eps z_i from the clean theta, no passes) and the four-pass S4 step visit the same points:
-    equal losses, weights and updated theta, bit for bit."""
+    eps z_i from the clean theta, no passes; the clean loss from the first fused pass) and
+    the four-pass S4 step visit the same points: equal losses, weights and updated theta,
+    bit for bit."""
     from forward_only_amd.step import spsa_step, spsa_step_fused
     from workloads import gen
     n, npert, step = 70_001, 9, 4
@@ -127,8 +135,9 @@ def test_fused_step_equals_s4_step_on_exact_inputs(ctx, kind):
     rf = spsa_step_fused(
         ctx, tf, step=step, npert=npert, eps=eps, eta=1e-2, delta=1e-6,
         loss_at=lambda probe, alpha, row, out: zo.zo_quad_loss(ctx, tf, ad, out=out),
-        loss_probes_at=lambda p0, k, alpha, rows, op, om: zo.zo_quad_loss_probes(
-            ctx, tf, ad, 0, step, p0, k, alpha, bits=rows, out_plus=op, out_minus=om))
+        loss_probes_at=lambda p0, k, alpha, rows, op, om, oc: zo.zo_quad_loss_probes(
+            ctx, tf, ad, 0, step, p0, k, alpha, bits=rows, out_plus=op, out_minus=om,
+            out_clean=oc), probes_give_clean=True)
     for key in ("L0", "Lp", "Lm", "c"):
         assert np.array_equal(r4[key].cpu().numpy(), rf[key].cpu().numpy()), key
     assert np.array_equal(_host(kind, t4), _host(kind, tf))

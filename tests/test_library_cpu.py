@@ -72,7 +72,9 @@ def test_null_context_and_arguments_are_rejected():
     assert L.zo_mlp_loss_pair(None, None, 0, 0, 0, 1.0, None, None, None, 16, 16, 16, 2, None,
                               0, None, None, None) == _lib.ZO_EINVAL
     assert L.zo_quad_loss_probes(None, None, 0, None, 0, 16, 0, 0, 1, 1.0, None, None, None,
-                                 None) == _lib.ZO_EINVAL
+                                 None, None) == _lib.ZO_EINVAL
+    assert L.zo_mlp_loss_probes(None, None, 0, 0, 0, 1, 1.0, None, None, None, 16, 16, 16, 2,
+                                None, 0, None, None, None, None) == _lib.ZO_EINVAL
 
 
 def test_init_without_gpu_fails_cleanly():
