@@ -34,7 +34,10 @@
 // each SIMD gets several to interleave (one 8-probe wave per tile left 1.5 waves per SIMD,
 // which serialised every wave's sign arithmetic with its own MFMAs).  Slot s = 2i + sign
 // (probe i of the launch; sign 0: +alpha, 1: -alpha) writes its partial logits, row losses
-// and loss to its own places.
+// and loss to its own places.  With a clean loss requested, one more group of waves
+// (blockIdx.y == gridDim.y - 1) computes the unperturbed loss into the slot after the
+// probes' -- the same tile code as the clean launch, staged like the probe waves (the
+// staging depth does not change the k order), so its result equals the clean launch's.
 #include <stdlib.h>
 
 #include "zo_device.hpp"
