@@ -522,7 +522,11 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
                               f"zo_quad_loss_probes call: {npass} passes and their sums)",
                     "bound": "hbm", "achieved": fa, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": fa / PEAK_HBM_GBPS, "traffic": None,
-                    "losses_per_s": (2.0 * n + 1.0) / (lp_ms * 1e-3)}
+                    "losses_per_s": (2.0 * n + 1.0) / (lp_ms * 1e-3),
+                    "note": "measured against HBM, but held by VALU issue: 13 fp64 operations "
+                            "per param keep each loss equal to the fp64 loss kernel's; counters "
+                            "show 82-84% of the VALU issue slots used, and the loads alone run "
+                            "at 6.6 TB/s (profiles/flat125m_fused_kernel_trace_and_traffic.md)"}
     elif mlp is not None:
         mlp_ms = avg_ms("mlp_probes")
         achieved = (2.0 * n + 1.0) * mlp["flop"] / (mlp_ms * 1e-3) / 1e12
