@@ -18,11 +18,11 @@ from workloads import CONFIGS, gen
 
 pytestmark = pytest.mark.gpu
 
-# 16 x 16 tiles where the batch or the hidden width is not a multiple of 32, 32 x 32 tiles
-# otherwise; K below one 16-k group's multiple of the staging, with a ragged group count, and
-# the workload's shape
+# 16 x 16 tiles where the batch or the hidden width is not a multiple of 32 (the batch, the
+# width, or both), 32 x 32 tiles otherwise; K below one 16-k group's multiple of the staging,
+# with a ragged group count, and the workload's shape
 SHAPES = [(16, 16, 16, 2), (32, 48, 64, 3), (48, 32, 128, 16), (64, 208, 96, 16),
-          (128, 768, 3072, 2)]
+          (64, 32, 48, 5), (128, 768, 3072, 2)]
 
 
 @pytest.fixture(scope="module")
@@ -93,7 +93,7 @@ def test_fused_perturbation_equals_perturb_then_forward(ctx, shape, mode):
 
 
 @pytest.mark.parametrize("shape", [(16, 16, 16, 2), (32, 48, 64, 3), (48, 144, 128, 16),
-                                   (64, 208, 96, 16), (128, 768, 3072, 2)])
+                                   (64, 208, 96, 16), (64, 32, 48, 5), (128, 768, 3072, 2)])
 @pytest.mark.parametrize("mode", ["regen", "bits"])
 def test_pair_equals_two_fused_calls(ctx, shape, mode):
     """zo_mlp_loss_pair gives exactly the two single fused losses (+alpha, -alpha), in
@@ -116,7 +116,7 @@ def test_pair_equals_two_fused_calls(ctx, shape, mode):
 
 
 @pytest.mark.parametrize("shape", [(16, 16, 16, 2), (32, 48, 64, 3), (48, 144, 128, 16),
-                                   (64, 208, 96, 16), (128, 768, 3072, 2)])
+                                   (64, 208, 96, 16), (64, 32, 48, 5), (128, 768, 3072, 2)])
 @pytest.mark.parametrize("mode", ["regen", "bits"])
 @pytest.mark.parametrize("nprobes", [1, 3, 8, 13, 21, 70])
 def test_probes_equal_pairs(ctx, shape, mode, nprobes):

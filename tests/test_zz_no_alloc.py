@@ -52,7 +52,8 @@ def _with_workspace(ctx, theta, X, y, d_hid, d_out, step, probe, alpha, bits, ou
 @pytest.mark.parametrize("mode", ["regen", "bits"])
 def test_noalloc_pair_equals_workspace_pair_twice(mode):
     ctx = zo.zo_init(3)
-    shapes = [(128, 768, 3072, 2), (32, 48, 64, 3)]     # the workload's shape, then smaller
+    # the workload's shape, then smaller ones (32 x 32 tiles, then 16 x 16 tiles)
+    shapes = [(128, 768, 3072, 2), (32, 48, 64, 3), (48, 32, 48, 5)]
     for i, (batch, d_in, d_hid, d_out) in enumerate(shapes):
         print(f"[noalloc] {mode} call {i}: {batch}x{d_in}->{d_hid}->{d_out}", flush=True)
         theta, X, y = _problem(batch, d_in, d_hid, d_out, seed=40 + i)
