@@ -90,7 +90,7 @@ def spsa_step(ctx, theta: torch.Tensor, *, step: int, npert: int, eps: float, et
 
 
 def spsa_step_fused(ctx, theta: torch.Tensor, *, step: int, npert: int, eps: float, eta: float,
-                    delta: float, loss_at, offset: int = 0, bits=None,
+                    delta: float, loss_at=None, offset: int = 0, bits=None,
                     buffers: dict | None = None, loss_pair_at=None,
                     loss_probes_at=None, probes_give_clean: bool = False) -> dict:
     """One step whose forward applies each probe while reading the parameters.
@@ -103,8 +103,10 @@ def spsa_step_fused(ctx, theta: torch.Tensor, *, step: int, npert: int, eps: flo
     out_minus) (zo_mlp_loss_probes) all probes' losses come from one call; with
     probes_give_clean it is called with a seventh argument, the clean loss's output, which it
     fills from the same call (the out_clean of zo_mlp_loss_probes / zo_quad_loss_probes), and
-    loss_at is not called.
+    loss_at is not called (it may be None then; otherwise it is required).
     """
+    if loss_at is None and not (loss_probes_at is not None and probes_give_clean):
+        raise ValueError("loss_at is required unless loss_probes_at gives the clean loss")
     a = applied_eps(eps)
     b = buffers if buffers is not None else {}
     dev = theta.device

@@ -277,13 +277,6 @@ def test_mlp_config_fused_step(ctx, mode):
                                                       e["d_out"], npert),
                      dtype=torch.uint8, device="cuda")
 
-    def loss_at(probe, alpha, row, out):
-        if probe is None:
-            zo.zo_mlp_loss(local, t, x, yl, e["d_hid"], e["d_out"], workspace=ws, out=out)
-        else:
-            zo.zo_mlp_loss_perturbed(local, t, 0, step, probe, alpha, x, yl, e["d_hid"],
-                                     e["d_out"], bits=row, workspace=ws, out=out)
-
     def probes_at(probe0, n, alpha, rows, op, om, oc):
         zo.zo_mlp_loss_probes(local, t, 0, step, probe0, n, alpha, x, yl, e["d_hid"],
                               e["d_out"], bits=rows, workspace=ws, out_plus=op, out_minus=om,
@@ -291,7 +284,7 @@ def test_mlp_config_fused_step(ctx, mode):
 
     bits = zo.zo_gen_probes(local, step, 0, npert, 0, cfg.M) if mode == "bits" else None
     out = spsa_step_fused(local, t, step=step, npert=npert, eps=cfg.eps, eta=cfg.eta,
-                          delta=cfg.delta, loss_at=loss_at, bits=bits, loss_probes_at=probes_at,
+                          delta=cfg.delta, bits=bits, loss_probes_at=probes_at,
                           probes_give_clean=True)
     a = float(np.float32(cfg.eps))
     lossf = lambda p: oracle.mlp_loss(p, X, y, e["d_hid"], e["d_out"])  # noqa: E731

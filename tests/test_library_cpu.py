@@ -87,3 +87,17 @@ def test_init_without_gpu_fails_cleanly():
     assert h.value is None
     with pytest.raises(zo.ZOError):
         zo.zo_init(1)
+
+
+def test_fused_step_needs_a_clean_loss_source():
+    """spsa_step_fused without loss_at must get the clean loss from loss_probes_at; the check
+    comes before any device call."""
+    import pytest
+    import torch
+    from forward_only_amd.step import spsa_step_fused
+    theta = torch.zeros(8)
+    with pytest.raises(ValueError):
+        spsa_step_fused(None, theta, step=0, npert=2, eps=1e-3, eta=1e-3, delta=1e-6)
+    with pytest.raises(ValueError):
+        spsa_step_fused(None, theta, step=0, npert=2, eps=1e-3, eta=1e-3, delta=1e-6,
+                        loss_probes_at=lambda *a: None)
