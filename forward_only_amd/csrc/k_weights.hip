@@ -524,15 +524,35 @@ __global__ __launch_bounds__(256) void k_lowrank_final(const double *__restrict_
                                                        uint32_t blocks, uint32_t r,
                                                        double *__restrict__ out)
 {
-    __shared__ double red[4];
+    // thread t adds the partial rows of blocks t, t + 256, ... (all its loads independent),
+    // a fixed butterfly adds each component over the wave's lanes, and the four waves' sums
+    // meet in LDS after one barrier
+    __shared__ double wsum[4][kLowRankMax + 1];
     __shared__ double comp[kLowRankMax + 1];
-    for (uint32_t q = 0; q <= r; ++q) {
-        double acc = 0.0;
-        for (uint32_t b = threadIdx.x; b < blocks; b += blockDim.x)
-            acc += part[(uint64_t)b * (kLowRankMax + 1) + q];
-        const double s = block_sum256(acc, red);
-        if (threadIdx.x == 0) comp[q] = s;
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    double acc[kLowRankMax + 1];
+#pragma unroll
+    for (uint32_t q = 0; q <= kLowRankMax; ++q) acc[q] = 0.0;
+    for (uint32_t b = threadIdx.x; b < blocks; b += blockDim.x) {
+        const double *row = part + (uint64_t)b * (kLowRankMax + 1);
+#pragma unroll
+        for (uint32_t q = 0; q <= kLowRankMax; ++q)
+            if (q <= r) acc[q] += row[q];
     }
+#pragma unroll
+    for (uint32_t q = 0; q <= kLowRankMax; ++q) {
+        if (q <= r) {
+            double v = acc[q];
+#pragma unroll
+            for (int w = 32; w >= 1; w >>= 1) v += __shfl_xor(v, w, 64);
+            if (lane == 0) wsum[wave][q] = v;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x <= r)
+        comp[threadIdx.x] = (wsum[0][threadIdx.x] + wsum[1][threadIdx.x]) +
+                            (wsum[2][threadIdx.x] + wsum[3][threadIdx.x]);
+    __syncthreads();
     if (threadIdx.x == 0) {
         double sq = 0.0;
         for (uint32_t k = 1; k <= r; ++k) sq += comp[k] * comp[k];
