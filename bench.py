@@ -536,7 +536,11 @@ def run_workload(args, name: str, K: int, W: int, cpu=None, gen_plane: bool = Tr
                               "kernels of all n_pert probes' 2 n_pert + 1 forwards)",
                     "bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS,
                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
-                    "traffic": None}
+                    "traffic": None,
+                    "note": "peak at 2.4 GHz; under this load the counters give a clock near "
+                            "2.11 GHz (GRBM_GUI_ACTIVE over the dispatch), where the fp32 "
+                            "MFMA peak is about 138 TFLOP/s; MFMA busy 68% and VALU issue 25% "
+                            "(profiles/k_mlp_tiles_mlp_trace_and_counters.md)"}
     else:
         achieved = pass_bytes / (pert_ms * 1e-3) / 1e9 if pert_ms else None
         roofline = None
